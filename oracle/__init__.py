@@ -1,0 +1,148 @@
+"""CPU oracle for the batched speculative-decoding verify step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The GPU library never
+imports it and has no fallback to it.
+
+`spec_oracle.c` holds the arithmetic (plain double-precision loops; see its
+header for the passages of the pages it follows).  This module only builds
+that file with gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spec_oracle.c")
+_LIB = os.path.join(_HERE, "libspec_oracle.so")
+
+F32, BF16 = 0, 1
+SAMPLE, GREEDY = 0, 1
+FAULT_NONE, FAULT_NO_CLAMP, FAULT_UNSCALED_TAU, FAULT_RESAMPLE_P, FAULT_GREEDY_RULE = range(5)
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile spec_oracle.c into libspec_oracle.so (gcc, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-fopenmp", "-std=c11", "-Wall", "-shared", "-fPIC",
+               "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        lib.oracle_verify.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, ctypes.c_double,
+                                      i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_verify.restype = i32
+        lib.oracle_draw_cdf.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, ctypes.c_double,
+                                        i32, P]
+        lib.oracle_draw_cdf.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("logits must be float32 or bf16 bit patterns stored as uint16")
+
+
+@dataclass
+class OracleResult:
+    tokens: np.ndarray      # int32 [B, G+1], -1 padded
+    n_accepted: np.ndarray  # int32 [B]
+    new_len: np.ndarray     # int32 [B]
+    px: np.ndarray          # float64 [B, G]; NaN where the position was not tested
+    qx: np.ndarray          # float64 [B, G]
+    z: np.ndarray           # float64 [B]; normaliser of the drawn distribution
+    m: np.ndarray           # float64 [B, 2G+1]; raw-logit max of t_0..t_G, d_0..d_{G-1}
+    s: np.ndarray           # float64 [B, 2G+1]; sum exp((l - m) / T)
+    draw_pos: np.ndarray    # int32 [B]; position drawn from, -1 if none
+    zero_resid: np.ndarray  # int32 [B]; 1 where the residual mass was exactly 0
+
+
+def _c(a, dt):
+    return None if a is None else np.ascontiguousarray(a, dtype=dt)
+
+
+def verify(target, draft, tokens, uniforms, gamma, kv_len=None, *, temperature=1.0,
+           mode=SAMPLE, fault=FAULT_NONE, threads=0) -> OracleResult:
+    """Run the oracle over a batch.
+
+    target: [B, G+1, V] float32 or uint16 (bf16 bits); draft: [B, G, V] same
+    dtype (may be None in greedy mode); tokens: int32 [B, G]; uniforms:
+    float32 [B, G+1] (may be None in greedy mode); gamma: int32 [B];
+    kv_len: int32 [B] or None.  threads=0 uses the OpenMP default.
+    """
+    lib = _load()
+    target = np.ascontiguousarray(target)
+    B, G1, V = target.shape
+    G = G1 - 1
+    dt = _dtype_code(target)
+    if draft is not None:
+        draft = np.ascontiguousarray(draft, dtype=target.dtype)
+        if draft.shape != (B, G, V):
+            raise ValueError("draft shape must be [B, G, V]")
+    tokens = _c(tokens, np.int32).reshape(B, G)
+    uniforms = _c(uniforms, np.float32)
+    if uniforms is not None:
+        uniforms = uniforms.reshape(B, G + 1)
+    gamma = _c(gamma, np.int32).reshape(B)
+    kv_len = _c(kv_len, np.int32)
+    out_tokens = np.empty((B, G + 1), np.int32)
+    out_n = np.empty(B, np.int32)
+    out_len = np.empty(B, np.int32)
+    px = np.empty((B, G), np.float64)
+    qx = np.empty((B, G), np.float64)
+    z = np.empty(B, np.float64)
+    m = np.empty((B, 2 * G + 1), np.float64)
+    s = np.empty((B, 2 * G + 1), np.float64)
+    pos = np.empty(B, np.int32)
+    zr = np.empty(B, np.int32)
+    rc = lib.oracle_verify(_ptr(target), _ptr(draft), dt, _ptr(tokens), _ptr(uniforms),
+                           _ptr(gamma), _ptr(kv_len), B, G, V, float(temperature), int(mode),
+                           int(fault), int(threads), _ptr(out_tokens), _ptr(out_n),
+                           _ptr(out_len), _ptr(px), _ptr(qx), _ptr(z), _ptr(m), _ptr(s),
+                           _ptr(pos), _ptr(zr))
+    if rc != 0:
+        raise ValueError(f"oracle refused its arguments (code {rc})")
+    return OracleResult(out_tokens, out_n, out_len, px, qx, z, m, s, pos, zr)
+
+
+def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0):
+    """Normalised CDF (C_j / Z, float64 [V]) of the distribution the oracle
+    drew row `row`'s last token from, and the position it was drawn at."""
+    lib = _load()
+    target = np.ascontiguousarray(target)
+    B, G1, V = target.shape
+    G = G1 - 1
+    draft = np.ascontiguousarray(draft, dtype=target.dtype)
+    tokens = _c(tokens, np.int32).reshape(B, G)
+    uniforms = _c(uniforms, np.float32).reshape(B, G + 1)
+    gamma = _c(gamma, np.int32).reshape(B)
+    cdf = np.empty(V, np.float64)
+    pos = lib.oracle_draw_cdf(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens),
+                              _ptr(uniforms), _ptr(gamma), None, B, G, V, float(temperature),
+                              int(row), _ptr(cdf))
+    return cdf, int(pos)

@@ -1,0 +1,377 @@
+/*
+ * spec_oracle.c -- plain, slow, double-precision CPU oracle for the batched
+ * verify step of speculative decoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the GPU library and must never be used as a
+ * fallback for it.
+ *
+ * What it computes (one batch row b, draft length g = gamma[b]):
+ *
+ *   Sources: "Speculative decoding" (mhtirogla.ai), sections "How it works"
+ *   steps 2-5 and "Code" (the verify function); "Speculative decoding: the
+ *   secretary who types ahead of the boss" (blog.lo0.es), section "The bare
+ *   mechanism", step 3; "Speculative Decoding" (inference.tusharamrit.in),
+ *   the loop and the modified rejection-sampling rule; "Speculative
+ *   Decoding" (tokentrails.org), steps 2 and 4 and its code block.
+ *
+ *   1. p_i = softmax(target_logits[b,i,:] / T) for i = 0..g (row g is the
+ *      bonus distribution), q_i = softmax(draft_logits[b,i,:] / T) for
+ *      i = 0..g-1.  Both sides get the same temperature processing (mhtirogla
+ *      "Implementation notes"; tusharamrit caveat after the proof).
+ *   2. Walk i = 0..g-1 left to right with draft token x = x_i and uniform u_i:
+ *      accept when u_i * q_i(x) < p_i(x) (the division-free form of
+ *      u < p/q used in the mhtirogla code); stop at the first rejection.
+ *   3. Rejection at n: draw from norm(max(0, p_n - q_n)) with the next unused
+ *      uniform u_{n+1}.  All g accepted: draw the bonus token from p_g with
+ *      u_g.  The draw is the inverse CDF: tau = u * Z, return the smallest j
+ *      with tau < sum_{k<=j} w_k (the mhtirogla `sample`, which scales u by
+ *      the sum so an unnormalised weight vector is fine).
+ *   4. Greedy mode: accept while x_i equals the target argmax g_i (lowest
+ *      index on ties), emit g_n at the first disagreement or g_g when all
+ *      agree (mhtirogla "How it works", last paragraph; tokentrails step 2
+ *      and its code block).
+ *   5. KV rollback: the new cache length is kv_len_in + n (mhtirogla step 5,
+ *      "truncate the length").
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *   - temperature: softmax(logit / T), T > 0 required when sampling; greedy
+ *     ignores T.
+ *   - uniforms: one stream of gamma_max+1 per row, consumed in order: u_0..u_n
+ *     by the tests, then the next unused one by the single draw.
+ *   - inverse-CDF fallback: when no j satisfies tau < C_j (rounding), the last
+ *     index with positive weight (the page's "last index" could pick a
+ *     zero-probability token).
+ *   - residual mass Z == 0 after a rejection (impossible in exact arithmetic):
+ *     draw from p_n with the same uniform and count it.
+ *   - bonus normaliser: the bonus row's own sum.
+ *   - data errors (gamma outside [0, gamma_max], a tested draft token outside
+ *     [0, V), or, when sampling, a needed row whose logits are all -inf):
+ *     n_accepted = -1, tokens all -1, new_len = kv_len_in.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_SAMPLE 0
+#define OR_GREEDY 1
+
+/* Mutations used only by negative-control tests, to show that the
+ * statistical tests can detect the classic mistakes named on the pages
+ * (mhtirogla "Pitfalls"; tusharamrit, the naive rule and the residual). */
+#define OR_FAULT_NONE 0
+#define OR_FAULT_NO_CLAMP 1      /* residual p - q without max(0, .)        */
+#define OR_FAULT_UNSCALED_TAU 2  /* threshold u instead of u * Z             */
+#define OR_FAULT_RESAMPLE_P 3    /* after a rejection draw from p, not residual */
+#define OR_FAULT_GREEDY_RULE 4   /* accept iff x == argmax p while sampling   */
+
+typedef struct {
+  const void* target;
+  const void* draft;
+  int dtype;
+  const int32_t* tokens;
+  const float* uniforms;
+  const int32_t* gamma;
+  const int32_t* kv_len;
+  int B, G, V;
+  double T;
+  int mode;
+  int fault;
+} oracle_ctx;
+
+/* Exact widening of one stored logit to double. */
+static double widen(const oracle_ctx* c, const void* base, size_t k) {
+  if (c->dtype == OR_F32) return (double)((const float*)base)[k];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[k] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Offset (in elements) of vocabulary row (b, i) in a [B, rows, V] tensor. */
+static size_t row_off(const oracle_ctx* c, int b, int rows, int i) {
+  return ((size_t)b * (size_t)rows + (size_t)i) * (size_t)c->V;
+}
+
+/* p = softmax(logits / T) in double.  Writes the raw-logit maximum and the
+ * sum S = sum_j exp((l_j - max)/T).  Returns 0 when every logit is -inf. */
+static int softmax_row(const oracle_ctx* c, const void* base, size_t off,
+                       double* prob, double* m_out, double* s_out) {
+  const int V = c->V;
+  double m = -INFINITY;
+  for (int j = 0; j < V; ++j) {
+    double l = widen(c, base, off + j);
+    if (l > m) m = l;
+  }
+  if (m_out) *m_out = m;
+  if (m == -INFINITY) {
+    if (s_out) *s_out = 0.0;
+    return 0;
+  }
+  double s = 0.0;
+  for (int j = 0; j < V; ++j) {
+    double l = widen(c, base, off + j);
+    double e = exp((l - m) / c->T);
+    prob[j] = e;
+    s += e;
+  }
+  for (int j = 0; j < V; ++j) prob[j] /= s;
+  if (s_out) *s_out = s;
+  return 1;
+}
+
+/* Lowest index of the largest raw logit of one row (float comparison, so
+ * -0 and +0 tie and the lower index wins). */
+static int argmax_row(const oracle_ctx* c, size_t off) {
+  int best = 0;
+  double bv = widen(c, c->target, off);
+  for (int j = 1; j < c->V; ++j) {
+    double l = widen(c, c->target, off + j);
+    if (l > bv) {
+      bv = l;
+      best = j;
+    }
+  }
+  return best;
+}
+
+/* Inverse-CDF draw over non-negative weights w[0..V): tau = u * Z, the
+ * smallest j with tau < C_j; fallback: the last index with w > 0.
+ * Writes Z.  cdf_out (optional) receives C_j / Z. */
+static int draw_index(const oracle_ctx* c, const double* w, double u,
+                      double* z_out, double* cdf_out) {
+  const int V = c->V;
+  double z = 0.0;
+  for (int j = 0; j < V; ++j) z += w[j];
+  if (z_out) *z_out = z;
+  double tau = (c->fault == OR_FAULT_UNSCALED_TAU) ? u : u * z;
+  int pick = -1, last_pos = -1;
+  double acc = 0.0;
+  for (int j = 0; j < V; ++j) {
+    acc += w[j];
+    if (cdf_out) cdf_out[j] = acc / z;
+    if (w[j] > 0.0) last_pos = j;
+    if (pick < 0 && tau < acc) pick = j;
+  }
+  if (pick < 0) pick = (last_pos >= 0) ? last_pos : V - 1;
+  return pick;
+}
+
+typedef struct {
+  double* px;       /* [G] p_i(x_i) for tested positions (NaN otherwise)   */
+  double* qx;       /* [G] q_i(x_i)                                         */
+  double* z;        /* [1] normaliser of the drawn distribution             */
+  double* m;        /* [2G+1] raw-logit max per vocabulary row (t0..tG, d0..dG-1) */
+  double* s;        /* [2G+1] exp-sum relative to that max                  */
+  int32_t* draw_pos;   /* [1] position whose distribution was drawn from (-1: none) */
+  int32_t* zero_resid; /* [1] 1 when the residual mass was exactly 0         */
+  double* cdf;      /* [V] normalised CDF of the drawn distribution, or NULL */
+} row_diag;
+
+static void write_sentinel(const oracle_ctx* c, int b, int32_t* tok, int32_t* n_out,
+                           int32_t* len_out) {
+  for (int i = 0; i <= c->G; ++i) tok[(size_t)b * (c->G + 1) + i] = -1;
+  n_out[b] = -1;
+  len_out[b] = c->kv_len ? c->kv_len[b] : 0;
+}
+
+static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t* out_n,
+                       int32_t* out_len, row_diag* d) {
+  const int G = c->G, V = c->V;
+  const int g = c->gamma[b];
+  int32_t* tok = out_tokens + (size_t)b * (G + 1);
+  const int32_t* x = c->tokens + (size_t)b * G;
+  const float* u = c->uniforms ? c->uniforms + (size_t)b * (G + 1) : NULL;
+  const int kv = c->kv_len ? c->kv_len[b] : 0;
+
+  if (d->draw_pos) *d->draw_pos = -1;
+  if (d->zero_resid) *d->zero_resid = 0;
+  if (g < 0 || g > G) {
+    write_sentinel(c, b, out_tokens, out_n, out_len);
+    return;
+  }
+
+  if (c->mode == OR_GREEDY) {
+    int n = g, emit = -1;
+    for (int i = 0; i <= g; ++i) {
+      int gi = argmax_row(c, row_off(c, b, G + 1, i));
+      if (i == g) {
+        emit = gi;
+        break;
+      }
+      if (x[i] < 0 || x[i] >= V) {
+        write_sentinel(c, b, out_tokens, out_n, out_len);
+        return;
+      }
+      if (x[i] != gi) {
+        n = i;
+        emit = gi;
+        break;
+      }
+    }
+    for (int i = 0; i < n; ++i) tok[i] = x[i];
+    tok[n] = emit;
+    for (int i = n + 1; i <= G; ++i) tok[i] = -1;
+    out_n[b] = n;
+    out_len[b] = kv + n;
+    return;
+  }
+
+  /* Sampling: p_0..p_g and q_0..q_{g-1}, all in double. */
+  double* P = (double*)malloc(sizeof(double) * (size_t)(g + 1) * V);
+  double* Q = (double*)malloc(sizeof(double) * (size_t)(g > 0 ? g : 1) * V);
+  double* w = (double*)malloc(sizeof(double) * (size_t)V);
+  int ok = 1;
+  for (int i = 0; i <= g; ++i) {
+    double m, s;
+    int live = softmax_row(c, c->target, row_off(c, b, G + 1, i), P + (size_t)i * V, &m, &s);
+    if (d->m) d->m[i] = m;
+    if (d->s) d->s[i] = s;
+    ok &= live;
+  }
+  for (int i = 0; i < g; ++i) {
+    double m, s;
+    int live = softmax_row(c, c->draft, row_off(c, b, G, i), Q + (size_t)i * V, &m, &s);
+    if (d->m) d->m[G + 1 + i] = m;
+    if (d->s) d->s[G + 1 + i] = s;
+    ok &= live;
+  }
+  if (!ok) {
+    write_sentinel(c, b, out_tokens, out_n, out_len);
+    free(P), free(Q), free(w);
+    return;
+  }
+
+  int n = g;
+  for (int i = 0; i < g; ++i) {
+    const double* p = P + (size_t)i * V;
+    const double* q = Q + (size_t)i * V;
+    int xi = x[i];
+    if (xi < 0 || xi >= V) {
+      write_sentinel(c, b, out_tokens, out_n, out_len);
+      free(P), free(Q), free(w);
+      return;
+    }
+    if (d->px) d->px[i] = p[xi];
+    if (d->qx) d->qx[i] = q[xi];
+    int accept;
+    if (c->fault == OR_FAULT_GREEDY_RULE) {
+      int am = 0;
+      for (int j = 1; j < V; ++j)
+        if (p[j] > p[am]) am = j;
+      accept = (xi == am);
+    } else {
+      accept = ((double)u[i] * q[xi] < p[xi]);
+    }
+    if (!accept) {
+      n = i;
+      break;
+    }
+  }
+
+  const double* pn = P + (size_t)n * V;
+  double ustar = (double)u[n < g ? n + 1 : g];
+  if (n < g) {
+    const double* qn = Q + (size_t)n * V;
+    for (int j = 0; j < V; ++j) {
+      double r = pn[j] - qn[j];
+      if (c->fault == OR_FAULT_NO_CLAMP)
+        w[j] = r;
+      else if (c->fault == OR_FAULT_RESAMPLE_P)
+        w[j] = pn[j];
+      else
+        w[j] = r > 0.0 ? r : 0.0;
+    }
+    double z = 0.0;
+    for (int j = 0; j < V; ++j) z += w[j];
+    if (z == 0.0) {
+      if (d->zero_resid) *d->zero_resid = 1;
+      memcpy(w, pn, sizeof(double) * (size_t)V);
+    }
+  } else {
+    memcpy(w, pn, sizeof(double) * (size_t)V);
+  }
+  int j = draw_index(c, w, ustar, d->z, d->cdf);
+  if (d->draw_pos) *d->draw_pos = n;
+
+  for (int i = 0; i < n; ++i) tok[i] = x[i];
+  tok[n] = j;
+  for (int i = n + 1; i <= G; ++i) tok[i] = -1;
+  out_n[b] = n;
+  out_len[b] = kv + n;
+  free(P), free(Q), free(w);
+}
+
+/* Returns 0 on success, a negative value for arguments the oracle refuses.
+ * Diagnostic outputs may be NULL: px/qx are [B, G] (NaN where a position
+ * was not tested), z/draw_pos/zero_resid are [B], m/s are [B, 2G+1]. */
+int oracle_verify(const void* target, const void* draft, int dtype, const int32_t* tokens,
+                  const float* uniforms, const int32_t* gamma, const int32_t* kv_len, int B,
+                  int G, int V, double T, int mode, int fault, int threads,
+                  int32_t* out_tokens, int32_t* out_n, int32_t* out_len, double* out_px,
+                  double* out_qx, double* out_z, double* out_m, double* out_s,
+                  int32_t* out_draw_pos, int32_t* out_zero_resid) {
+  if (!target || !tokens || !gamma || !out_tokens || !out_n || !out_len) return -1;
+  if (B < 0 || G < 0 || V <= 0) return -2;
+  if (dtype != OR_F32 && dtype != OR_BF16) return -3;
+  if (mode != OR_SAMPLE && mode != OR_GREEDY) return -3;
+  if (mode == OR_SAMPLE && (!draft || !uniforms || !(T > 0.0) || !isfinite(T))) return -3;
+  oracle_ctx c = {target, draft, dtype, tokens, uniforms, gamma, kv_len, B, G, V, T, mode, fault};
+  const size_t nr = (size_t)(2 * G + 1);
+  if (out_px)
+    for (size_t k = 0; k < (size_t)B * G; ++k) out_px[k] = NAN;
+  if (out_qx)
+    for (size_t k = 0; k < (size_t)B * G; ++k) out_qx[k] = NAN;
+  if (out_z)
+    for (int b = 0; b < B; ++b) out_z[b] = NAN;
+  if (out_m)
+    for (size_t k = 0; k < (size_t)B * nr; ++k) out_m[k] = NAN;
+  if (out_s)
+    for (size_t k = 0; k < (size_t)B * nr; ++k) out_s[k] = NAN;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int b = 0; b < B; ++b) {
+    row_diag d = {out_px ? out_px + (size_t)b * G : NULL,
+                  out_qx ? out_qx + (size_t)b * G : NULL,
+                  out_z ? out_z + b : NULL,
+                  out_m ? out_m + (size_t)b * nr : NULL,
+                  out_s ? out_s + (size_t)b * nr : NULL,
+                  out_draw_pos ? out_draw_pos + b : NULL,
+                  out_zero_resid ? out_zero_resid + b : NULL,
+                  NULL};
+    verify_row(&c, b, out_tokens, out_n, out_len, &d);
+  }
+  (void)threads;
+  return 0;
+}
+
+/* Re-runs row b alone and writes the normalised CDF (C_j / Z) of the
+ * distribution the oracle drew its last token from into cdf[0..V).
+ * Returns the drawn position, or -1 when the row drew nothing (greedy or a
+ * data error). */
+int oracle_draw_cdf(const void* target, const void* draft, int dtype, const int32_t* tokens,
+                    const float* uniforms, const int32_t* gamma, const int32_t* kv_len, int B,
+                    int G, int V, double T, int b, double* cdf) {
+  if (!target || !draft || !tokens || !uniforms || !gamma || !cdf) return -1;
+  if (b < 0 || b >= B) return -1;
+  oracle_ctx c = {target, draft, dtype, tokens, uniforms, gamma, kv_len, B, G, V, T, OR_SAMPLE,
+                  OR_FAULT_NONE};
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)B * (G + 1));
+  int32_t* nn = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+  int32_t* ln = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+  int32_t pos = -1;
+  row_diag d = {NULL, NULL, NULL, NULL, NULL, &pos, NULL, cdf};
+  verify_row(&c, b, tok, nn, ln, &d);
+  free(tok), free(nn), free(ln);
+  return pos;
+}
