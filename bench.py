@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched verify step on one MI355X.
+
+One step = one spec_verify call (the whole verify: statistics, acceptance,
+residual/bonus draw) over one batch of the B=64, gamma=4, V=128256 bf16,
+T=1.0 sampling workload (target N(0, 3^2) plus a +8 spike per position,
+draft = target + N(0, 1.5^2)), with all inputs already in HBM.  Several
+device copies of the logits are rotated so that successive steps do not hit
+the 256 MB Infinity Cache.
+
+Prints one JSON line.  `value` is verified rows per second; the roofline
+object gives the dominant (only) kernel's achieved HBM rate from the
+compulsory logit bytes and its event-timed average launch duration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+ROTATE_BYTES = 1 << 30  # at least this much distinct logit memory in rotation
+COUNTERS = os.path.join(ROOT, "profiles", "verify_kernel_c3_sample_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_07_amd", "csrc",
+                          "spec_verify.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
+    ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
+    ap.add_argument("--rotate", type=int, default=0, help="device copies (0: enough for 1 GiB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--with-copy", action="store_true",
+                    help="also run the reference copy kernel (counter calibration)")
+    ap.add_argument("--tune", default="", help="chunk_bytes,slice_elems,lag_rows")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify step is "
+              "independent per batch row, so N GPUs would each run this same benchmark on "
+              "their own rows", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_07_amd as sv
+    from speculative_decoding_verification_07_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sv.load()
+    if args.tune:
+        sv.tune(*[int(v) for v in args.tune.split(",")])
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    t0 = time.time()
+    case = inputs.make_case(args.config, rnd=0, mode=args.mode)
+    gen_s = time.time() - t0
+    B, G, V = case.B, case.G, case.V
+    dt = sv.BF16 if case.target.dtype == np.uint16 else sv.F32
+    mode = sv.GREEDY if args.mode == "greedy" else sv.SAMPLE
+    step_bytes = inputs.algorithmic_bytes(case)
+    logit_bytes = case.target.nbytes + (case.draft.nbytes if mode == sv.SAMPLE else 0)
+    rot = args.rotate or max(1, -(-ROTATE_BYTES // logit_bytes))
+
+    def logits(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    tgt0, dft0 = logits(case.target), logits(case.draft)
+    sets = [(tgt0, dft0)] + [(tgt0.clone(), dft0.clone()) for _ in range(rot - 1)]
+    tok = torch.from_numpy(case.tokens).to(dev)
+    uni = torch.from_numpy(case.uniforms).to(dev)
+    gam = torch.from_numpy(case.gamma).to(dev)
+    kv = torch.from_numpy(case.kv_len).to(dev)
+    ws = sv.Workspace(sv.workspace_bytes(B, G, V, dt, mode))
+    out = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+           torch.empty(B, dtype=torch.int32, device=dev),
+           torch.empty(B, dtype=torch.int32, device=dev))
+
+    def step(k):
+        t, d = sets[k % rot]
+        sv.verify(t, d, tok, uni, gam, kv, temperature=case.T, mode=mode, workspace=ws, out=out)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        ev0[k].record(stream)
+        step(k)
+        ev1[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev0[0].elapsed_time(ev1[K - 1])
+    launch_ms = np.array([ev0[k].elapsed_time(ev1[k]) for k in range(K)])
+    diag = ws.diagnostics()
+    n_acc = out[1].cpu().numpy()
+
+    ms_per_step = total_ms / K
+    kern_s = float(launch_ms.mean()) * 1e-3
+    achieved = step_bytes / kern_s / 1e9
+    emitted = int((n_acc + 1).sum())
+    tested = int(np.minimum(n_acc + 1, case.gamma).sum())
+
+    # HBM read ceiling of this machine: plain streaming read of 4 GiB
+    probe = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    pout = None
+    for _ in range(3):
+        pout = sv.probe_read(probe, pout)
+    torch.cuda.synchronize()
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe0.record(stream)
+    for _ in range(10):
+        sv.probe_read(probe, pout)
+    pe1.record(stream)
+    torch.cuda.synchronize()
+    ceiling = probe.numel() * 10 / (pe0.elapsed_time(pe1) * 1e-3) / 1e9
+    if args.with_copy:
+        dst = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            sv.probe_copy(probe[: 1 << 28], dst)
+        torch.cuda.synchronize()
+        del dst
+    del probe
+
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            cnt = json.load(f)
+        if cnt.get("source_sha256_16") == source_hash() and cnt.get("workload_config") == args.config \
+                and cnt.get("mode") == args.mode:
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and reps < 50:
+            c0 = time.perf_counter()
+            oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
+                          case.kv_len, temperature=case.T,
+                          mode=oracle.GREEDY if mode == sv.GREEDY else oracle.SAMPLE,
+                          threads=threads)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        cpu = {"value": B * reps / t_cpu, "unit": "rows/s", "cores": threads, "kind": "oracle",
+               "sample": f"{reps} full batches of this workload ({B} rows each), "
+                         f"{t_cpu:.1f} s of double-precision oracle work"}
+
+    cfgd = {"workload": f"verify B={B} gamma={G} V={V} "
+                        f"{'bf16' if dt == sv.BF16 else 'fp32'} logits T={case.T} {args.mode}"
+                        f" (config {args.config})",
+            "B": B, "gamma": G, "V": V, "logits_dtype": "bf16" if dt == sv.BF16 else "fp32",
+            "mode": args.mode, "temperature": case.T, "rotated_copies": rot,
+            "compulsory_bytes_per_step": step_bytes}
+    line = {
+        "metric": "verified rows/s (batched speculative-decoding verify step)",
+        "value": B * K / (total_ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": cfgd,
+        "emitted_tokens_per_s": emitted * K / (total_ms * 1e-3),
+        "step_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "kernel_us": kern_s * 1e6,
+        "kernel_us_p50": float(np.median(launch_ms)) * 1e3,
+        "acceptance_rate": (emitted - B) / max(tested, 1),
+        "mean_emitted_per_row": emitted / B,
+        "read_ceiling_gbps": ceiling,
+        "wall_s_timed": wall,
+        "input_gen_s": gen_s,
+        "diagnostics": diag,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "verify_kernel", "bytes_per_launch": step_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) batched verify step of
+ * speculative decoding.
+ *
+ * The operation (sources: "Speculative decoding", mhtirogla.ai, sections
+ * "How it works" steps 2-5 and "Code"; "Speculative decoding: the secretary
+ * who types ahead of the boss", blog.lo0.es, "The bare mechanism" step 3;
+ * "Speculative decoding", inference.tusharamrit.in, the loop and the
+ * modified rejection-sampling rule; "Speculative Decoding", tokentrails.org,
+ * steps 2 and 4):
+ *
+ *   For every batch row b with draft length g = gamma_per_row[b]:
+ *     p_i = softmax(target_logits[b, i, :] / T), i = 0..g   (row g: bonus)
+ *     q_i = softmax(draft_logits[b, i, :] / T),  i = 0..g-1
+ *     walking i = 0..g-1, accept x_i = draft_tokens[b, i] while
+ *       u_i * q_i(x_i) < p_i(x_i)        (u_i = uniforms[b, i])
+ *     at the first rejection n: emit x_0..x_{n-1}, then one token drawn by
+ *       inverse CDF from norm(max(0, p_n - q_n)) with uniform u_{n+1};
+ *     if all g are accepted: emit x_0..x_{g-1}, then one token drawn from
+ *       p_g with uniform u_g.
+ *     The inverse CDF returns the smallest j with u * Z < sum_{k<=j} w_k
+ *     (Z = sum of the weights); if rounding leaves no such j, the last index
+ *     with positive weight.
+ *   GREEDY mode ignores T, q and u: g_i = lowest index of the largest
+ *   target logit of row i; accept while x_i == g_i; emit x_0..x_{n-1}, g_n.
+ *   new_len[b] = kv_len_in[b] + n (the KV caches keep the accepted drafts;
+ *   the emitted correction or bonus token has no cache entry yet).
+ *
+ * All device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronising: outputs are valid
+ * once the stream has completed the call.  Argument errors are reported by
+ * the return value before anything is launched, and then no output is
+ * written.  The library allocates no memory and keeps no state other than
+ * the caller's workspace (and a process-wide tuning override, see
+ * spec_verify_tune).  Calls on distinct workspaces may run concurrently;
+ * two calls that share a workspace must be ordered (same stream).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum spec_mode { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1 };
+enum spec_dtype { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 };
+
+enum spec_status {
+  SPEC_OK = 0,
+  SPEC_ERR_NULL = -1,      /* a required pointer is NULL                              */
+  SPEC_ERR_SHAPE = -2,     /* B < 1, V < 1, V > 2^30, gamma_max outside [0, 63]       */
+  SPEC_ERR_ARG = -3,       /* unknown mode or dtype; T not finite and > 0 when sampling */
+  SPEC_ERR_WORKSPACE = -4, /* workspace NULL or smaller than spec_verify_workspace_bytes */
+  SPEC_ERR_ALIGN = -5,     /* logits not aligned to their element size, or an int32/float
+                              array not 4-byte aligned                                 */
+  SPEC_ERR_HIP = -100      /* a HIP runtime error e is returned as SPEC_ERR_HIP - e     */
+};
+
+#define SPEC_GAMMA_MAX_LIMIT 63
+
+/* Bytes of device workspace a call with these sizes needs (host only, pure
+ * function of its arguments and of the tuning override).  Returns 0 for
+ * sizes spec_verify would reject.
+ *
+ * The workspace holds per-chunk softmax statistics, per-row decisions, and
+ * self-resetting counters.  It must be zero-filled once before its first use
+ * (spec_verify_workspace_reset, or any zero fill); every call that completes
+ * leaves its counters at zero again, so one workspace serves any sequence of
+ * stream-ordered calls with sizes up to the ones it was sized for. */
+size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype, int mode);
+
+/* Zero-fills `bytes` of a workspace with a small fill kernel on `stream`
+ * (no memset node, so it may be captured in a HIP graph). */
+int spec_verify_workspace_reset(void* workspace, size_t bytes, void* stream);
+
+/* The verify step.  Device pointers unless stated; all arrays dense,
+ * row-major, innermost index last:
+ *   target_logits  [B, gamma_max+1, V] of dtype (fp32, or bf16 bit patterns)
+ *   draft_logits   [B, gamma_max, V]   of dtype; may be NULL in GREEDY mode
+ *   draft_tokens   int32 [B, gamma_max]; x_i for i < gamma_per_row[b]
+ *   uniforms       fp32 [B, gamma_max+1] in [0, 1); may be NULL in GREEDY
+ *   gamma_per_row  int32 [B]; each in [0, gamma_max]
+ *   kv_len_in      int32 [B], or NULL for 0
+ *   temperature    T > 0 (SAMPLE); ignored in GREEDY
+ *   out_tokens     int32 [B, gamma_max+1]: n+1 emitted tokens, then -1
+ *   out_n_accepted int32 [B]: n
+ *   out_new_len    int32 [B]: kv_len_in + n
+ * Any 2-byte (bf16) or 4-byte (fp32) aligned logits base works; rows need
+ * not be 16-byte aligned.  Logits must be finite or -inf.
+ * Per-row data errors (gamma outside [0, gamma_max]; a tested draft token
+ * outside [0, V); when sampling, a needed row whose logits are all -inf)
+ * give n_accepted = -1, tokens all -1 and new_len = kv_len_in for that row
+ * only. */
+int spec_verify(const void* target_logits, const void* draft_logits,
+                const int32_t* draft_tokens, const float* uniforms,
+                const int32_t* gamma_per_row, const int32_t* kv_len_in, int B, int gamma_max,
+                int V, int dtype, float temperature, int mode, int32_t* out_tokens,
+                int32_t* out_n_accepted, int32_t* out_new_len, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* spec_verify plus the intermediate values, for parity checks (same
+ * arguments and semantics, slower).  Each probe pointer may be NULL:
+ *   out_px, out_qx  fp32 [B, gamma_max]: p_i(x_i), q_i(x_i) for every
+ *                   i < gamma_per_row[b] with a valid token (untouched
+ *                   otherwise; sampling only)
+ *   out_z           fp32 [B]: normaliser Z of the drawn distribution
+ *   out_m, out_s    fp32 [B, 2*gamma_max+1]: per vocabulary row (target
+ *                   rows 0..gamma_max, then draft rows 0..gamma_max-1) the
+ *                   largest raw logit and S = sum_j exp((l_j - max) / T)
+ *                   (GREEDY: out_m only, out_s holds the argmax as float) */
+int spec_verify_probe(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
+                      int gamma_max, int V, int dtype, float temperature, int mode,
+                      int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_new_len,
+                      void* workspace, size_t workspace_bytes, void* stream, float* out_px,
+                      float* out_qx, float* out_z, float* out_m, float* out_s);
+
+/* Launch plan of a call with these sizes (host only): fills out[0..7] with
+ * {workgroups, chunks per vocabulary row, chunk length, draw slices per
+ * row, slice length, lag rows, vocabulary rows per batch row, threads per
+ * workgroup}.  Returns SPEC_OK or an argument error. */
+int spec_verify_plan(int B, int gamma_max, int V, int dtype, int mode, int64_t* out);
+
+/* Process-wide override of the launch tuning (for benchmarking sweeps):
+ * target bytes of one statistics chunk, elements of one draw slice, and the
+ * number of rows whose statistics run ahead of their draws.  0 keeps the
+ * default.  Changes spec_verify_workspace_bytes; not thread-safe against
+ * concurrent calls. */
+int spec_verify_tune(int chunk_bytes, int slice_elems, int lag_rows);
+
+/* Reads the workspace's diagnostic word (device -> host copy on `stream`,
+ * synchronous): bit 0 set if a draw ever gave up waiting for its row's
+ * decision (cannot happen in a correct launch), bit 1 set if a residual
+ * with zero mass fell back to p. */
+int spec_verify_diagnostics(const void* workspace, uint32_t* out_flags, void* stream);
+
+const char* spec_verify_strerror(int status);
+int spec_verify_version(void);
+
+/* Streaming-read bandwidth probe: reads `bytes` (a multiple of 16) from
+ * src, writes one float per workgroup into out (at least
+ * spec_probe_read_blocks(bytes) floats).  Used to measure the box's
+ * achievable HBM read rate next to the 8 TB/s specification. */
+int spec_probe_read(const void* src, size_t bytes, float* out, void* stream);
+int spec_probe_read_blocks(size_t bytes);
+
+/* Plain copy of `bytes` (a multiple of 16) from src to dst: the reference
+ * kernel of known traffic against which hardware byte counters are scaled. */
+int spec_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,167 @@
+"""Comparison of a GPU verify result with the oracle (test infrastructure).
+
+Acceptance rule:
+  * greedy: tokens, accepted counts and new lengths bit-exact;
+  * sampling: probabilities p_i(x_i), q_i(x_i) within 1e-5 relative (values
+    below 1e-30 within 1e-35 absolute, where fp32 exp loses relative
+    accuracy and no decision depends on them); every row whose tokens,
+    count or new length differ must be attributable to rounding: its first
+    divergence is either an accept decision with |u - p/q| < 1e-5, or a draw
+    where the oracle's normalised CDF between the two tokens stays within
+    1e-5 of u (and the GPU's token has positive weight).
+  * the number of such rows must stay within what fp32 weights allow.  A
+    draw weight carries about 1e-7 relative rounding; with 10^5 tokens the
+    CDF steps are ~1e-5 apart, so u falls between the fp32 and the exact
+    boundary for ~1e-4..3e-4 of the rows (measured by emulating fp32 weights
+    with fp64 sums against this oracle on the five workloads).  The count is
+    checked against a Poisson bound at rate MISMATCH_RATE, exceeded by
+    chance with probability 1e-4.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+
+TOL = 1e-5
+TINY, TINY_ABS = 1e-30, 1e-35
+MISMATCH_RATE = 5e-4
+
+
+def allowed_mismatches(rows: int) -> int:
+    from scipy.stats import poisson
+    return int(poisson.isf(1e-4, MISMATCH_RATE * rows)) if rows else 0
+
+
+@dataclass
+class Report:
+    rows: int = 0
+    mismatched: list = field(default_factory=list)      # (row, reason)
+    attributed: list = field(default_factory=list)      # (row, reason)
+    prob_errors: list = field(default_factory=list)     # (row, pos, what, gpu, oracle)
+    max_rel_p: float = 0.0
+    max_rel_stats: float = 0.0
+
+    @property
+    def ok(self) -> bool:
+        unexplained = len(self.mismatched) - len(self.attributed)
+        rate_ok = len(self.mismatched) <= allowed_mismatches(self.rows)
+        return unexplained == 0 and rate_ok and not self.prob_errors
+
+    def merge(self, other: "Report"):
+        self.rows += other.rows
+        self.mismatched += other.mismatched
+        self.attributed += other.attributed
+        self.prob_errors += other.prob_errors
+        self.max_rel_p = max(self.max_rel_p, other.max_rel_p)
+        self.max_rel_stats = max(self.max_rel_stats, other.max_rel_stats)
+
+    def summary(self) -> str:
+        return (f"rows={self.rows} mismatched={len(self.mismatched)} "
+                f"(allowed {allowed_mismatches(self.rows)}) "
+                f"attributed={len(self.attributed)} prob_errors={len(self.prob_errors)} "
+                f"max_rel_p={self.max_rel_p:.2e} max_rel_stats={self.max_rel_stats:.2e}")
+
+
+def _close(gpu, ref):
+    ref = np.asarray(ref, np.float64)
+    gpu = np.asarray(gpu, np.float64)
+    tiny = np.abs(ref) < TINY
+    err = np.abs(gpu - ref)
+    ok = np.where(tiny, err <= TINY_ABS, err <= TOL * np.abs(ref))
+    rel = np.where(tiny, 0.0, err / np.where(tiny, 1.0, np.abs(ref)))
+    return ok, rel
+
+
+def run_oracle(case, threads=0):
+    mode = oracle.GREEDY if case.mode == "greedy" else oracle.SAMPLE
+    return oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
+                         case.kv_len, temperature=case.T, mode=mode, threads=threads)
+
+
+def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) -> Report:
+    """Compare GPU outputs (numpy) for one batch with the oracle."""
+    if ref is None:
+        ref = run_oracle(case)
+    rep = Report(rows=case.B)
+    greedy = case.mode == "greedy"
+    if greedy:
+        for b in range(case.B):
+            if (n_acc[b] != ref.n_accepted[b] or new_len[b] != ref.new_len[b]
+                    or not np.array_equal(tokens[b], ref.tokens[b])):
+                rep.mismatched.append((row_offset + b, "greedy differs"))
+        return rep
+
+    if probe is not None:
+        g = case.gamma
+        for b in range(case.B):
+            if ref.n_accepted[b] < 0:
+                continue
+            for i in range(int(g[b])):
+                if np.isnan(ref.px[b, i]):
+                    continue
+                for what, gv, ov in (("p", probe["px"][b, i], ref.px[b, i]),
+                                     ("q", probe["qx"][b, i], ref.qx[b, i])):
+                    ok, rel = _close(gv, ov)
+                    rep.max_rel_p = max(rep.max_rel_p, float(rel))
+                    if not ok:
+                        rep.prob_errors.append((row_offset + b, i, what, float(gv), float(ov)))
+            # per vocabulary row statistics: max exact, S within 1e-5 relative
+            nr = 2 * int(g[b]) + 1
+            slots = list(range(int(g[b]) + 1)) + [case.G + 1 + i for i in range(int(g[b]))]
+            for sl in slots[:nr]:
+                if probe["m"][b, sl] != np.float32(ref.m[b, sl]):
+                    rep.prob_errors.append((row_offset + b, sl, "m", float(probe["m"][b, sl]),
+                                            float(ref.m[b, sl])))
+                ok, rel = _close(probe["s"][b, sl], ref.s[b, sl])
+                rep.max_rel_stats = max(rep.max_rel_stats, float(rel))
+                if not ok:
+                    rep.prob_errors.append((row_offset + b, sl, "S", float(probe["s"][b, sl]),
+                                            float(ref.s[b, sl])))
+            # normaliser of the drawn distribution
+            zr, zg = ref.z[b], probe["z"][b]
+            if not (abs(zg - zr) <= TOL * abs(zr) + 1e-6):
+                rep.prob_errors.append((row_offset + b, -1, "Z", float(zg), float(zr)))
+
+    for b in range(case.B):
+        same = (n_acc[b] == ref.n_accepted[b] and new_len[b] == ref.new_len[b]
+                and np.array_equal(tokens[b], ref.tokens[b]))
+        if same:
+            continue
+        rep.mismatched.append((row_offset + b, "sample differs"))
+        why = _attribute(case, b, int(n_acc[b]), tokens[b], ref)
+        if why:
+            rep.attributed.append((row_offset + b, why))
+    return rep
+
+
+def _attribute(case, b, n_gpu, tok_gpu, ref):
+    n_or = int(ref.n_accepted[b])
+    if n_gpu < 0 or n_or < 0:
+        return None
+    u = case.uniforms[b].astype(np.float64)
+    if n_gpu != n_or:
+        k = min(n_gpu, n_or)
+        ratio = ref.px[b, k] / ref.qx[b, k] if ref.qx[b, k] > 0 else np.inf
+        if abs(u[k] - ratio) < TOL and np.array_equal(tok_gpu[:k], ref.tokens[b, :k]):
+            return f"accept decision at {k}: |u - p/q| = {abs(u[k] - ratio):.2e}"
+        return None
+    if not np.array_equal(tok_gpu[:n_or], ref.tokens[b, :n_or]):
+        return None
+    jg, jo = int(tok_gpu[n_or]), int(ref.tokens[b, n_or])
+    if not (0 <= jg < case.V):
+        return None
+    cdf, pos = oracle.draw_cdf(case.target, case.draft, case.tokens, case.uniforms, case.gamma, b,
+                               temperature=case.T)
+    if pos != n_or:
+        return None
+    us = u[n_or + 1] if n_or < case.gamma[b] else u[int(case.gamma[b])]
+    lo, hi = min(jg, jo), max(jg, jo)
+    f_lo = cdf[lo]
+    f_hi1 = cdf[hi - 1]
+    w_gpu = cdf[jg] - (cdf[jg - 1] if jg > 0 else 0.0)
+    if f_lo >= us - TOL and f_hi1 <= us + TOL and w_gpu > 0:
+        return f"draw boundary: u={us:.7f} F[{lo}]={f_lo:.7f} F[{hi - 1}]={f_hi1:.7f}"
+    return None

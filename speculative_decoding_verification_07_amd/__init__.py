@@ -1,0 +1,231 @@
+"""MI355X (gfx950) batched verify step of speculative decoding.
+
+Thin ctypes binding over the C ABI declared in include/spec_verify.h.  Every
+step of the verify runs in the HIP kernels of libspecverify.so; this module
+only checks tensor shapes, allocates outputs with torch, and passes raw device
+pointers and the current HIP stream.  There is no CPU fallback: importing the
+binding when the library has not been built raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SAMPLE, GREEDY = 0, 1
+F32, BF16 = 0, 1
+OK, ERR_NULL, ERR_SHAPE, ERR_ARG, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5, -100
+GAMMA_MAX_LIMIT = 63
+
+EXPORTS = (
+    "spec_verify", "spec_verify_probe", "spec_verify_workspace_bytes",
+    "spec_verify_workspace_reset", "spec_verify_plan", "spec_verify_tune",
+    "spec_verify_diagnostics", "spec_verify_strerror", "spec_verify_version",
+    "spec_probe_read", "spec_probe_read_blocks", "spec_probe_copy",
+)
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def load():
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (__graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    verify_args = [P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, P, P, P, P, sz, P]
+    lib.spec_verify.argtypes = verify_args
+    lib.spec_verify.restype = i32
+    lib.spec_verify_probe.argtypes = verify_args + [P, P, P, P, P]
+    lib.spec_verify_probe.restype = i32
+    lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.spec_verify_workspace_bytes.restype = sz
+    lib.spec_verify_workspace_reset.argtypes = [P, sz, P]
+    lib.spec_verify_workspace_reset.restype = i32
+    lib.spec_verify_plan.argtypes = [i32, i32, i32, i32, i32, P]
+    lib.spec_verify_plan.restype = i32
+    lib.spec_verify_tune.argtypes = [i32, i32, i32]
+    lib.spec_verify_tune.restype = i32
+    lib.spec_verify_diagnostics.argtypes = [P, P, P]
+    lib.spec_verify_diagnostics.restype = i32
+    lib.spec_verify_strerror.argtypes = [i32]
+    lib.spec_verify_strerror.restype = ctypes.c_char_p
+    lib.spec_verify_version.argtypes = []
+    lib.spec_verify_version.restype = i32
+    lib.spec_probe_read.argtypes = [P, sz, P, P]
+    lib.spec_probe_read.restype = i32
+    lib.spec_probe_read_blocks.argtypes = [sz]
+    lib.spec_probe_read_blocks.restype = i32
+    lib.spec_probe_copy.argtypes = [P, P, sz, P]
+    lib.spec_probe_copy.restype = i32
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().spec_verify_strerror(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise SpecVerifyError(status, what)
+
+
+def workspace_bytes(B: int, gamma_max: int, V: int, dtype: int, mode: int) -> int:
+    return int(load().spec_verify_workspace_bytes(B, gamma_max, V, dtype, mode))
+
+
+def plan(B: int, gamma_max: int, V: int, dtype: int, mode: int) -> dict:
+    out = (ctypes.c_int64 * 8)()
+    _check(load().spec_verify_plan(B, gamma_max, V, dtype, mode, out), "spec_verify_plan")
+    keys = ("workgroups", "chunks", "chunk_len", "slices", "slice_len", "lag_rows",
+            "vocab_rows", "threads")
+    return dict(zip(keys, (int(v) for v in out)))
+
+
+def tune(chunk_bytes: int = 0, slice_elems: int = 0, lag_rows: int = 0):
+    _check(load().spec_verify_tune(chunk_bytes, slice_elems, lag_rows), "spec_verify_tune")
+
+
+# ---------------------------------------------------------------- torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("logits must be torch.float32 or torch.bfloat16")
+
+
+class Workspace:
+    """Device workspace: a torch byte tensor zero-filled once by the
+    library's fill kernel; every completed call leaves it zero again."""
+
+    def __init__(self, nbytes: int, device="cuda", stream=None):
+        torch = _torch()
+        self.nbytes = int(nbytes)
+        self.tensor = torch.empty(max(self.nbytes, 256) + 256, dtype=torch.uint8, device=device)
+        base = self.tensor.data_ptr()
+        self.offset = (-base) % 256
+        self.ptr = base + self.offset
+        _check(load().spec_verify_workspace_reset(ctypes.c_void_p(self.ptr), self.nbytes,
+                                                  _stream_handle(stream)), "workspace reset")
+
+    def diagnostics(self, stream=None) -> int:
+        flags = ctypes.c_uint32(0)
+        _check(load().spec_verify_diagnostics(ctypes.c_void_p(self.ptr), ctypes.byref(flags),
+                                              _stream_handle(stream)), "diagnostics")
+        return int(flags.value)
+
+
+def _shape_check(target, draft, tokens, uniforms, gamma, kv_len, mode):
+    if target.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma_max+1, V]")
+    B, G1, V = target.shape
+    G = G1 - 1
+    for name, t in (("target_logits", target), ("draft_logits", draft), ("draft_tokens", tokens),
+                    ("uniforms", uniforms), ("gamma_per_row", gamma), ("kv_len_in", kv_len)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    if draft is not None and (tuple(draft.shape) != (B, G, V) or draft.dtype != target.dtype):
+        raise ValueError("draft_logits must be [B, gamma_max, V] with the target's dtype")
+    if tokens is not None and tuple(tokens.shape) != (B, G):
+        raise ValueError("draft_tokens must be int32 [B, gamma_max]")
+    if uniforms is not None and tuple(uniforms.shape) != (B, G + 1):
+        raise ValueError("uniforms must be float32 [B, gamma_max+1]")
+    if tuple(gamma.shape) != (B,):
+        raise ValueError("gamma_per_row must be int32 [B]")
+    if kv_len is not None and tuple(kv_len.shape) != (B,):
+        raise ValueError("kv_len_in must be int32 [B]")
+    return B, G, V
+
+
+def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in=None,
+           *, temperature: float = 1.0, mode: int = SAMPLE, workspace: Workspace | None = None,
+           out=None, stream=None, probe: bool = False):
+    """Run spec_verify on torch device tensors.
+
+    Returns (tokens [B, G+1] int32, n_accepted [B] int32, new_len [B] int32),
+    plus a dict of probe tensors (px, qx, z, m, s) when probe=True.  `out`
+    may pass preallocated (tokens, n_accepted, new_len).  The call is
+    asynchronous on `stream` (default: torch's current stream)."""
+    torch = _torch()
+    lib = load()
+    B, G, V = _shape_check(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row,
+                           kv_len_in, mode)
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    need = workspace_bytes(B, G, V, dt, mode)
+    if workspace is None:
+        workspace = Workspace(need, device=dev, stream=stream)
+    if out is None:
+        out = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    tok, nacc, nlen = out
+    args = [_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
+            _ptr(gamma_per_row), _ptr(kv_len_in), B, G, V, dt, float(temperature), int(mode),
+            _ptr(tok), _ptr(nacc), _ptr(nlen), ctypes.c_void_p(workspace.ptr),
+            workspace.nbytes, _stream_handle(stream)]
+    if not probe:
+        _check(lib.spec_verify(*args), "spec_verify")
+        return tok, nacc, nlen
+    nan = float("nan")
+    pr = {
+        "px": torch.full((B, G), nan, dtype=torch.float32, device=dev),
+        "qx": torch.full((B, G), nan, dtype=torch.float32, device=dev),
+        "z": torch.full((B,), nan, dtype=torch.float32, device=dev),
+        "m": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
+        "s": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
+    }
+    _check(lib.spec_verify_probe(*args, _ptr(pr["px"]), _ptr(pr["qx"]), _ptr(pr["z"]),
+                                 _ptr(pr["m"]), _ptr(pr["s"])), "spec_verify_probe")
+    return tok, nacc, nlen, pr
+
+
+def probe_read(src, out=None, stream=None):
+    """Streaming read of a device tensor (bandwidth probe)."""
+    torch = _torch()
+    nbytes = src.numel() * src.element_size()
+    nb = int(load().spec_probe_read_blocks(nbytes))
+    if out is None:
+        out = torch.empty(nb, dtype=torch.float32, device=src.device)
+    _check(load().spec_probe_read(_ptr(src), nbytes, _ptr(out), _stream_handle(stream)),
+           "spec_probe_read")
+    return out
+
+
+def probe_copy(src, dst, stream=None):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("destination too small")
+    _check(load().spec_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream_handle(stream)),
+           "spec_probe_copy")

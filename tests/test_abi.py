@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/spec_verify.h declares, and rejects bad arguments with the documented
+status before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_07_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+# stand-in addresses: validation never dereferences them
+A = 0x10000
+A2 = 0x20000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return sv.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(spec_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(sv.EXPORTS) == set(names)
+
+
+def test_version_and_strerror(lib):
+    assert lib.spec_verify_version() >= 100
+    for code in (sv.OK, sv.ERR_NULL, sv.ERR_SHAPE, sv.ERR_ARG, sv.ERR_WORKSPACE, sv.ERR_ALIGN):
+        assert sv.strerror(code)
+    assert sv.strerror(12345) == "unknown status"
+
+
+def _call(lib, **kw):
+    a = dict(tgt=A, dft=A, tok=A, uni=A, gam=A, kv=None, B=4, G=4, V=1000, dtype=sv.BF16,
+             T=1.0, mode=sv.SAMPLE, out_tok=A, out_n=A, out_len=A, ws=A2, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.spec_verify(a["tgt"], a["dft"], a["tok"], a["uni"], a["gam"], a["kv"], a["B"],
+                           a["G"], a["V"], a["dtype"], a["T"], a["mode"], a["out_tok"],
+                           a["out_n"], a["out_len"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), sv.ERR_SHAPE), (dict(B=-3), sv.ERR_SHAPE), (dict(V=0), sv.ERR_SHAPE),
+    (dict(V=(1 << 30) + 1), sv.ERR_SHAPE), (dict(G=-1), sv.ERR_SHAPE), (dict(G=64), sv.ERR_SHAPE),
+    (dict(dtype=2), sv.ERR_ARG), (dict(mode=7), sv.ERR_ARG),
+    (dict(tgt=None), sv.ERR_NULL), (dict(gam=None), sv.ERR_NULL), (dict(out_tok=None), sv.ERR_NULL),
+    (dict(out_n=None), sv.ERR_NULL), (dict(out_len=None), sv.ERR_NULL), (dict(tok=None), sv.ERR_NULL),
+    (dict(dft=None), sv.ERR_NULL), (dict(uni=None), sv.ERR_NULL),
+    (dict(T=0.0), sv.ERR_ARG), (dict(T=-1.0), sv.ERR_ARG), (dict(T=float("nan")), sv.ERR_ARG),
+    (dict(T=float("inf")), sv.ERR_ARG),
+    (dict(ws=None), sv.ERR_WORKSPACE), (dict(ws_bytes=16), sv.ERR_WORKSPACE),
+    (dict(tgt=A + 1), sv.ERR_ALIGN), (dict(dtype=sv.F32, tgt=A + 2), sv.ERR_ALIGN),
+    (dict(dft=A + 1), sv.ERR_ALIGN), (dict(tok=A + 2), sv.ERR_ALIGN), (dict(kv=A + 1), sv.ERR_ALIGN),
+    (dict(out_n=A + 3), sv.ERR_ALIGN), (dict(ws=A2 + 16), sv.ERR_ALIGN),
+])
+def test_argument_errors(lib, kw, code):
+    assert _call(lib, **kw) == code
+
+
+def test_null_tolerated_where_documented(lib):
+    """Greedy may omit draft logits and uniforms, gamma_max = 0 may omit the
+    draft tokens: validation must get past those (checked here with a
+    too-small workspace so that nothing is launched)."""
+    assert _call(lib, mode=sv.GREEDY, dft=None, uni=None, ws_bytes=1) == sv.ERR_WORKSPACE
+    assert _call(lib, G=0, tok=None, dft=None, ws_bytes=1) == sv.ERR_WORKSPACE
+    assert _call(lib, mode=sv.GREEDY, T=0.0, ws_bytes=1) == sv.ERR_WORKSPACE
+
+
+def test_probe_pointer_pairing(lib):
+    r = lib.spec_verify_probe(A, A, A, A, A, None, 4, 4, 1000, sv.BF16, 1.0, sv.SAMPLE, A, A, A,
+                              A2, 1 << 30, None, A, None, None, None, None)
+    assert r == sv.ERR_NULL
+
+
+def test_workspace_bytes_and_plan(lib):
+    assert sv.workspace_bytes(0, 4, 100, sv.BF16, sv.SAMPLE) == 0
+    assert sv.workspace_bytes(4, 64, 100, sv.BF16, sv.SAMPLE) == 0
+    small = sv.workspace_bytes(64, 4, 128256, sv.BF16, sv.SAMPLE)
+    big = sv.workspace_bytes(256, 8, 151936, sv.BF16, sv.SAMPLE)
+    assert 0 < small < big < 64 << 20
+    assert sv.workspace_bytes(64, 4, 128256, sv.BF16, sv.GREEDY) < small
+    p = sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)
+    assert p["vocab_rows"] == 9 and p["threads"] == 256
+    assert p["chunks"] * p["chunk_len"] >= 128256 > (p["chunks"] - 1) * p["chunk_len"]
+    assert p["chunk_len"] % 8 == 0
+    assert p["slices"] * p["slice_len"] >= 128256 > (p["slices"] - 1) * p["slice_len"]
+    assert p["workgroups"] == 64 * (p["vocab_rows"] * p["chunks"] + p["slices"])
+    g = sv.plan(64, 4, 128256, sv.BF16, sv.GREEDY)
+    assert g["slices"] == 0 and g["vocab_rows"] == 5
+    f = sv.plan(1, 4, 50257, sv.F32, sv.SAMPLE)
+    assert f["chunk_len"] % 4 == 0
+
+
+def test_tune_changes_plan_and_restores(lib):
+    base = sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)
+    try:
+        sv.tune(chunk_bytes=65536, slice_elems=4096, lag_rows=3)
+        p = sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)
+        assert p["chunks"] < base["chunks"] and p["slice_len"] == 4096 and p["lag_rows"] == 3
+        with pytest.raises(sv.SpecVerifyError):
+            sv.tune(chunk_bytes=-1)
+    finally:
+        sv.tune()
+    assert sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE) == base
+
+
+def test_probe_kernel_argument_errors(lib):
+    assert lib.spec_probe_read(None, 1024, A, None) == sv.ERR_NULL
+    assert lib.spec_probe_read(A, 1000, A, None) == sv.ERR_ALIGN
+    assert lib.spec_probe_copy(A, A2 + 8, 1024, None) == sv.ERR_ALIGN
+    assert lib.spec_verify_workspace_reset(None, 64, None) == sv.ERR_NULL
+    assert lib.spec_verify_diagnostics(None, A, None) == sv.ERR_NULL
+    assert lib.spec_probe_read_blocks(65536) == 1 and lib.spec_probe_read_blocks(65537) == 2
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    t = torch.zeros((2, 3, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sv.verify(t, t[:, :2].contiguous(), torch.zeros((2, 2), dtype=torch.int32),
+                  torch.zeros((2, 3)), torch.zeros(2, dtype=torch.int32))
