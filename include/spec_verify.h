@@ -65,11 +65,13 @@ enum spec_status {
  * function of its arguments and of the tuning override).  Returns 0 for
  * sizes spec_verify would reject.
  *
- * The workspace holds per-chunk softmax statistics, per-row decisions, and
- * self-resetting counters.  It must be zero-filled once before its first use
- * (spec_verify_workspace_reset, or any zero fill); every call that completes
- * leaves its counters at zero again, so one workspace serves any sequence of
- * stream-ordered calls with sizes up to the ones it was sized for. */
+ * The workspace holds per-chunk softmax statistics, per-slice draw sums and,
+ * at its end, one block of self-resetting counters per batch row.  It must be
+ * zero-filled once before its first use (spec_verify_workspace_reset, or any
+ * zero fill).  Every call that completes leaves the counters at zero again.
+ * A workspace is identified by its pointer and size: pass both unchanged on
+ * every call, and it serves any sequence of stream-ordered calls, of any
+ * shapes, whose spec_verify_workspace_bytes does not exceed its size. */
 size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype, int mode);
 
 /* Zero-fills `bytes` of a workspace with a small fill kernel on `stream`

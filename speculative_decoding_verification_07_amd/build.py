@@ -12,6 +12,9 @@ OUT = os.path.join(_HERE, "libspecverify.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+    # no implicit a*b+c fusion: every fused multiply-add is written as fmaf,
+    # so a weight computed in two places is bit-identical in both
+    "-ffp-contract=off",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

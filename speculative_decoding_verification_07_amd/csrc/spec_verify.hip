@@ -43,8 +43,17 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;            // 16-byte loads in flight per thread
 constexpr int kSub = kThreads;        // draw: elements per sub-slice
 constexpr int kMaxSubs = 64;          // draw: sub-slices per slice
-constexpr unsigned kFlagDraw = 1u, kFlagNone = 2u;
+constexpr unsigned kFlagStats = 1u, kFlagNone = 2u;  // row flag values
 constexpr unsigned kDiagSpin = 1u, kDiagZeroResid = 2u;
+// Per-row counters (statistics ticket, draw ticket, row flag) each sit on
+// their own 256-byte line.  The row blocks are laid out downwards from the
+// end of the workspace, so a counter's address depends only on the workspace
+// (pointer and size) and the row, never on the call's sizes: calls of any
+// shape can share a workspace, and none finds another call's data where its
+// counters belong.
+constexpr int kCounterStride = 64;                   // unsigned words per counter line
+constexpr int kRowBlock = 3 * kCounterStride;        // words per row block
+constexpr size_t kRowBlockBytes = kRowBlock * sizeof(unsigned);
 #define NEG_INF (-__builtin_inff())
 
 struct Tuning {
@@ -63,7 +72,7 @@ struct Plan {
   int L;         // lag rows
   int NP;        // statistics slots per batch row = NR * NC
   int64_t total; // workgroups
-  size_t off_rowt, off_drawt, off_flag, off_rec, off_part, off_ssum, off_sub, bytes;
+  size_t off_part, off_sub, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -95,14 +104,9 @@ int make_plan(int B, int G, int V, int dtype, int mode, Plan* p) {
   p->total = (int64_t)B * (p->NP + p->ND);
   if (p->total >= (int64_t)1 << 31) return SPEC_ERR_SHAPE;
   size_t off = 256;  // header: [0] unused, [1] diagnostic word
-  p->off_rowt = off; off = align256(off + sizeof(unsigned) * B);
-  p->off_drawt = off; off = align256(off + sizeof(unsigned) * B);
-  p->off_flag = off; off = align256(off + sizeof(unsigned) * B);
-  p->off_rec = off; off = align256(off + sizeof(float) * 8 * B);
   p->off_part = off; off = align256(off + sizeof(float2) * (size_t)B * p->NP);
-  p->off_ssum = off; off = align256(off + sizeof(double) * (size_t)B * (p->ND ? p->ND : 1));
   p->off_sub = off; off = align256(off + sizeof(double) * (size_t)B * (p->ND ? p->ND : 1) * (sl / kSub));
-  p->bytes = off;
+  p->bytes = off + kRowBlockBytes * (size_t)B + 256;  // + counter blocks + end alignment
   return SPEC_OK;
 }
 
@@ -123,12 +127,8 @@ struct Args {
   float* pr_m;
   float* pr_s;
   unsigned* hdr;
-  unsigned* rowt;
-  unsigned* drawt;
-  unsigned* flag;
-  float* rec;
+  unsigned* ctr_end;  // 256-byte aligned end of the workspace; row blocks below it
   float2* part;
-  double* ssum;
   double* sub;
   int B, G, V, NR, NC, CH, ND, SL, L, NP;
   float k2;  // log2(e) / T
@@ -180,21 +180,28 @@ struct Span {
 };
 
 // ------------------------------------------------------------------ reductions
-// (m, S) with S relative to m in units of 2^((l - m) k2); m = -inf means empty.
+// Softmax statistics are kept in the scaled domain z = l * k2 (k2 = log2(e)/T):
+// a pair (m, S) has m = the largest raw logit and S = sum_j 2^(l_j k2 - R(m)),
+// where R(m) = fl(m * k2) is the rounded reference.  Every weight is formed
+// as 2^fma(l, k2, -R) against the same R that its sum used, so the rounding of
+// R is a factor common to a weight and its normaliser and cancels in p.
+__device__ __forceinline__ float ref_of(float m, float k2) { return m * k2; }
+
 __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2, float k2) {
-  float M = fmaxf(m, m2);
-  float a = (m == NEG_INF) ? 0.f : s * ex2((m - M) * k2);
-  float b = (m2 == NEG_INF) ? 0.f : s2 * ex2((m2 - M) * k2);
+  const float M = fmaxf(m, m2);
+  const float R = ref_of(M, k2);
+  const float a = (m == NEG_INF) ? 0.f : s * ex2(ref_of(m, k2) - R);
+  const float b = (m2 == NEG_INF) ? 0.f : s2 * ex2(ref_of(m2, k2) - R);
   m = M;
   s = a + b;
 }
 
 __device__ __forceinline__ void ms_fold(float& m, float& s, float v, float k2) {
   if (v > m) {
-    s = (m == NEG_INF) ? 0.f : s * ex2((m - v) * k2);
+    s = (m == NEG_INF) ? 0.f : s * ex2(ref_of(m, k2) - ref_of(v, k2));
     m = v;
   }
-  if (m != NEG_INF) s += ex2((v - m) * k2);
+  if (m != NEG_INF) s += ex2(fmaf(v, k2, -ref_of(m, k2)));
 }
 
 // argmax pair: larger value wins, equal values go to the lower index.
@@ -278,10 +285,11 @@ __device__ void stats_range(const void* row, int lo, int hi, float k2, float& m,
       }
     }
     if (bm > m) {
-      s = (m == NEG_INF) ? 0.f : s * ex2((m - bm) * k2);
+      s = (m == NEG_INF) ? 0.f : s * ex2(ref_of(m, k2) - ref_of(bm, k2));
       m = bm;
     }
     if (m != NEG_INF) {
+      const float R = ref_of(m, k2);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         int k = k0 + u * kThreads + t;
@@ -289,7 +297,7 @@ __device__ void stats_range(const void* row, int lo, int hi, float k2, float& m,
           float f[E::kVec];
           E::unpack(raw[u], f);
 #pragma unroll
-          for (int e = 0; e < E::kVec; ++e) s += ex2((f[e] - m) * k2);
+          for (int e = 0; e < E::kVec; ++e) s += ex2(fmaf(f[e], k2, -R));
         }
       }
     }
@@ -334,30 +342,57 @@ __device__ void argmax_range(const void* row, int lo, int hi, float& bv, int& bi
 // Weights are fp32; their sums and prefix sums are accumulated in fp64 so
 // that the CDF is as exact as the fp32 weights allow.
 struct DrawParams {
-  float mt, st_inv, md, sd_inv, k2;
+  float rt, st_inv, rd, sd_inv, k2;  // references R(m) of target/draft row n, 1/S
   int kind;
 };
 
 __device__ __forceinline__ float draw_weight(const DrawParams& d, float t, float q_logit) {
-  const float et = ex2((t - d.mt) * d.k2);
+  const float et = ex2(fmaf(t, d.k2, -d.rt));
   if (d.kind == 1) {
     const float p = et * d.st_inv;
-    const float q = ex2((q_logit - d.md) * d.k2) * d.sd_inv;
+    const float q = ex2(fmaf(q_logit, d.k2, -d.rd)) * d.sd_inv;
     return fmaxf(p - q, 0.f);
   }
   return d.kind == 2 ? et * d.st_inv : et;
 }
 
-// ------------------------------------------------------------------ fences
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// ------------------------------------------------------------------ hand-off
+// Workgroups pass data to each other through the workspace without writing
+// back the L2 (an agent-scope release fence does that, costs microseconds and
+// serialises across the device; so does an acquire's L2 invalidate).  A
+// writer stores the data with agent-scope
+// atomic stores, which complete only once the data is visible to every XCD,
+// waits for them to complete (publish), and only then takes its ticket or
+// sets its flag.  A reader that observes the last ticket or the flag does an
+// agent-scope atomic loads for the data, which are served coherently at the
+// device level; so no cache write-back or invalidate is ever needed.
+__device__ __forceinline__ void publish() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void put64(void* p, uint64_t v) {
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_f2(float2* p, float2 v) {
+  put64(p, (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32));
+}
+__device__ __forceinline__ void put_d(double* p, double v) {
+  put64(p, (uint64_t)__double_as_longlong(v));
+}
+__device__ __forceinline__ uint64_t get64(const void* p) {
+  return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 get_f2(const float2* p) {
+  const uint64_t v = get64(p);
+  return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
+}
+__device__ __forceinline__ double get_d(const double* p) {
+  return __longlong_as_double((long long)get64(p));
+}
 __device__ __forceinline__ unsigned ticket(unsigned* p) {
   return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_rel(unsigned* p, unsigned v) {
+__device__ __forceinline__ void put_u(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned load_rlx(unsigned* p) {
+__device__ __forceinline__ unsigned get_u(unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -372,153 +407,170 @@ template <int DT>
 __device__ __forceinline__ const void* row_ptr(const void* base, int64_t off) {
   return (const char*)base + off * Elt<DT>::kBytes;
 }
+enum { kRowTicket = 0, kDrawTicket = 1, kRowFlag = 2 };
+__device__ __forceinline__ unsigned* counter(const Args& a, int which, int b) {
+  return a.ctr_end - (int64_t)(b + 1) * kRowBlock + which * kCounterStride;
+}
 
-struct LdsDecide {
-  float m[2 * SPEC_GAMMA_MAX_LIMIT + 1];
-  float s[2 * SPEC_GAMMA_MAX_LIMIT + 1];
+// The row's decision, shared through LDS.
+struct Decision {
+  int n;        // accepted drafts
+  int dead;     // 1: data error, the row holds the sentinel
+  int resid;    // 1: draw from the residual at n, 0: bonus draw from p_g
+  float ustar;  // uniform of the draw
+  float mt, st, md, sd;  // (max, exp-sum) of target row n and draft row n
 };
+
+constexpr int kSubChunks = 4;  // final draw: sub-slice sums staged per thread
 
 struct Lds {
   double red_d[kWaves];
   double subs[kMaxSubs];
+  double fsub[kThreads * kSubChunks];
   double fin_base;
   float red[2 * kWaves];
+  float m[2 * SPEC_GAMMA_MAX_LIMIT + 1];
+  float s[2 * SPEC_GAMMA_MAX_LIMIT + 1];
+  Decision dec;
   unsigned flag;
   int last;
   int cand, lastpos;
-  LdsDecide dec;
 };
 
-__device__ void write_sentinel(const Args& a, int b) {
-  for (int i = threadIdx.x; i <= a.G; i += kThreads) a.out_tok[(int64_t)b * (a.G + 1) + i] = -1;
-  if (threadIdx.x == 0) {
-    a.out_n[b] = -1;
-    a.out_len[b] = a.kv ? a.kv[b] : 0;
+// Draw-side inputs of one position, read before the row's statistics are
+// complete (they are immutable inputs): lane i of wave 0 holds x_i, u_i and
+// the target and draft logits at x_i.
+struct Gathered {
+  int x;
+  float tv, dv, u;
+};
+
+template <int DT, int MODE>
+__device__ Gathered gather_inputs(const Args& a, int b, int g) {
+  Gathered r{-1, 0.f, 0.f, 0.f};
+  const int lane = threadIdx.x;
+  if (threadIdx.x >= 64) return r;
+  if (lane < g) {
+    r.x = a.tok[(int64_t)b * a.G + lane];
+    if (MODE == SPEC_MODE_SAMPLE && (unsigned)r.x < (unsigned)a.V) {
+      r.tv = Elt<DT>::one(a.tgt, trow_off(a, b, lane) + r.x);
+      r.dv = Elt<DT>::one(a.dft, drow_off(a, b, lane) + r.x);
+    }
   }
+  if (MODE == SPEC_MODE_SAMPLE && lane <= g) r.u = a.uni[(int64_t)b * (a.G + 1) + lane];
+  return r;
 }
 
 // ------------------------------------------------------------------ decision
-// Run by the workgroup holding the row's last statistics ticket.
+// Merges the row's chunk statistics, runs every acceptance test at once and
+// finds the first rejection with a wave ballot.  Must be called by the whole
+// workgroup after an acquire; the result is in L.dec after the call.  With
+// write_out the row's outputs (all but the drawn token when sampling) and
+// probes are written.
 template <int DT, int MODE>
-__device__ void decide_row(const Args& a, Lds& L, int b, int g) {
+__device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, bool write_out) {
   constexpr bool kSample = MODE == SPEC_MODE_SAMPLE;
   const int t = threadIdx.x, lane = t & 63;
   const int nrows = kSample ? 2 * g + 1 : g + 1;
-  // wave 0: per-position gathers; lanes 0..G also hold the uniforms
-  int x = -1;
-  float tv = 0.f, dv = 0.f, u = 0.f;
-  if (t < 64) {
-    if (lane < g) {
-      x = a.tok[(int64_t)b * a.G + lane];
-      if ((unsigned)x < (unsigned)a.V && kSample) {
-        tv = Elt<DT>::one(a.tgt, trow_off(a, b, lane) + x);
-        dv = Elt<DT>::one(a.dft, drow_off(a, b, lane) + x);
-      }
-    }
-    if (kSample && lane <= g) u = a.uni[(int64_t)b * (a.G + 1) + lane];
-  }
-  // waves 1..: merge the chunk pairs of every needed vocabulary row
   for (int r = t - 64; r >= 0 && r < nrows; r += kThreads - 64) {
     const int slot = (r <= g) ? r : (a.G + 1 + (r - g - 1));
     const float2* pp = a.part + ((int64_t)b * a.NR + slot) * a.NC;
     if (kSample) {
       float m = NEG_INF, s = 0.f;
       for (int c = 0; c < a.NC; ++c) {
-        float2 v = pp[c];
+        const float2 v = get_f2(&pp[c]);
         ms_merge(m, s, v.x, v.y, a.k2);
       }
-      L.dec.m[slot] = m, L.dec.s[slot] = s;
+      L.m[slot] = m, L.s[slot] = s;
     } else {
       float v = NEG_INF;
       int i = 0x7fffffff;
       for (int c = 0; c < a.NC; ++c) {
-        float2 q = pp[c];
+        const float2 q = get_f2(&pp[c]);
         am_merge(v, i, q.x, __float_as_int(q.y));
       }
-      L.dec.m[slot] = v, L.dec.s[slot] = __int_as_float(i);
+      L.m[slot] = v, L.s[slot] = __int_as_float(i);
     }
   }
   __syncthreads();
-  if (t >= 64) return;
-
-  // probes of the merged statistics
-  if (a.pr_m) {
-    for (int r = lane; r < nrows; r += 64) {
-      const int slot = (r <= g) ? r : (a.G + 1 + (r - g - 1));
-      a.pr_m[(int64_t)b * (2 * a.G + 1) + slot] = L.dec.m[slot];
-      if (a.pr_s) a.pr_s[(int64_t)b * (2 * a.G + 1) + slot] = L.dec.s[slot];
-    }
-  }
-  // sampling needs every row to have a finite logit
-  bool dead = false;
-  if (kSample) {
-    for (int r = lane; r < nrows; r += 64) {
-      const int slot = (r <= g) ? r : (a.G + 1 + (r - g - 1));
-      dead |= (L.dec.m[slot] == NEG_INF);
-    }
-  }
-  const bool any_dead = __ballot(dead) != 0;
-
-  const bool valid = (unsigned)x < (unsigned)a.V;
-  bool fail = false;
-  if (lane < g) {
-    if (!valid) {
-      fail = true;
-    } else if (kSample) {
-      float p = ex2((tv - L.dec.m[lane]) * a.k2) / L.dec.s[lane];
-      const int ds = a.G + 1 + lane;
-      float q = ex2((dv - L.dec.m[ds]) * a.k2) / L.dec.s[ds];
-      if (a.pr_px) {
-        a.pr_px[(int64_t)b * a.G + lane] = p;
-        a.pr_qx[(int64_t)b * a.G + lane] = q;
-      }
-      fail = !(u * q < p);
-    } else {
-      fail = (x != __float_as_int(L.dec.s[lane]));
-    }
-  }
-  const unsigned long long mask = __ballot(fail);
-  const int n = mask ? (__ffsll((long long)mask) - 1) : g;
-  const bool bad_token = mask && (__shfl(valid ? 1 : 0, n, 64) == 0);
-  if (any_dead || bad_token) {
-    for (int i = lane; i <= a.G; i += 64) a.out_tok[(int64_t)b * (a.G + 1) + i] = -1;
-    if (lane == 0) {
-      a.out_n[b] = -1;
-      a.out_len[b] = a.kv ? a.kv[b] : 0;
-      if (kSample) {
-        fence_release();
-        store_rel(&a.flag[b], kFlagNone);
+  if (t < 64) {
+    if (write_out && a.pr_m) {
+      for (int r = lane; r < nrows; r += 64) {
+        const int slot = (r <= g) ? r : (a.G + 1 + (r - g - 1));
+        const float mm = L.m[slot];
+        a.pr_m[(int64_t)b * (2 * a.G + 1) + slot] = mm;
+        // sampling: S relative to the raw max, i.e. undo the rounding of R(m)
+        const float sv = kSample && mm != NEG_INF
+                             ? L.s[slot] * ex2(-fmaf(mm, a.k2, -ref_of(mm, a.k2)))
+                             : L.s[slot];
+        if (a.pr_s) a.pr_s[(int64_t)b * (2 * a.G + 1) + slot] = sv;
       }
     }
-    return;
-  }
-  const float ustar = __shfl(u, n < g ? n + 1 : g, 64);
-  // gamma_max <= 63, so lane i owns output position i (and holds x_i)
-  if (lane <= a.G && !(kSample && lane == n)) {
-    int v = -1;
-    if (lane < n)
-      v = x;
-    else if (lane == n)
-      v = __float_as_int(L.dec.s[n]);  // greedy: the target's argmax at n
-    a.out_tok[(int64_t)b * (a.G + 1) + lane] = v;
-  }
-  if (lane == 0) {
-    a.out_n[b] = n;
-    a.out_len[b] = (a.kv ? a.kv[b] : 0) + n;
+    // sampling needs every row to have a finite logit
+    bool dead = false;
     if (kSample) {
-      float* rc = a.rec + (int64_t)b * 8;
-      const int ts = n;                    // target slot n (or g: bonus)
-      const int ds = a.G + 1 + n;          // draft slot n (residual only)
-      rc[0] = __int_as_float(n);
-      rc[1] = __int_as_float(n < g ? 1 : 0);  // 1: residual, 0: bonus
-      rc[2] = ustar;
-      rc[3] = L.dec.m[ts];
-      rc[4] = L.dec.s[ts];
-      rc[5] = n < g ? L.dec.m[ds] : 0.f;
-      rc[6] = n < g ? L.dec.s[ds] : 1.f;
-      fence_release();
-      store_rel(&a.flag[b], kFlagDraw);
+      for (int r = lane; r < nrows; r += 64) {
+        const int slot = (r <= g) ? r : (a.G + 1 + (r - g - 1));
+        dead |= (L.m[slot] == NEG_INF);
+      }
     }
+    const bool any_dead = __ballot(dead) != 0;
+    const bool valid = (unsigned)in.x < (unsigned)a.V;
+    bool fail = false;
+    if (lane < g) {
+      if (!valid) {
+        fail = true;
+      } else if (kSample) {
+        const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.m[lane], a.k2))) / L.s[lane];
+        const int ds = a.G + 1 + lane;
+        const float q = ex2(fmaf(in.dv, a.k2, -ref_of(L.m[ds], a.k2))) / L.s[ds];
+        if (write_out && a.pr_px) {
+          a.pr_px[(int64_t)b * a.G + lane] = p;
+          a.pr_qx[(int64_t)b * a.G + lane] = q;
+        }
+        fail = !(in.u * q < p);
+      } else {
+        fail = (in.x != __float_as_int(L.s[lane]));
+      }
+    }
+    const unsigned long long mask = __ballot(fail);
+    const int n = mask ? (__ffsll((long long)mask) - 1) : g;
+    const bool bad_token = mask && (__shfl(valid ? 1 : 0, n, 64) == 0);
+    const bool sentinel = any_dead || bad_token;
+    const float ustar = __shfl(in.u, n < g ? n + 1 : g, 64);
+    if (write_out) {
+      // gamma_max <= 63, so lane i owns output position i (and holds x_i)
+      if (lane <= a.G && !(kSample && lane == n && !sentinel)) {
+        int v = -1;
+        if (!sentinel && lane < n)
+          v = in.x;
+        else if (!sentinel && lane == n)
+          v = __float_as_int(L.s[n]);  // greedy: the target's argmax at n
+        a.out_tok[(int64_t)b * (a.G + 1) + lane] = v;
+      }
+      if (lane == 0) {
+        const int kv = a.kv ? a.kv[b] : 0;
+        a.out_n[b] = sentinel ? -1 : n;
+        a.out_len[b] = sentinel ? kv : kv + n;
+      }
+    }
+    if (lane == 0) {
+      Decision d;
+      d.n = n, d.dead = sentinel, d.resid = n < g, d.ustar = ustar;
+      d.mt = L.m[n], d.st = L.s[n];
+      d.md = n < g ? L.m[a.G + 1 + n] : 0.f;
+      d.sd = n < g ? L.s[a.G + 1 + n] : 1.f;
+      L.dec = d;
+    }
+  }
+  __syncthreads();
+}
+
+__device__ void write_sentinel(const Args& a, int b) {
+  for (int i = threadIdx.x; i <= a.G; i += kThreads) a.out_tok[(int64_t)b * (a.G + 1) + i] = -1;
+  if (threadIdx.x == 0) {
+    a.out_n[b] = -1;
+    a.out_len[b] = a.kv ? a.kv[b] : 0;
   }
 }
 
@@ -594,12 +646,7 @@ __device__ void draw_slice(const Args& a, Lds& L, int b, int slot, const void* t
   }
   __syncthreads();
   double* sub = a.sub + ((int64_t)b * a.ND + slot) * (a.SL / kSub);
-  if (t < nsub) sub[t] = L.subs[t];
-  if (t == 0) {
-    double tot = 0.0;
-    for (int k = 0; k < nsub; ++k) tot += L.subs[k];
-    a.ssum[(int64_t)b * a.ND + slot] = tot;
-  }
+  if (t < nsub) put_d(&sub[t], L.subs[t]);
 }
 
 // Inclusive and exclusive block prefix sums of one double per thread, in a
@@ -662,63 +709,133 @@ __device__ int block_find(int count, double base, double tau, F val, Lds& L, dou
   return lastpos >= 0 ? -(1 + lastpos) : (int)0x80000000;
 }
 
-// Run by the row's last draw item.
+__device__ __forceinline__ DrawParams draw_params(const Decision& dc, float k2) {
+  return DrawParams{ref_of(dc.mt, k2), 1.f / dc.st, ref_of(dc.md, k2), 1.f / dc.sd, k2,
+                    dc.resid ? 1 : 0};
+}
+
+// Number of sub-slices of slice s.
+__device__ __forceinline__ int subs_in_slice(const Args& a, int s) {
+  const int lo = s * a.SL;
+  return (min(a.V, lo + a.SL) - lo + kSub - 1) / kSub;
+}
+
+// Sum Z of the row's sub-slice weights and the first sub-slice whose running
+// sum exceeds tau = u * Z, over the flattened (slice, sub-slice) array with
+// every entry prefetched at once (count <= kThreads * kSubChunks).  Returns
+// the flat index, or -(1 + last positive entry) when rounding leaves no hit.
+template <class F>
+__device__ int find_sub_prefetched(int count, float u, F val, Lds& L, double& base_out,
+                                   double& z_out) {
+  const int t = threadIdx.x;
+  // every entry is loaded at once and staged in LDS
+#pragma unroll
+  for (int c = 0; c < kSubChunks; ++c) {
+    const int i = c * kThreads + t;
+    L.fsub[i] = i < count ? val(i) : 0.0;
+  }
+  __syncthreads();
+  // pass 1: the total, in the same chunk order as the search
+  double z = 0.0;
+#pragma unroll 1
+  for (int c = 0; c < kSubChunks; ++c) {
+    double incl, excl, tot;
+    block_scan_d(L.fsub[c * kThreads + t], L.red_d, incl, excl, tot);
+    z += tot;
+  }
+  z_out = z;
+  const double tau = (double)u * z;
+  // pass 2: first entry whose running sum exceeds tau
+  double carry = 0.0;
+  int last = -1;
+#pragma unroll 1
+  for (int c = 0; c < kSubChunks; ++c) {
+    const int i = c * kThreads + t;
+    const double v = L.fsub[i];
+    double incl, excl, tot;
+    block_scan_d(v, L.red_d, incl, excl, tot);
+    if (t == 0) L.cand = 0x7fffffff, L.lastpos = -1;
+    __syncthreads();
+    const bool pos = i < count && v > 0.0;
+    if (pos && tau < carry + incl) atomicMin(&L.cand, i);
+    if (pos) atomicMax(&L.lastpos, i);
+    __syncthreads();
+    const int first = L.cand;
+    if (L.lastpos >= 0) last = L.lastpos;
+    if (first != 0x7fffffff) {
+      if (i == first) L.fin_base = carry + excl;
+      __syncthreads();
+      base_out = L.fin_base;
+      __syncthreads();
+      return first;
+    }
+    carry += tot;
+    __syncthreads();
+  }
+  return last >= 0 ? -(1 + last) : (int)0x80000000;
+}
+
+// Run by the row's last draw item; its own L.dec holds the row's decision.
 template <int DT>
 __device__ void final_draw(const Args& a, Lds& L, int b) {
   const int t = threadIdx.x;
-  const float* rc = a.rec + (int64_t)b * 8;
-  const int n = __float_as_int(rc[0]);
-  const bool resid = __float_as_int(rc[1]) != 0;
-  const float ustar = rc[2];
-  DrawParams d{rc[3], 1.f / rc[4], rc[5], 1.f / rc[6], a.k2, resid ? 1 : 0};
+  const int n = L.dec.n;
+  DrawParams d = draw_params(L.dec, a.k2);
   const void* trow = row_ptr<DT>(a.tgt, trow_off(a, b, n));
-  const void* drow = resid ? row_ptr<DT>(a.dft, drow_off(a, b, n)) : trow;
-  const double* ss = a.ssum + (int64_t)b * a.ND;
+  const void* drow = L.dec.resid ? row_ptr<DT>(a.dft, drow_off(a, b, n)) : trow;
   const int nsub_max = a.SL / kSub;
-
-  // Z = sum of the slice totals (scanned in the same order as the search)
-  double z = 0.0;
-  for (int c0 = 0; c0 < a.ND; c0 += kThreads) {
-    const int i = c0 + t;
-    double incl, excl, tot;
-    block_scan_d(i < a.ND ? ss[i] : 0.0, L.red_d, incl, excl, tot);
-    z += tot;
-  }
-  if (!(z > 0.0)) {
-    // rounding left the residual without mass: draw from p_n (slow path)
+  const double* sub = a.sub + (int64_t)b * a.ND * nsub_max;
+  // flattened (slice, sub-slice) entries; the last slice may hold fewer
+  auto sub_val = [&](int i) {
+    const int s = i / nsub_max, k = i % nsub_max;
+    return k < subs_in_slice(a, s) ? get_d(&sub[i]) : 0.0;
+  };
+  const int count = a.ND * nsub_max;
+  const auto pick = [](int r) { return r >= 0 ? r : (r == (int)0x80000000 ? 0 : -(r + 1)); };
+  double base = 0.0, z = 0.0, tau = 0.0;
+  int fs = 0;
+  bool fallback = false;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (count <= kThreads * kSubChunks) {
+      fs = find_sub_prefetched(count, L.dec.ustar, sub_val, L, base, z);
+      tau = (double)L.dec.ustar * z;
+    } else {
+      // long vocabularies: total first, then a chunked search
+      z = 0.0;
+      for (int c0 = 0; c0 < count; c0 += kThreads) {
+        const int i = c0 + t;
+        double incl, excl, tot;
+        block_scan_d(i < count ? sub_val(i) : 0.0, L.red_d, incl, excl, tot);
+        z += tot;
+      }
+      tau = (double)L.dec.ustar * z;
+      fs = block_find(count, 0.0, tau, sub_val, L, base);
+    }
+    if (z > 0.0 || d.kind != 1) break;
+    // rounding left the residual without mass: draw from p_n instead (slow
+    // path, one sub-slice per thread; exact arithmetic never gets here)
     d.kind = 2;
-    for (int s = 0; s < a.ND; ++s) draw_slice<DT>(a, L, b, s, trow, drow, d);
+    for (int f = t; f < count; f += kThreads) {
+      const int s = f / nsub_max, k = f % nsub_max;
+      double acc = 0.0;
+      if (k < subs_in_slice(a, s)) {
+        const int j0 = s * a.SL + k * kSub, j1 = min(a.V, j0 + kSub);
+        for (int j = j0; j < j1; ++j) acc += (double)weight_at<DT>(d, trow, drow, j);
+      }
+      put_d(const_cast<double*>(&sub[f]), acc);
+    }
+    publish();
     __syncthreads();
     if (t == 0) atomicOr(&a.hdr[1], kDiagZeroResid);
-    z = 0.0;
-    for (int c0 = 0; c0 < a.ND; c0 += kThreads) {
-      const int i = c0 + t;
-      double incl, excl, tot;
-      block_scan_d(i < a.ND ? ss[i] : 0.0, L.red_d, incl, excl, tot);
-      z += tot;
-    }
   }
-  const double tau = (double)ustar * z;
   if (a.pr_z && t == 0) a.pr_z[b] = (float)(d.kind == 0 ? z * (double)d.st_inv : z);
-
-  // slices -> sub-slices -> elements.  Once rounding leaves no entry whose
-  // running sum exceeds tau, the rest of the descent takes the last entry
-  // with positive weight (tau = +inf finds nothing and reports it).
-  auto pick = [](int r) { return r >= 0 ? r : (r == (int)0x80000000 ? 0 : -(r + 1)); };
+  fallback = fs < 0;
+  fs = pick(fs);
+  // elements of that sub-slice: one per thread
+  const int s = fs / nsub_max, k = fs % nsub_max;
+  const int j0 = s * a.SL + k * kSub;
+  const int cnt = min(kSub, a.V - j0);
   const double never = __builtin_inf();
-  double base = 0.0;
-  int s = block_find(a.ND, 0.0, tau, [&](int i) { return ss[i]; }, L, base);
-  bool fallback = s < 0;
-  s = pick(s);
-  const int lo = s * a.SL;
-  const int len = min(a.V, lo + a.SL) - lo;
-  const int nsub = (len + kSub - 1) / kSub;
-  const double* sub = a.sub + ((int64_t)b * a.ND + s) * nsub_max;
-  int k = block_find(nsub, base, fallback ? never : tau, [&](int i) { return sub[i]; }, L, base);
-  fallback = fallback || k < 0;
-  k = pick(k);
-  const int j0 = lo + k * kSub;
-  const int cnt = min(kSub, lo + len - j0);
   int j = block_find(cnt, base, fallback ? never : tau,
                      [&](int i) { return (double)weight_at<DT>(d, trow, drow, j0 + i); }, L, base);
   j = pick(j);
@@ -761,17 +878,14 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(Args a) {
   const bool gvalid = (g >= 0) && (g <= a.G);
 
   if (!is_draw) {
-    const int nrows = gvalid ? (kSample ? 2 * g + 1 : g + 1) : 0;
     if (!gvalid) {
       if (slot == 0) {
         write_sentinel(a, b);
-        if (kSample && t == 0) {
-          fence_release();
-          store_rel(&a.flag[b], kFlagNone);
-        }
+        if (kSample && t == 0) put_u(counter(a, kRowFlag, b), kFlagNone);
       }
       return;
     }
+    const int nrows = kSample ? 2 * g + 1 : g + 1;
     const int r = slot / a.NC, c = slot % a.NC;
     if (r >= nrows) return;  // padding of a short row: no work, no ticket
     const bool is_target = r <= g;
@@ -794,27 +908,32 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(Args a) {
       res = make_float2(v, __int_as_float(ix));
     }
     if (t == 0) {
-      a.part[((int64_t)b * a.NR + pslot) * a.NC + c] = res;
-      fence_release();
-      const unsigned total = (unsigned)(nrows * a.NC);
-      const unsigned tk = ticket(&a.rowt[b]);
-      L.last = (tk == total - 1);
-      if (L.last) store_rel(&a.rowt[b], 0u);
+      put_f2(&a.part[((int64_t)b * a.NR + pslot) * a.NC + c], res);
+      publish();
+      const unsigned tk = ticket(counter(a, kRowTicket, b));
+      L.last = (tk == (unsigned)(nrows * a.NC) - 1);
+      if (L.last) {
+        put_u(counter(a, kRowTicket, b), 0u);
+        // sampling: the row's draw items take the decision from here on
+        if (kSample) put_u(counter(a, kRowFlag, b), kFlagStats);
+      }
     }
     __syncthreads();
-    if (!L.last) return;
-    fence_acquire();
-    decide_row<DT, MODE>(a, L, b, g);
+    if (kSample || !L.last) return;
+    const Gathered in = gather_inputs<DT, MODE>(a, b, g);
+    decide<DT, MODE>(a, L, b, g, in, true);
     return;
   }
 
-  // ---------------- draw item (b, slot)
+  // ---------------- draw item (b, slot): sampling only
+  Gathered in{-1, 0.f, 0.f, 0.f};
+  if (gvalid) in = gather_inputs<DT, MODE>(a, b, g);  // immutable inputs: read while waiting
   if (t == 0) {
-    unsigned f = load_rlx(&a.flag[b]);
+    unsigned f = get_u(counter(a, kRowFlag, b));
     unsigned spins = 0;
     while (f == 0u) {
       __builtin_amdgcn_s_sleep(2);
-      f = load_rlx(&a.flag[b]);
+      f = get_u(counter(a, kRowFlag, b));
       if (++spins > a.max_spin) {
         atomicOr(&a.hdr[1], kDiagSpin);
         f = kFlagNone;
@@ -824,29 +943,31 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(Args a) {
     L.flag = f;
   }
   __syncthreads();
-  fence_acquire();
-  const unsigned f = L.flag;
-  if (f == kFlagDraw) {
-    const float* rc = a.rec + (int64_t)b * 8;
-    const int n = __float_as_int(rc[0]);
-    const bool resid = __float_as_int(rc[1]) != 0;
-    DrawParams d{rc[3], 1.f / rc[4], rc[5], 1.f / rc[6], a.k2, resid ? 1 : 0};
+  bool work = false;
+  if (L.flag == kFlagStats) {
+    decide<DT, MODE>(a, L, b, g, in, slot == 0);
+    work = !L.dec.dead;
+  }
+  if (work) {
+    const int n = L.dec.n;
+    const DrawParams d = draw_params(L.dec, a.k2);
     const void* trow = row_ptr<DT>(a.tgt, trow_off(a, b, n));
-    const void* drow = resid ? row_ptr<DT>(a.dft, drow_off(a, b, n)) : trow;
+    const void* drow = L.dec.resid ? row_ptr<DT>(a.dft, drow_off(a, b, n)) : trow;
     draw_slice<DT>(a, L, b, slot, trow, drow, d);
   }
   if (t == 0) {
-    fence_release();
-    const unsigned tk = ticket(&a.drawt[b]);
+    publish();
+    const unsigned tk = ticket(counter(a, kDrawTicket, b));
     L.last = (tk == (unsigned)a.ND - 1);
   }
   __syncthreads();
   if (!L.last) return;
-  fence_acquire();
-  if (f == kFlagDraw) final_draw<DT>(a, L, b);
+  if (work) {
+    final_draw<DT>(a, L, b);
+  }
   if (t == 0) {
-    store_rel(&a.drawt[b], 0u);
-    store_rel(&a.flag[b], 0u);
+    put_u(counter(a, kDrawTicket, b), 0u);
+    put_u(counter(a, kRowFlag, b), 0u);
   }
 }
 
@@ -919,12 +1040,8 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.pr_px = px, a.pr_qx = qx, a.pr_z = pz, a.pr_m = pm, a.pr_s = ps;
   char* w = (char*)ws;
   a.hdr = (unsigned*)w;
-  a.rowt = (unsigned*)(w + p.off_rowt);
-  a.drawt = (unsigned*)(w + p.off_drawt);
-  a.flag = (unsigned*)(w + p.off_flag);
-  a.rec = (float*)(w + p.off_rec);
+  a.ctr_end = (unsigned*)(((uintptr_t)w + ws_bytes) & ~(uintptr_t)255);
   a.part = (float2*)(w + p.off_part);
-  a.ssum = (double*)(w + p.off_ssum);
   a.sub = (double*)(w + p.off_sub);
   a.B = B, a.G = G, a.V = V, a.NR = p.NR, a.NC = p.NC, a.CH = p.CH, a.ND = p.ND, a.SL = p.SL;
   a.L = p.L, a.NP = p.NP;
