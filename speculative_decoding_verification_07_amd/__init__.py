@@ -155,6 +155,11 @@ def _shape_check(target, draft, tokens, uniforms, gamma, kv_len, mode):
             raise ValueError(f"{name} must be contiguous")
         if t is not None and not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
+    torch = _torch()
+    for name, t, want in (("draft_tokens", tokens, torch.int32), ("uniforms", uniforms, torch.float32),
+                          ("gamma_per_row", gamma, torch.int32), ("kv_len_in", kv_len, torch.int32)):
+        if t is not None and t.dtype != want:
+            raise TypeError(f"{name} must be {want}")
     if draft is not None and (tuple(draft.shape) != (B, G, V) or draft.dtype != target.dtype):
         raise ValueError("draft_logits must be [B, gamma_max, V] with the target's dtype")
     if tokens is not None and tuple(tokens.shape) != (B, G):
@@ -209,6 +214,36 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, k
     _check(lib.spec_verify_probe(*args, _ptr(pr["px"]), _ptr(pr["qx"]), _ptr(pr["z"]),
                                  _ptr(pr["m"]), _ptr(pr["s"])), "spec_verify_probe")
     return tok, nacc, nlen, pr
+
+
+class Prepared:
+    """One spec_verify call with its arguments checked and marshalled once.
+
+    Calling the object re-issues the same call (same tensors, workspace,
+    outputs and stream); for tight loops where per-call Python work would
+    otherwise delay the launches."""
+
+    def __init__(self, target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row,
+                 kv_len_in=None, *, temperature: float = 1.0, mode: int = SAMPLE,
+                 workspace: Workspace, out, stream=None):
+        B, G, V = _shape_check(target_logits, draft_logits, draft_tokens, uniforms,
+                               gamma_per_row, kv_len_in, mode)
+        dt = _dtype_code(target_logits)
+        if workspace.nbytes < workspace_bytes(B, G, V, dt, mode):
+            raise ValueError("workspace too small")
+        self._keep = (target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row,
+                      kv_len_in, workspace, out)
+        tok, nacc, nlen = out
+        self._fn = load().spec_verify
+        self._args = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
+                      _ptr(uniforms), _ptr(gamma_per_row), _ptr(kv_len_in), B, G, V, dt,
+                      ctypes.c_float(temperature), int(mode), _ptr(tok), _ptr(nacc), _ptr(nlen),
+                      ctypes.c_void_p(workspace.ptr), workspace.nbytes, _stream_handle(stream))
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != OK:
+            raise SpecVerifyError(rc, "spec_verify")
 
 
 def probe_read(src, out=None, stream=None):

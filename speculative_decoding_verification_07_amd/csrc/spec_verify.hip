@@ -57,10 +57,14 @@ constexpr size_t kRowBlockBytes = kRowBlock * sizeof(unsigned);
 #define NEG_INF (-__builtin_inff())
 
 struct Tuning {
-  int chunk_bytes = 32768;
+  int chunk_bytes = 65536;
   int slice_elems = 8192;
   int lag_rows = 0;  // 0: derived from the plan
 };
+// Draw items of row k follow the statistics of row k + lag: about this many
+// statistics workgroups run ahead of a row's draws (measured best on MI355X
+// for 64-256 rows at V = 128K-152K).
+constexpr int kLeadWorkgroups = 600;
 Tuning g_tune;
 
 // ------------------------------------------------------------------ plan
@@ -99,7 +103,8 @@ int make_plan(int B, int G, int V, int dtype, int mode, Plan* p) {
   p->ND = mode == SPEC_MODE_SAMPLE ? (V + sl - 1) / sl : 0;
   p->NP = p->NR * p->NC;
   int lag = g_tune.lag_rows;
-  if (lag <= 0) lag = (4096 + p->NP - 1) / p->NP + 1;
+  if (lag <= 0) lag = (kLeadWorkgroups + p->NP / 2) / p->NP;
+  if (lag < 1) lag = 1;
   p->L = lag < B ? lag : B;
   p->total = (int64_t)B * (p->NP + p->ND);
   if (p->total >= (int64_t)1 << 31) return SPEC_ERR_SHAPE;
@@ -419,22 +424,22 @@ struct Decision {
   int resid;    // 1: draw from the residual at n, 0: bonus draw from p_g
   float ustar;  // uniform of the draw
   float mt, st, md, sd;  // (max, exp-sum) of target row n and draft row n
+  int n_hit;    // final draw: broadcast slot for the index found
 };
 
-constexpr int kSubChunks = 4;  // final draw: sub-slice sums staged per thread
+constexpr int kSubChunks = 4;  // final draw: sub-slice sums held per thread
 
 struct Lds {
   double red_d[kWaves];
   double subs[kMaxSubs];
-  double fsub[kThreads * kSubChunks];
   double fin_base;
   float red[2 * kWaves];
   float m[2 * SPEC_GAMMA_MAX_LIMIT + 1];
   float s[2 * SPEC_GAMMA_MAX_LIMIT + 1];
+  unsigned long long mask[kWaves];
   Decision dec;
   unsigned flag;
   int last;
-  int cand, lastpos;
 };
 
 // Draw-side inputs of one position, read before the row's statistics are
@@ -674,10 +679,41 @@ __device__ void block_scan_d(double v, double* red, double& incl, double& excl, 
   total = tot;
 }
 
+// Lowest (highest) thread index whose predicate holds, or -1: one wave
+// ballot per wave, then a scan of kWaves masks.
+__device__ int block_first(bool pred, Lds& L) {
+  const unsigned long long m = __ballot(pred);
+  if ((threadIdx.x & 63) == 0) L.mask[threadIdx.x >> 6] = m;
+  __syncthreads();
+  int r = -1;
+  for (int k = 0; k < kWaves; ++k)
+    if (L.mask[k]) {
+      r = k * 64 + __ffsll((long long)L.mask[k]) - 1;
+      break;
+    }
+  __syncthreads();
+  return r;
+}
+
+__device__ int block_last(bool pred, Lds& L) {
+  const unsigned long long m = __ballot(pred);
+  if ((threadIdx.x & 63) == 0) L.mask[threadIdx.x >> 6] = m;
+  __syncthreads();
+  int r = -1;
+  for (int k = kWaves - 1; k >= 0; --k)
+    if (L.mask[k]) {
+      r = k * 64 + 63 - __clzll((long long)L.mask[k]);
+      break;
+    }
+  __syncthreads();
+  return r;
+}
+
 // First index i in [0, count) with weight val(i) > 0 and tau < base + the
-// inclusive prefix at i.  On success returns i and the exclusive prefix at i
-// (base included) in base_out.  If rounding leaves no such index, returns
-// -(1 + the last index with positive weight), or INT_MIN if there is none.
+// inclusive prefix at i (one entry per thread per chunk of kThreads).  On
+// success returns i and the exclusive prefix at i (base included) in
+// base_out.  If rounding leaves no such index, returns -(1 + the last index
+// with positive weight), or INT_MIN if there is none.
 template <class F>
 __device__ int block_find(int count, double base, double tau, F val, Lds& L, double& base_out) {
   const int t = threadIdx.x;
@@ -688,23 +724,18 @@ __device__ int block_find(int count, double base, double tau, F val, Lds& L, dou
     const double v = i < count ? val(i) : 0.0;
     double incl, excl, tot;
     block_scan_d(v, L.red_d, incl, excl, tot);
-    if (t == 0) L.cand = 0x7fffffff, L.lastpos = -1;
-    __syncthreads();
     const bool pos = i < count && v > 0.0;
-    if (pos && tau < carry + incl) atomicMin(&L.cand, i);
-    if (pos) atomicMax(&L.lastpos, i);
-    __syncthreads();
-    const int first = L.cand;
-    if (L.lastpos >= 0) lastpos = L.lastpos;
-    if (first != 0x7fffffff) {
-      if (i == first) L.fin_base = carry + excl;
+    const int first = block_first(pos && tau < carry + incl, L);
+    if (first >= 0) {
+      if (t == first) L.fin_base = carry + excl;
       __syncthreads();
       base_out = L.fin_base;
       __syncthreads();
-      return first;
+      return c0 + first;
     }
+    const int last = block_last(pos, L);
+    if (last >= 0) lastpos = c0 + last;
     carry += tot;
-    __syncthreads();
   }
   return lastpos >= 0 ? -(1 + lastpos) : (int)0x80000000;
 }
@@ -728,51 +759,51 @@ template <class F>
 __device__ int find_sub_prefetched(int count, float u, F val, Lds& L, double& base_out,
                                    double& z_out) {
   const int t = threadIdx.x;
-  // every entry is loaded at once and staged in LDS
+  // thread t owns entries [t * kSubChunks, (t + 1) * kSubChunks)
+  double v[kSubChunks];
+  double mine = 0.0;
 #pragma unroll
-  for (int c = 0; c < kSubChunks; ++c) {
-    const int i = c * kThreads + t;
-    L.fsub[i] = i < count ? val(i) : 0.0;
+  for (int e = 0; e < kSubChunks; ++e) {
+    const int i = t * kSubChunks + e;
+    v[e] = i < count ? val(i) : 0.0;
   }
-  __syncthreads();
-  // pass 1: the total, in the same chunk order as the search
-  double z = 0.0;
-#pragma unroll 1
-  for (int c = 0; c < kSubChunks; ++c) {
-    double incl, excl, tot;
-    block_scan_d(L.fsub[c * kThreads + t], L.red_d, incl, excl, tot);
-    z += tot;
-  }
+#pragma unroll
+  for (int e = 0; e < kSubChunks; ++e) mine += v[e];
+  double incl, excl, z;
+  block_scan_d(mine, L.red_d, incl, excl, z);
   z_out = z;
   const double tau = (double)u * z;
-  // pass 2: first entry whose running sum exceeds tau
-  double carry = 0.0;
-  int last = -1;
-#pragma unroll 1
-  for (int c = 0; c < kSubChunks; ++c) {
-    const int i = c * kThreads + t;
-    const double v = L.fsub[i];
-    double incl, excl, tot;
-    block_scan_d(v, L.red_d, incl, excl, tot);
-    if (t == 0) L.cand = 0x7fffffff, L.lastpos = -1;
-    __syncthreads();
-    const bool pos = i < count && v > 0.0;
-    if (pos && tau < carry + incl) atomicMin(&L.cand, i);
-    if (pos) atomicMax(&L.lastpos, i);
-    __syncthreads();
-    const int first = L.cand;
-    if (L.lastpos >= 0) last = L.lastpos;
-    if (first != 0x7fffffff) {
-      if (i == first) L.fin_base = carry + excl;
-      __syncthreads();
-      base_out = L.fin_base;
-      __syncthreads();
-      return first;
+  // first entry, in order, whose running sum exceeds tau; last positive entry
+  double c = excl;
+  int hit = -1, lastpos = -1;
+  double hit_base = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSubChunks; ++e) {
+    const double nxt = c + v[e];
+    if (v[e] > 0.0) {
+      lastpos = t * kSubChunks + e;
+      if (hit < 0 && tau < nxt) hit = t * kSubChunks + e, hit_base = c;
     }
-    carry += tot;
-    __syncthreads();
+    c = nxt;
   }
-  return last >= 0 ? -(1 + last) : (int)0x80000000;
+  const int owner = block_first(hit >= 0, L);
+  if (owner >= 0) {
+    if (t == owner) L.fin_base = hit_base, L.dec.n_hit = hit;
+    __syncthreads();
+    base_out = L.fin_base;
+    const int r = L.dec.n_hit;
+    __syncthreads();
+    return r;
+  }
+  const int lo = block_last(lastpos >= 0, L);
+  if (lo >= 0) {
+    if (t == lo) L.dec.n_hit = lastpos;
+    __syncthreads();
+    const int r = L.dec.n_hit;
+    __syncthreads();
+    return -(1 + r);
+  }
+  return (int)0x80000000;
 }
 
 // Run by the row's last draw item; its own L.dec holds the row's decision.
