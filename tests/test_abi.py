@@ -110,7 +110,7 @@ def test_workspace_bytes_and_plan(lib):
 def test_tune_changes_plan_and_restores(lib):
     base = sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)
     try:
-        sv.tune(chunk_bytes=65536, slice_elems=4096, lag_rows=3)
+        sv.tune(chunk_bytes=262144, slice_elems=4096, lag_rows=3)
         p = sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)
         assert p["chunks"] < base["chunks"] and p["slice_len"] == 4096 and p["lag_rows"] == 3
         with pytest.raises(sv.SpecVerifyError):
