@@ -65,22 +65,29 @@ FULL_SIZES = [(1, "sample"), (1, "greedy"), (2, "sample"), (3, "sample"), (3, "g
 @pytest.mark.parametrize("cfg,mode", FULL_SIZES)
 def test_parity_full_size(torch, cfg, mode):
     """The workloads at their full sizes, in the launch configuration the
-    benchmark times; several calls with fresh uniforms (or fresh ragged
-    gamma, draft tokens and uniforms) over the same logits."""
-    case = inputs.make_case(cfg, rnd=0, mode=mode)
-    dev = case_to_dev(case, torch)
-    calls = {1: 64, 2: 16, 3: 4, 4: 1, 5: 8}[cfg] * (16 if FULL else 1)
+    benchmark times.  Every call redraws the uniforms (ragged workloads also
+    gamma_b and the draft tokens); fresh logits every 16 calls.  By default a
+    few calls per workload; SPEC_FULL_PARITY=1 runs at least 10^4 rows per
+    workload."""
+    B = inputs.CONFIGS[cfg].B
+    calls = -(-10_000 // B) if FULL else {1: 64, 2: 16, 3: 4, 4: 1, 5: 8}[cfg]
     total = parity.Report()
+    case = dev = None
     for k in range(calls):
-        if k:
-            case = inputs.redraw_round(case, k) if cfg == 5 else inputs.fresh_uniforms(case, k)
+        if k % 16 == 0:
+            case = inputs.make_case(cfg, rnd=k // 16, mode=mode)
+            dev = case_to_dev(case, torch)
+        else:
+            case = inputs.redraw_round(case, 1000 + k) if cfg == 5 else \
+                inputs.fresh_uniforms(case, 1000 + k)
             dev["uniforms"] = torch.from_numpy(case.uniforms).cuda()
             dev["tokens"] = torch.from_numpy(case.tokens).cuda()
             dev["gamma"] = torch.from_numpy(case.gamma).cuda()
-        print(f"full cfg={cfg} mode={mode} call={k}", flush=True)
-        tok, n, ln, pr = run(case, torch, dev=dev, probe=(k < 2))
+        if k % 50 == 0:
+            print(f"full cfg={cfg} mode={mode} call={k}/{calls}", flush=True)
+        tok, n, ln, pr = run(case, torch, dev=dev, probe=(k % 16 < 2))
         total.merge(parity.compare(case, tok, n, ln, pr))
-    print(total.summary(), total.attributed[:3])
+    print(f"cfg={cfg} mode={mode}", total.summary(), total.attributed[:3], flush=True)
     assert total.ok, (total.summary(), total.mismatched[:5], total.prob_errors[:5])
 
 
