@@ -93,9 +93,10 @@ int spec_verify_workspace_reset(void* workspace, size_t bytes, void* stream);
  * Any 2-byte (bf16) or 4-byte (fp32) aligned logits base works; rows need
  * not be 16-byte aligned.  Logits must be finite or -inf.
  * Per-row data errors (gamma outside [0, gamma_max]; a tested draft token
- * outside [0, V); when sampling, a needed row whose logits are all -inf)
- * give n_accepted = -1, tokens all -1 and new_len = kv_len_in for that row
- * only. */
+ * outside [0, V); when sampling, a row the walk uses -- p_i and q_i of a
+ * tested position, p_g for the bonus -- whose logits are all -inf) give
+ * n_accepted = -1, tokens all -1 and new_len = kv_len_in for that row only.
+ * Rows after the first rejection are never used. */
 int spec_verify(const void* target_logits, const void* draft_logits,
                 const int32_t* draft_tokens, const float* uniforms,
                 const int32_t* gamma_per_row, const int32_t* kv_len_in, int B, int gamma_max,

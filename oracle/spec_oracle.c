@@ -48,8 +48,10 @@
  *     draw from p_n with the same uniform and count it.
  *   - bonus normaliser: the bonus row's own sum.
  *   - data errors (gamma outside [0, gamma_max], a tested draft token outside
- *     [0, V), or, when sampling, a needed row whose logits are all -inf):
- *     n_accepted = -1, tokens all -1, new_len = kv_len_in.
+ *     [0, V), or, when sampling, a row the walk uses -- p_i and q_i of a
+ *     tested position, p_g for the bonus -- whose logits are all -inf; rows
+ *     after the stop are never used): n_accepted = -1, tokens all -1,
+ *     new_len = kv_len_in.
  */
 #include <math.h>
 #include <stdint.h>
@@ -225,39 +227,37 @@ static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t*
     return;
   }
 
-  /* Sampling: p_0..p_g and q_0..q_{g-1}, all in double. */
+  /* Sampling.  Diagnostics first: (max, exp-sum) of every row t_0..t_g,
+   * d_0..d_{g-1}; they play no part in the decisions. */
   double* P = (double*)malloc(sizeof(double) * (size_t)(g + 1) * V);
   double* Q = (double*)malloc(sizeof(double) * (size_t)(g > 0 ? g : 1) * V);
   double* w = (double*)malloc(sizeof(double) * (size_t)V);
-  int ok = 1;
+  int* live_p = (int*)malloc(sizeof(int) * (size_t)(g + 1));
+  int* live_q = (int*)malloc(sizeof(int) * (size_t)(g > 0 ? g : 1));
   for (int i = 0; i <= g; ++i) {
     double m, s;
-    int live = softmax_row(c, c->target, row_off(c, b, G + 1, i), P + (size_t)i * V, &m, &s);
+    live_p[i] = softmax_row(c, c->target, row_off(c, b, G + 1, i), P + (size_t)i * V, &m, &s);
     if (d->m) d->m[i] = m;
     if (d->s) d->s[i] = s;
-    ok &= live;
   }
   for (int i = 0; i < g; ++i) {
     double m, s;
-    int live = softmax_row(c, c->draft, row_off(c, b, G, i), Q + (size_t)i * V, &m, &s);
+    live_q[i] = softmax_row(c, c->draft, row_off(c, b, G, i), Q + (size_t)i * V, &m, &s);
     if (d->m) d->m[G + 1 + i] = m;
     if (d->s) d->s[G + 1 + i] = s;
-    ok &= live;
-  }
-  if (!ok) {
-    write_sentinel(c, b, out_tokens, out_n, out_len);
-    free(P), free(Q), free(w);
-    return;
   }
 
+  /* Walk left to right.  A row the walk uses (p_i, q_i at a tested
+   * position, p_g for the bonus) with no finite logit, or a tested token out
+   * of range, is a data error; rows after the stop are never used. */
   int n = g;
   for (int i = 0; i < g; ++i) {
     const double* p = P + (size_t)i * V;
     const double* q = Q + (size_t)i * V;
     int xi = x[i];
-    if (xi < 0 || xi >= V) {
+    if (!live_p[i] || !live_q[i] || xi < 0 || xi >= V) {
       write_sentinel(c, b, out_tokens, out_n, out_len);
-      free(P), free(Q), free(w);
+      free(P), free(Q), free(w), free(live_p), free(live_q);
       return;
     }
     if (d->px) d->px[i] = p[xi];
@@ -275,6 +275,11 @@ static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t*
       n = i;
       break;
     }
+  }
+  if (n == g && !live_p[g]) {
+    write_sentinel(c, b, out_tokens, out_n, out_len);
+    free(P), free(Q), free(w), free(live_p), free(live_q);
+    return;
   }
 
   const double* pn = P + (size_t)n * V;
@@ -307,7 +312,7 @@ static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t*
   for (int i = n + 1; i <= G; ++i) tok[i] = -1;
   out_n[b] = n;
   out_len[b] = kv + n;
-  free(P), free(Q), free(w);
+  free(P), free(Q), free(w), free(live_p), free(live_q);
 }
 
 /* Returns 0 on success, a negative value for arguments the oracle refuses.

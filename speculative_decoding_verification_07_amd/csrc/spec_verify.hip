@@ -511,15 +511,6 @@ __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, 
         if (a.pr_s) a.pr_s[(int64_t)b * (2 * a.G + 1) + slot] = sv;
       }
     }
-    // sampling needs every row to have a finite logit
-    bool dead = false;
-    if (kSample) {
-      for (int r = lane; r < nrows; r += 64) {
-        const int slot = (r <= g) ? r : (a.G + 1 + (r - g - 1));
-        dead |= (L.m[slot] == NEG_INF);
-      }
-    }
-    const bool any_dead = __ballot(dead) != 0;
     const bool valid = (unsigned)in.x < (unsigned)a.V;
     bool fail = false;
     if (lane < g) {
@@ -541,7 +532,11 @@ __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, 
     const unsigned long long mask = __ballot(fail);
     const int n = mask ? (__ffsll((long long)mask) - 1) : g;
     const bool bad_token = mask && (__shfl(valid ? 1 : 0, n, 64) == 0);
-    const bool sentinel = any_dead || bad_token;
+    // sampling: a row the walk uses must have a finite logit.  A dead p_i or
+    // q_i makes the test at i fail (NaN), so only the stop position can hold
+    // one; rows after the stop are never used.
+    const bool dead_n = kSample && (L.m[n] == NEG_INF || (n < g && L.m[a.G + 1 + n] == NEG_INF));
+    const bool sentinel = dead_n || bad_token;
     const float ustar = __shfl(in.u, n < g ? n + 1 : g, 64);
     if (write_out) {
       // gamma_max <= 63, so lane i owns output position i (and holds x_i)

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import speculative_decoding_verification_07_amd as sv
+import oracle
 from oracle import parity
 from speculative_decoding_verification_07_amd import inputs
 
@@ -103,11 +104,31 @@ def test_edge_gamma_zero_ragged_and_errors(torch):
     x = case.tokens.copy()
     x[5, 0] = case.V      # tested token out of range
     t = case.target.copy()
-    t[6, 1, :] = 0xFF80   # a needed row all -inf
-    case.gamma, case.tokens, case.target = g, x, t
+    t[6, 0, :] = 0xFF80   # p_0, used by every walk, all -inf
+    d = case.draft.copy()
+    d[7, 0, :] = 0xFF80   # q_0 likewise
+    case.gamma, case.tokens, case.target, case.draft = g, x, t, d
     rep, tok, n, ln, pr = _check(case, torch)
-    for b in (2, 3, 5, 6):
+    for b in (2, 3, 5, 6, 7):
         assert n[b] == -1 and np.all(tok[b] == -1) and ln[b] == case.kv_len[b]
+
+
+def test_edge_dead_rows_after_the_stop(torch):
+    """Rows the walk never reaches may hold no finite logit: the result is
+    that of the same rows with ordinary logits."""
+    case = inputs.make_case(3, rnd=10, B=32, V=3001)
+    r0 = oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
+                       case.kv_len, temperature=case.T)
+    rows = [b for b in range(case.B) if r0.n_accepted[b] < case.gamma[b] - 1]
+    assert len(rows) >= 4
+    t, d = case.target.copy(), case.draft.copy()
+    for b in rows:
+        k = r0.n_accepted[b] + 1
+        t[b, k:, :] = 0xFF80
+        d[b, k:, :] = 0xFF80
+    case.target, case.draft = t, d
+    rep, tok, n, ln, pr = _check(case, torch)
+    np.testing.assert_array_equal(n, r0.n_accepted)
 
 
 def test_edge_greedy_ties_and_dead_rows(torch):

@@ -236,12 +236,40 @@ def test_data_errors_write_sentinel():
     x = case.tokens.copy()
     x[2, 0] = case.V          # tested token out of range
     t = case.target.copy()
-    t[3, 2, :] = 0xFF80       # bf16 -inf: a needed row with no finite logit
-    r = oracle.verify(t, case.draft, x, case.uniforms, g, case.kv_len, temperature=case.T)
-    for b in range(4):
+    t[3, 0, :] = 0xFF80       # bf16 -inf: p_0, which every walk uses, has no finite logit
+    d = case.draft.copy()
+    d[4, 0, :] = 0xFF80       # q_0 likewise (row 4 tests position 0: gamma >= 1)
+    assert g[4] >= 1
+    r = oracle.verify(t, d, x, case.uniforms, g, case.kv_len, temperature=case.T)
+    for b in range(5):
         assert r.n_accepted[b] == -1
         assert np.all(r.tokens[b] == -1)
         assert r.new_len[b] == case.kv_len[b]
+    assert r.n_accepted[5] >= 0
+    # a dead row after the stop is never used: the result is unchanged
+    case3 = inputs.make_case(3, rnd=10, B=32, V=300)
+    r0 = oracle.verify(case3.target, case3.draft, case3.tokens, case3.uniforms, case3.gamma,
+                       temperature=case3.T)
+    rows = [b for b in range(case3.B) if r0.n_accepted[b] < case3.gamma[b] - 1]
+    assert len(rows) >= 4
+    t3, d3 = case3.target.copy(), case3.draft.copy()
+    for b in rows:
+        n = r0.n_accepted[b]
+        t3[b, n + 1, :] = 0xFF80
+        d3[b, n + 1, :] = 0xFF80
+        t3[b, case3.gamma[b], :] = 0xFF80   # the bonus row is not used after a rejection
+    r1 = oracle.verify(t3, d3, case3.tokens, case3.uniforms, case3.gamma, temperature=case3.T)
+    np.testing.assert_array_equal(r1.tokens, r0.tokens)
+    np.testing.assert_array_equal(r1.n_accepted, r0.n_accepted)
+    # ... but a dead bonus row is used when every draft is accepted
+    full = [b for b in range(case3.B) if r0.n_accepted[b] == case3.gamma[b]]
+    assert full
+    if full:
+        t4 = case3.target.copy()
+        t4[full[0], case3.gamma[full[0]], :] = 0xFF80
+        r2 = oracle.verify(t4, case3.draft, case3.tokens, case3.uniforms, case3.gamma,
+                           temperature=case3.T)
+        assert r2.n_accepted[full[0]] == -1
     # an out-of-range token after the first rejection is never tested
     case2 = inputs.make_case(3, rnd=9, B=16, V=400)
     r0 = oracle.verify(case2.target, case2.draft, case2.tokens, case2.uniforms, case2.gamma,
