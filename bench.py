@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--with-copy", action="store_true",
                     help="also run the reference copy kernel (counter calibration)")
-    ap.add_argument("--tune", default="", help="chunk_bytes,slice_elems,lag_rows")
+    ap.add_argument("--tune", default="", help="vectors[,target_workgroups]")
     return ap.parse_args()
 
 

@@ -51,8 +51,10 @@ enum spec_dtype { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 };
 enum spec_status {
   SPEC_OK = 0,
   SPEC_ERR_NULL = -1,      /* a required pointer is NULL                              */
-  SPEC_ERR_SHAPE = -2,     /* B < 1, V < 1, V > 2^30, gamma_max outside [0, 63]       */
-  SPEC_ERR_ARG = -3,       /* unknown mode or dtype; T not finite and > 0 when sampling */
+  SPEC_ERR_SHAPE = -2,     /* B < 1, V < 1, V > 2^20, gamma_max outside [0, 63], or
+                              more than 2^31 - 1 workgroups                          */
+  SPEC_ERR_ARG = -3,       /* unknown mode or dtype; T not finite and > 0 when
+                              sampling; a tuning value spec_verify_tune refuses      */
   SPEC_ERR_WORKSPACE = -4, /* workspace NULL or smaller than spec_verify_workspace_bytes */
   SPEC_ERR_ALIGN = -5,     /* logits not aligned to their element size, or an int32/float
                               array not 4-byte aligned                                 */
@@ -65,13 +67,14 @@ enum spec_status {
  * function of its arguments and of the tuning override).  Returns 0 for
  * sizes spec_verify would reject.
  *
- * The workspace holds per-chunk softmax statistics, per-slice draw sums and,
- * at its end, one block of self-resetting counters per batch row.  It must be
+ * The workspace holds two counters per batch row, the softmax statistics of
+ * every vocabulary slice and the draw sums of every slice.  It must be
  * zero-filled once before its first use (spec_verify_workspace_reset, or any
- * zero fill).  Every call that completes leaves the counters at zero again.
- * A workspace is identified by its pointer and size: pass both unchanged on
- * every call, and it serves any sequence of stream-ordered calls, of any
- * shapes, whose spec_verify_workspace_bytes does not exceed its size. */
+ * zero fill).  Every call that completes clears everything it wrote, leaving
+ * the workspace all zero again (the diagnostic word aside), so one workspace
+ * serves any sequence of stream-ordered calls, of any shapes, whose
+ * spec_verify_workspace_bytes does not exceed its size.  A call that gave up
+ * waiting (diagnostic bit 0) may leave it dirty: zero-fill it again. */
 size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype, int mode);
 
 /* Zero-fills `bytes` of a workspace with a small fill kernel on `stream`
@@ -122,23 +125,28 @@ int spec_verify_probe(const void* target_logits, const void* draft_logits,
                       void* workspace, size_t workspace_bytes, void* stream, float* out_px,
                       float* out_qx, float* out_z, float* out_m, float* out_s);
 
-/* Launch plan of a call with these sizes (host only): fills out[0..7] with
- * {workgroups, chunks per vocabulary row, chunk length, draw slices per
- * row, slice length, lag rows, vocabulary rows per batch row, threads per
- * workgroup}.  Returns SPEC_OK or an argument error. */
+/* Launch plan of a call with these sizes (host only).  Each batch row is
+ * served by `slices` workgroups; workgroup c owns elements [c * slice_len,
+ * (c + 1) * slice_len) of every vocabulary row of the batch row.  Fills
+ * out[0..7] with {workgroups, slices per vocabulary row, slice length
+ * (elements), 16-byte vectors per thread and vocabulary row, vocabulary rows
+ * per batch row at gamma_max, threads per workgroup, workspace bytes, target
+ * workgroup count}.  Returns SPEC_OK or an argument error. */
 int spec_verify_plan(int B, int gamma_max, int V, int dtype, int mode, int64_t* out);
 
-/* Process-wide override of the launch tuning (for benchmarking sweeps):
- * target bytes of one statistics chunk, elements of one draw slice, and the
- * number of rows whose statistics run ahead of their draws.  0 keeps the
- * default.  Changes spec_verify_workspace_bytes; not thread-safe against
- * concurrent calls. */
-int spec_verify_tune(int chunk_bytes, int slice_elems, int lag_rows);
+/* Process-wide override of the launch tuning (for benchmarking sweeps).
+ * vectors: 16-byte vectors per thread and vocabulary row, which sets the
+ * slice length (vectors * 4 KiB of logits): 1, 2 or 4, or 0 to choose it
+ * from the sizes -- the largest slices that still
+ * give at least target_workgroups workgroups.  target_workgroups: 0 keeps
+ * the default (1024).  reserved: must be 0.  Changes
+ * spec_verify_workspace_bytes; not thread-safe against concurrent calls. */
+int spec_verify_tune(int vectors, int target_workgroups, int reserved);
 
 /* Reads the workspace's diagnostic word (device -> host copy on `stream`,
- * synchronous): bit 0 set if a draw ever gave up waiting for its row's
- * decision (cannot happen in a correct launch), bit 1 set if a residual
- * with zero mass fell back to p. */
+ * synchronous): bit 0 set if a workgroup ever gave up waiting for the rest
+ * of its batch row's workgroups (cannot happen in a correct launch), bit 1
+ * set if a residual with zero mass fell back to p. */
 int spec_verify_diagnostics(const void* workspace, uint32_t* out_flags, void* stream);
 
 const char* spec_verify_strerror(int status);

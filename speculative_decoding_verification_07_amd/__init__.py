@@ -89,13 +89,15 @@ def workspace_bytes(B: int, gamma_max: int, V: int, dtype: int, mode: int) -> in
 def plan(B: int, gamma_max: int, V: int, dtype: int, mode: int) -> dict:
     out = (ctypes.c_int64 * 8)()
     _check(load().spec_verify_plan(B, gamma_max, V, dtype, mode, out), "spec_verify_plan")
-    keys = ("workgroups", "chunks", "chunk_len", "slices", "slice_len", "lag_rows",
-            "vocab_rows", "threads")
+    keys = ("workgroups", "slices", "slice_len", "vectors", "vocab_rows", "threads",
+            "workspace_bytes", "target_workgroups")
     return dict(zip(keys, (int(v) for v in out)))
 
 
-def tune(chunk_bytes: int = 0, slice_elems: int = 0, lag_rows: int = 0):
-    _check(load().spec_verify_tune(chunk_bytes, slice_elems, lag_rows), "spec_verify_tune")
+def tune(vectors: int = 0, target_workgroups: int = 0):
+    """Process-wide launch tuning (see spec_verify_tune); no arguments
+    restores the defaults."""
+    _check(load().spec_verify_tune(vectors, target_workgroups, 0), "spec_verify_tune")
 
 
 # ---------------------------------------------------------------- torch helpers

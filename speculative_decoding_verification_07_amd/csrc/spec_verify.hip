@@ -1,29 +1,36 @@
 // spec_verify.hip -- batched speculative-decoding verify step for MI355X (gfx950).
 //
-// One launch does the whole step.  Its workgroups are of two kinds, laid out
-// in blockIdx order:
+// One launch does the whole step.  Batch row b is served by a group of NC
+// workgroups with consecutive ids; workgroup c of the group owns the slice
+// [c*CL, (c+1)*CL) of every vocabulary row of b: target rows 0..g and, when
+// sampling, draft rows 0..g-1 (g = gamma_per_row[b]).
 //
-//   statistics items (b, r, c): chunk c of vocabulary row r of batch row b.
-//     Streams the chunk from HBM with 16-byte loads and reduces it to the
-//     online-softmax pair (m, S) = (max logit, sum 2^((l - m) log2e / T))
-//     -- or, greedy, to (max, lowest argmax) -- then writes the pair to the
-//     workspace and takes a ticket on the row.  The item that takes the
-//     row's last ticket merges the row's pairs, gathers t[x_i] and d[x_i],
-//     runs the acceptance test u * q < p for every position at once, finds
-//     the first rejection with a wave ballot, writes the row's outputs and
-//     publishes the row's decision.
-//   draw items (b, s): slice s of the one or two vocabulary rows the row
-//     draws from (the residual max(0, p_n - q_n) after a rejection at n, or
-//     p_g for the bonus).  Each waits for its row's decision, sums its
-//     slice's weights and takes a ticket; the last one prefix-sums the slice
-//     totals, finds the slice holding tau = u * Z, re-reads that slice and
-//     finds the token with a block prefix scan.
+//   1. Each workgroup streams its slice of every row from HBM with 16-byte
+//      loads (the next row's loads in flight while the current row is
+//      reduced) and reduces each to the softmax pair (m, S) = (largest logit,
+//      sum 2^((l - m) log2e / T)); greedy: (largest logit, lowest index).
+//   2. It publishes its pairs to the workspace and counts itself in on the
+//      row's arrival counter.
+//      Greedy: the workgroup that arrives last merges the row's pairs,
+//      compares the draft tokens with the target's argmaxes and writes the
+//      row.
+//      Sampling: every workgroup waits for its whole group, merges the pairs
+//      in the same fixed order (so all of them hold bit-identical statistics),
+//      runs every acceptance test u_i q_i(x_i) < p_i(x_i) at once and finds
+//      the first rejection n with a wave ballot.
+//   3. Sampling: every workgroup re-reads its slice of the row(s) the token is
+//      drawn from -- the residual max(0, p_n - q_n) after a rejection at n,
+//      p_g for the bonus -- sums the weights in fp64, publishes the sum and
+//      waits for the group's sums.  The workgroup whose slice holds
+//      tau = u * Z finds the token with block prefix scans over the slice it
+//      still holds in registers.
+//   4. The last workgroup of a row to leave clears the row's workspace
+//      entries, so a completed call leaves the workspace all zero.
 //
-// Draw items of row k sit after the statistics items of row k + lag, so they
-// rarely wait.  They wait only on items with smaller workgroup ids (the
-// dispatcher issues ids in increasing order on each XCD), so every wait ends;
-// a bounded spin backs that up.  Counters reset themselves, so the workspace
-// is left zero after each call.
+// Waits are only on workgroups of the waiter's own group.  A group's ids are
+// consecutive and each XCD dispatches its ids in increasing order, so the
+// lowest unfinished group always has every member running or next in line:
+// every wait ends.  A bounded spin backs that up.
 //
 // Method: "Speculative decoding" (mhtirogla.ai), "How it works" steps 2-5
 // and "Code"; blog.lo0.es, "The bare mechanism" step 3; tusharamrit, the
@@ -40,78 +47,76 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 8;            // 16-byte loads in flight per thread
-constexpr int kSub = kThreads;        // draw: elements per sub-slice
-constexpr int kMaxSubs = 64;          // draw: sub-slices per slice
-constexpr unsigned kFlagStats = 1u, kFlagNone = 2u;  // row flag values
+constexpr int kMaxSlices = kThreads;  // the draw scans one slice sum per thread
+constexpr int kMaxRows = 2 * SPEC_GAMMA_MAX_LIMIT + 1;
+constexpr int kStage = 1024;          // LDS entries for staging a group's pairs
+constexpr int kMaxVocab = 1 << 20;
+constexpr int kDefaultTargetWorkgroups = 1024;
 constexpr unsigned kDiagSpin = 1u, kDiagZeroResid = 2u;
-// Per-row counters (statistics ticket, draw ticket, row flag) each sit on
-// their own 256-byte line.  The row blocks are laid out downwards from the
-// end of the workspace, so a counter's address depends only on the workspace
-// (pointer and size) and the row, never on the call's sizes: calls of any
-// shape can share a workspace, and none finds another call's data where its
-// counters belong.
-constexpr int kCounterStride = 64;                   // unsigned words per counter line
-constexpr int kRowBlock = 3 * kCounterStride;        // words per row block
-constexpr size_t kRowBlockBytes = kRowBlock * sizeof(unsigned);
+// Per-row counters (arrivals, exits), each on its own 128-byte line.
+constexpr int kLine = 32;
+enum { kArrive = 0, kExit = kLine };
+constexpr int kRowWords = 2 * kLine;
 #define NEG_INF (-__builtin_inff())
 
 struct Tuning {
-  int chunk_bytes = 65536;
-  int slice_elems = 8192;
-  int lag_rows = 0;  // 0: derived from the plan
+  int vectors = 0;  // 16-byte vectors per thread and row; 0: chosen from the sizes
+  int target_workgroups = kDefaultTargetWorkgroups;
 };
-// Draw items of row k follow the statistics of row k + lag: about this many
-// statistics workgroups run ahead of a row's draws (measured best on MI355X
-// for 64-256 rows at V = 128K-152K).
-constexpr int kLeadWorkgroups = 600;
 Tuning g_tune;
 
 // ------------------------------------------------------------------ plan
 struct Plan {
   int B, G, V, dtype, mode;
-  int NR;        // vocabulary rows per batch row
-  int NC, CH;    // statistics chunks per vocabulary row, chunk length
-  int ND, SL;    // draw slices per batch row, slice length
-  int L;         // lag rows
-  int NP;        // statistics slots per batch row = NR * NC
-  int64_t total; // workgroups
-  size_t off_part, off_sub, bytes;
+  int R;       // 16-byte vectors per thread per vocabulary row
+  int CL, NC;  // slice length (elements), slices per vocabulary row
+  int NR;      // vocabulary rows per batch row at gamma_max
+  int64_t total;
+  size_t off_ctr, off_part, off_wsum, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int make_plan(int B, int G, int V, int dtype, int mode, Plan* p) {
-  if (B < 1 || V < 1 || V > (1 << 30) || G < 0 || G > SPEC_GAMMA_MAX_LIMIT) return SPEC_ERR_SHAPE;
+  if (B < 1 || V < 1 || V > kMaxVocab || G < 0 || G > SPEC_GAMMA_MAX_LIMIT) return SPEC_ERR_SHAPE;
   if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return SPEC_ERR_ARG;
   if (mode != SPEC_MODE_SAMPLE && mode != SPEC_MODE_GREEDY) return SPEC_ERR_ARG;
-  const int e = dtype == SPEC_DTYPE_F32 ? 4 : 2;
-  const int vec = 16 / e;
+  const bool sample = mode == SPEC_MODE_SAMPLE;
+  const int vec = dtype == SPEC_DTYPE_F32 ? 4 : 8;
   p->B = B, p->G = G, p->V = V, p->dtype = dtype, p->mode = mode;
-  p->NR = mode == SPEC_MODE_SAMPLE ? 2 * G + 1 : G + 1;
-  int target = g_tune.chunk_bytes / e;
-  target = target < vec ? vec : target - target % vec;
-  int nc = (V + target - 1) / target;
-  int ch = (V + nc - 1) / nc;
-  ch = (ch + vec - 1) / vec * vec;
-  p->CH = ch;
-  p->NC = (V + ch - 1) / ch;
-  int sl = g_tune.slice_elems;
-  if (sl > kSub * kMaxSubs) sl = kSub * kMaxSubs;
-  sl = sl < kSub ? kSub : sl - sl % kSub;
-  p->SL = sl;
-  p->ND = mode == SPEC_MODE_SAMPLE ? (V + sl - 1) / sl : 0;
-  p->NP = p->NR * p->NC;
-  int lag = g_tune.lag_rows;
-  if (lag <= 0) lag = (kLeadWorkgroups + p->NP / 2) / p->NP;
-  if (lag < 1) lag = 1;
-  p->L = lag < B ? lag : B;
-  p->total = (int64_t)B * (p->NP + p->ND);
+  p->NR = sample ? 2 * G + 1 : G + 1;
+  // a ring of rows in flight plus (sampling) the drawn rows' slices held in
+  // registers: at most 4 vectors per thread and row
+  const int rmax = 4;
+  auto slices = [&](int r) { return (V + r * kThreads * vec - 1) / (r * kThreads * vec); };
+  int R = 0;
+  if (g_tune.vectors) {
+    R = g_tune.vectors < rmax ? g_tune.vectors : rmax;
+    if (slices(R) > kMaxSlices) return SPEC_ERR_SHAPE;
+  } else {
+    // the largest slices that still give target_workgroups workgroups, else
+    // the smallest slices allowed
+    for (int r = rmax; r >= 1; r /= 2) {
+      if (slices(r) > kMaxSlices) break;
+      R = r;
+      if ((int64_t)B * slices(r) >= g_tune.target_workgroups) break;
+    }
+    if (R == 0) return SPEC_ERR_SHAPE;
+  }
+  p->R = R;
+  const int nc = slices(R);
+  int cl = (V + nc - 1) / nc;
+  cl = (cl + vec - 1) / vec * vec;
+  p->CL = cl;
+  p->NC = (V + cl - 1) / cl;
+  p->total = (int64_t)B * p->NC;
   if (p->total >= (int64_t)1 << 31) return SPEC_ERR_SHAPE;
-  size_t off = 256;  // header: [0] unused, [1] diagnostic word
-  p->off_part = off; off = align256(off + sizeof(float2) * (size_t)B * p->NP);
-  p->off_sub = off; off = align256(off + sizeof(double) * (size_t)B * (p->ND ? p->ND : 1) * (sl / kSub));
-  p->bytes = off + kRowBlockBytes * (size_t)B + 256;  // + counter blocks + end alignment
+  size_t off = 256;  // header: [1] diagnostic word
+  p->off_ctr = off; off = align256(off + sizeof(unsigned) * kRowWords * (size_t)B);
+  p->off_part = off; off = align256(off + sizeof(uint64_t) * (size_t)B * p->NC * p->NR);
+  p->off_wsum = off;
+  if (sample) off = align256(off + sizeof(uint64_t) * 2 * (size_t)B * p->NC);
+  p->bytes = off;
   return SPEC_OK;
 }
 
@@ -132,11 +137,11 @@ struct Args {
   float* pr_m;
   float* pr_s;
   unsigned* hdr;
-  unsigned* ctr_end;  // 256-byte aligned end of the workspace; row blocks below it
-  float2* part;
-  double* sub;
-  int B, G, V, NR, NC, CH, ND, SL, L, NP;
-  float k2;  // log2(e) / T
+  unsigned* ctr;   // [B][kRowWords]
+  uint64_t* part;  // [B][NC][NR] pairs of each slice: (m, S) or (max, argmax + 1)
+  uint64_t* wsum;  // [B][2][NC] draw weight sums of each slice (two attempts)
+  int B, G, V, NC, CL, NR;
+  float k2;        // log2(e) / T
   unsigned max_spin;
 };
 
@@ -146,16 +151,23 @@ struct Elt;
 template <>
 struct Elt<SPEC_DTYPE_F32> {
   static constexpr int kBytes = 4, kVec = 4;
-  __device__ static float one(const void* p, int64_t k) { return ((const float*)p)[k]; }
+  static constexpr uint32_t kNegInfWord = 0xff800000u;
+  __device__ static float one(const char* p, int k) { return ((const float*)p)[k]; }
   __device__ static void unpack(const uint4& v, float* f) {
     f[0] = __uint_as_float(v.x), f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z), f[3] = __uint_as_float(v.w);
+  }
+  // elements [k, k + 4) packed as one vector, read element by element
+  __device__ static uint4 gather(const char* p, int k) {
+    const uint32_t* w = (const uint32_t*)p + k;
+    return make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
 template <>
 struct Elt<SPEC_DTYPE_BF16> {
   static constexpr int kBytes = 2, kVec = 8;
-  __device__ static float one(const void* p, int64_t k) {
+  static constexpr uint32_t kNegInfWord = 0xff80ff80u;
+  __device__ static float one(const char* p, int k) {
     return __uint_as_float((uint32_t)((const uint16_t*)p)[k] << 16);
   }
   __device__ static void unpack(const uint4& v, float* f) {
@@ -164,25 +176,126 @@ struct Elt<SPEC_DTYPE_BF16> {
     f[4] = __uint_as_float(v.z << 16), f[5] = __uint_as_float(v.z & 0xffff0000u);
     f[6] = __uint_as_float(v.w << 16), f[7] = __uint_as_float(v.w & 0xffff0000u);
   }
+  __device__ static uint4 gather(const char* p, int k) {
+    const uint16_t* h = (const uint16_t*)p + k;
+    return make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16,
+                      h[4] | (uint32_t)h[5] << 16, h[6] | (uint32_t)h[7] << 16);
+  }
 };
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Split [j0, j1) of a row into an unaligned head, a 16-byte aligned body of
-// nv vectors starting at ja, and a tail starting at jb.
-template <int DT>
-struct Span {
-  int j0, ja, jb, j1, nv, head;
-  __device__ Span(const void* row, int lo, int hi) {
-    using E = Elt<DT>;
-    uintptr_t a = (uintptr_t)((const char*)row + (int64_t)lo * E::kBytes);
-    int h = (int)(((16u - (unsigned)(a & 15u)) & 15u) / E::kBytes);
-    if (h > hi - lo) h = hi - lo;
-    j0 = lo, j1 = hi, head = h, ja = lo + h;
-    nv = (hi - ja) / E::kVec;
-    jb = ja + nv * E::kVec;
-  }
+// ------------------------------------------------------------------ slices in registers
+// A slice [lo, lo + len) of one row splits into an unaligned head of `head`
+// elements, nv 16-byte vectors and a tail of len - jb elements.  Thread t
+// holds head element t, body vectors k * kThreads + t for k < R, and tail
+// element t; whatever is absent reads as -inf.  In index order: the head (in
+// thread order), then round 0 of the body (thread order, each vector in
+// element order), ..., round R-1, then the tail.
+struct Geom {
+  int head, nv, jb, len;
 };
+
+// AL: every row of the call is 16-byte aligned and V is a whole number of
+// vectors, so no slice has a head or a tail (decided on the host).
+template <int DT, bool AL>
+__device__ __forceinline__ Geom geom_of(const char* p, int len) {
+  using E = Elt<DT>;
+  Geom g;
+  if (AL) {
+    g.head = 0, g.nv = len / E::kVec, g.jb = len, g.len = len;
+    return g;
+  }
+  int h = (int)(((16u - ((unsigned)(uintptr_t)p & 15u)) & 15u) / E::kBytes);
+  if (h > len) h = len;
+  g.head = h;
+  g.nv = (len - h) / E::kVec;
+  g.jb = h + g.nv * E::kVec;
+  g.len = len;
+  return g;
+}
+
+template <int DT, int R>
+struct Slice {
+  uint4 v[R];
+  float hd, tl;
+};
+
+// Makes a slice's registers opaque to the optimiser, so that values computed
+// from them (unpacked logits, weights) are recomputed after this point
+// instead of being kept live across waits.
+template <int DT, int R>
+__device__ __forceinline__ void opaque(Slice<DT, R>& s) {
+#pragma unroll
+  for (int k = 0; k < R; ++k)
+    asm volatile("" : "+v"(s.v[k].x), "+v"(s.v[k].y), "+v"(s.v[k].z), "+v"(s.v[k].w));
+  asm volatile("" : "+v"(s.hd), "+v"(s.tl));
+}
+
+template <int DT, int R, bool AL>
+__device__ __forceinline__ void load_slice(const char* p, const Geom& g, Slice<DT, R>& s) {
+  using E = Elt<DT>;
+  const int t = threadIdx.x;
+  const uint4* vp = (const uint4*)(p + g.head * E::kBytes);
+  const uint4 ninf = make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+  if (AL) {
+    // straight-line code: unconditional loads (clamped index; an aligned
+    // slice holds at least one vector).  Absent vectors hold a copy of the
+    // last one: readers mask them with vget, after the wait for the load.
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int q = k * kThreads + t;
+      s.v[k] = vp[q < g.nv ? q : g.nv - 1];
+    }
+    s.hd = NEG_INF;
+    s.tl = NEG_INF;
+    return;
+  }
+  if (g.nv > 0) {  // uniform
+    // unconditional loads (clamped index), then -inf for what is absent
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int q = k * kThreads + t;
+      const uint4 raw = vp[q < g.nv ? q : g.nv - 1];
+      s.v[k] = q < g.nv ? raw : ninf;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < R; ++k) s.v[k] = ninf;
+  }
+  s.hd = NEG_INF;
+  s.tl = NEG_INF;
+  if (g.head > 0 || g.jb < g.len) {  // uniform: only rows that are not 16-byte aligned
+    if (t < g.head) s.hd = E::one(p, t);
+    if (t < g.len - g.jb) s.tl = E::one(p, g.jb + t);
+  }
+}
+
+// Vector k of this thread's share, -inf where the slice has none.
+template <int DT, int R>
+__device__ __forceinline__ uint4 vget(const Slice<DT, R>& s, int k, const Geom& g) {
+  using E = Elt<DT>;
+  const uint4 ninf = make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+  return k * kThreads + (int)threadIdx.x < g.nv ? s.v[k] : ninf;
+}
+
+// Loads a slice of another row into the register layout `g` of the slice
+// [lo, lo + len) of a row with a different 16-byte alignment, element by
+// element (the draft row of the draw, when it is aligned unlike the target
+// row; only rows that are not 16-byte aligned get here).
+template <int DT, int R>
+__device__ void load_slice_as(const char* p, const Geom& g, Slice<DT, R>& s) {
+  using E = Elt<DT>;
+  const int t = threadIdx.x;
+  const uint4 ninf = make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int q = k * kThreads + t;
+    s.v[k] = q < g.nv ? E::gather(p, g.head + q * E::kVec) : ninf;
+  }
+  s.hd = t < g.head ? E::one(p, t) : NEG_INF;
+  s.tl = t < g.len - g.jb ? E::one(p, g.jb + t) : NEG_INF;
+}
 
 // ------------------------------------------------------------------ reductions
 // Softmax statistics are kept in the scaled domain z = l * k2 (k2 = log2(e)/T):
@@ -192,6 +305,8 @@ struct Span {
 // R is a factor common to a weight and its normaliser and cancels in p.
 __device__ __forceinline__ float ref_of(float m, float k2) { return m * k2; }
 
+// Merge of two pairs; symmetric in its operands (max and + commute), so a
+// butterfly leaves every lane with the same bits.  (-inf, 0) is the identity.
 __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2, float k2) {
   const float M = fmaxf(m, m2);
   const float R = ref_of(M, k2);
@@ -201,17 +316,10 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2,
   s = a + b;
 }
 
-__device__ __forceinline__ void ms_fold(float& m, float& s, float v, float k2) {
-  if (v > m) {
-    s = (m == NEG_INF) ? 0.f : s * ex2(ref_of(m, k2) - ref_of(v, k2));
-    m = v;
-  }
-  if (m != NEG_INF) s += ex2(fmaf(v, k2, -ref_of(m, k2)));
-}
-
-// argmax pair: larger value wins, equal values go to the lower index.
+// argmax pair: larger value wins, equal values go to the lower index
+// (symmetric; (-inf, INT_MAX) is the identity).
 __device__ __forceinline__ void am_merge(float& v, int& i, float v2, int i2) {
-  bool take = (v2 > v) | ((v2 == v) & (i2 < i));
+  const bool take = (v2 > v) | ((v2 == v) & (i2 < i));
   v = take ? v2 : v;
   i = take ? i2 : i;
 }
@@ -221,437 +329,202 @@ __device__ __forceinline__ T shfl_xor(T v, int lane_mask) {
   return __shfl_xor(v, lane_mask, 64);
 }
 
-// Block-wide reductions; results valid in thread 0.  `red` is LDS scratch of
-// at least 2 * kWaves words.
-__device__ void block_ms(float& m, float& s, float k2, float* red) {
+// Wave-wide reductions on the DPP path (no LDS round trips): a butterfly
+// inside each row of 16 lanes, then row broadcasts that leave the total in
+// lane 63, which is read back as a wave-uniform value.  The order of the
+// operations is fixed, so the result is deterministic.
+#define SPEC_DPP(v, ident, ctrl, rows) __builtin_amdgcn_update_dpp((ident), (v), (ctrl), (rows), 0xf, false)
+#define SPEC_WAVE_REDUCE(T, TO_I, FROM_I, OP, IDENT)                                     \
+  {                                                                                     \
+    const int id_ = TO_I(IDENT);                                                        \
+    v = OP(v, FROM_I(SPEC_DPP(TO_I(v), id_, 0xB1, 0xf)));  /* quad_perm [1,0,3,2] */    \
+    v = OP(v, FROM_I(SPEC_DPP(TO_I(v), id_, 0x4E, 0xf)));  /* quad_perm [2,3,0,1] */    \
+    v = OP(v, FROM_I(SPEC_DPP(TO_I(v), id_, 0x141, 0xf))); /* row_half_mirror */       \
+    v = OP(v, FROM_I(SPEC_DPP(TO_I(v), id_, 0x140, 0xf))); /* row_mirror */            \
+    v = OP(v, FROM_I(SPEC_DPP(TO_I(v), id_, 0x142, 0xa))); /* row_bcast:15 */          \
+    v = OP(v, FROM_I(SPEC_DPP(TO_I(v), id_, 0x143, 0xc))); /* row_bcast:31 */          \
+    return FROM_I(__builtin_amdgcn_readlane(TO_I(v), 63));                              \
+  }
+__device__ __forceinline__ int as_i(float x) { return __float_as_int(x); }
+__device__ __forceinline__ float as_f(int x) { return __int_as_float(x); }
+__device__ __forceinline__ int id_i(int x) { return x; }
+__device__ __forceinline__ float add_f(float x, float y) { return x + y; }
+__device__ __forceinline__ int min_i(int x, int y) { return x < y ? x : y; }
+__device__ __forceinline__ float wave_sum(float v) SPEC_WAVE_REDUCE(float, as_i, as_f, add_f, 0.f)
+__device__ __forceinline__ float wave_max(float v) SPEC_WAVE_REDUCE(float, as_i, as_f, fmaxf, NEG_INF)
+__device__ __forceinline__ int wave_min(int v) SPEC_WAVE_REDUCE(int, id_i, id_i, min_i, 0x7fffffff)
+
+// (m, S) pairs of the lanes merged over the wave (result in every lane): the
+// wave's largest m, then each lane's S rescaled to it, then the sum.
+__device__ __forceinline__ void wave_ms_dpp(float& m, float& s, float k2) {
+  const float M = wave_max(m);
+  const float sc = (m == NEG_INF) ? 0.f : s * ex2(ref_of(m, k2) - ref_of(M, k2));
+  s = wave_sum(sc);
+  m = M;
+}
+
+// (max, lowest index) over the wave (result in every lane).
+__device__ __forceinline__ void wave_am_dpp(float& v, int& i) {
+  const float M = wave_max(v);
+  i = wave_min(v == M ? i : 0x7fffffff);
+  v = M;
+}
+
+__device__ __forceinline__ void wave_ms(float& m, float& s, float k2) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ms_merge(m, s, shfl_xor(m, o), shfl_xor(s, o), k2);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[w] = m, red[kWaves + w] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    m = red[0], s = red[kWaves];
-    for (int k = 1; k < kWaves; ++k) ms_merge(m, s, red[k], red[kWaves + k], k2);
-  }
 }
 
-__device__ void block_am(float& v, int& i, float* red) {
+__device__ __forceinline__ void wave_am(float& v, int& i) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) am_merge(v, i, shfl_xor(v, o), shfl_xor(i, o));
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[w] = v, red[kWaves + w] = __int_as_float(i);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    v = red[0], i = __float_as_int(red[kWaves]);
-    for (int k = 1; k < kWaves; ++k) am_merge(v, i, red[k], __float_as_int(red[kWaves + k]));
-  }
 }
 
-__device__ void block_sum_d(double& a, double* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) a += shfl_xor(a, o);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[w] = a;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    a = red[0];
-    for (int k = 1; k < kWaves; ++k) a += red[k];
-  }
-}
-
-// ------------------------------------------------------------------ streaming loops
-// Per-thread online (m, S) over [lo, hi) of one vocabulary row.
-template <int DT>
-__device__ void stats_range(const void* row, int lo, int hi, float k2, float& m, float& s) {
+// (max, lowest index of the max) of this thread's share; lo = the slice's
+// first index.  Only present elements count, so a slice of -inf yields its
+// lowest present index.
+template <int DT, int R>
+__device__ __forceinline__ void slice_am(const Slice<DT, R>& s, const Geom& g, int lo, float& v,
+                                         int& idx) {
   using E = Elt<DT>;
-  Span<DT> sp(row, lo, hi);
   const int t = threadIdx.x;
-  if (t < sp.head) ms_fold(m, s, E::one(row, sp.j0 + t), k2);
-  const uint4* vp = (const uint4*)((const char*)row + (int64_t)sp.ja * E::kBytes);
-  for (int k0 = 0; k0 < sp.nv; k0 += kThreads * kUnroll) {
-    uint4 raw[kUnroll];
+  float mx = fmaxf(s.hd, s.tl);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int k = k0 + u * kThreads + t;
-      if (k < sp.nv) raw[u] = vp[k];
-    }
-    float bm = NEG_INF;
+  for (int k = 0; k < R; ++k) {
+    float f[E::kVec];
+    E::unpack(vget(s, k, g), f);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int k = k0 + u * kThreads + t;
-      if (k < sp.nv) {
-        float f[E::kVec];
-        E::unpack(raw[u], f);
+    for (int e = 0; e < E::kVec; ++e) mx = fmaxf(mx, f[e]);
+  }
+  // walk the thread's elements from the highest index down
+  int j = 0x7fffffff;
+  if (t < g.len - g.jb && s.tl == mx) j = lo + g.jb + t;
 #pragma unroll
-        for (int e = 0; e < E::kVec; ++e) bm = fmaxf(bm, f[e]);
-      }
-    }
-    if (bm > m) {
-      s = (m == NEG_INF) ? 0.f : s * ex2(ref_of(m, k2) - ref_of(bm, k2));
-      m = bm;
-    }
-    if (m != NEG_INF) {
-      const float R = ref_of(m, k2);
+  for (int k = R - 1; k >= 0; --k) {
+    const int q = k * kThreads + t;
+    if (q < g.nv) {
+      float f[E::kVec];
+      E::unpack(s.v[k], f);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        int k = k0 + u * kThreads + t;
-        if (k < sp.nv) {
-          float f[E::kVec];
-          E::unpack(raw[u], f);
-#pragma unroll
-          for (int e = 0; e < E::kVec; ++e) s += ex2(fmaf(f[e], k2, -R));
-        }
-      }
+      for (int e = E::kVec - 1; e >= 0; --e)
+        if (f[e] == mx) j = lo + g.head + q * E::kVec + e;
     }
   }
-  if (t < sp.j1 - sp.jb) ms_fold(m, s, E::one(row, sp.jb + t), k2);
-}
-
-// Per-thread (max, lowest argmax) over [lo, hi) of one vocabulary row.
-template <int DT>
-__device__ void argmax_range(const void* row, int lo, int hi, float& bv, int& bi) {
-  using E = Elt<DT>;
-  Span<DT> sp(row, lo, hi);
-  const int t = threadIdx.x;
-  if (t < sp.head) am_merge(bv, bi, E::one(row, sp.j0 + t), sp.j0 + t);
-  const uint4* vp = (const uint4*)((const char*)row + (int64_t)sp.ja * E::kBytes);
-  for (int k0 = 0; k0 < sp.nv; k0 += kThreads * kUnroll) {
-    uint4 raw[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int k = k0 + u * kThreads + t;
-      if (k < sp.nv) raw[u] = vp[k];
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int k = k0 + u * kThreads + t;
-      if (k < sp.nv) {
-        float f[E::kVec];
-        E::unpack(raw[u], f);
-        const int jb = sp.ja + k * E::kVec;
-#pragma unroll
-        for (int e = 0; e < E::kVec; ++e) am_merge(bv, bi, f[e], jb + e);
-      }
-    }
-  }
-  if (t < sp.j1 - sp.jb) am_merge(bv, bi, E::one(row, sp.jb + t), sp.jb + t);
-}
-
-// Draw weights.  kind 1 (residual after a rejection at n):
-// p_j = 2^((t_j - mt) k2) / St, q_j likewise, w_j = max(0, p_j - q_j).
-// kind 0 (bonus): w_j = 2^((t_j - mt) k2), the bonus row's own sum being the
-// normaliser.  kind 2 (a residual that rounding left without mass): w_j = p_j.
-// Weights are fp32; their sums and prefix sums are accumulated in fp64 so
-// that the CDF is as exact as the fp32 weights allow.
-struct DrawParams {
-  float rt, st_inv, rd, sd_inv, k2;  // references R(m) of target/draft row n, 1/S
-  int kind;
-};
-
-__device__ __forceinline__ float draw_weight(const DrawParams& d, float t, float q_logit) {
-  const float et = ex2(fmaf(t, d.k2, -d.rt));
-  if (d.kind == 1) {
-    const float p = et * d.st_inv;
-    const float q = ex2(fmaf(q_logit, d.k2, -d.rd)) * d.sd_inv;
-    return fmaxf(p - q, 0.f);
-  }
-  return d.kind == 2 ? et * d.st_inv : et;
+  if (t < g.head && s.hd == mx) j = lo + t;
+  v = mx;
+  idx = j;
 }
 
 // ------------------------------------------------------------------ hand-off
 // Workgroups pass data to each other through the workspace without writing
-// back the L2 (an agent-scope release fence does that, costs microseconds and
-// serialises across the device; so does an acquire's L2 invalidate).  A
-// writer stores the data with agent-scope
-// atomic stores, which complete only once the data is visible to every XCD,
-// waits for them to complete (publish), and only then takes its ticket or
-// sets its flag.  A reader that observes the last ticket or the flag does an
-// agent-scope atomic loads for the data, which are served coherently at the
-// device level; so no cache write-back or invalidate is ever needed.
+// back or invalidating the L2 (an agent-scope release fence writes back an
+// XCD's whole L2, an acquire invalidates it; both cost microseconds).  A
+// writer stores its data with agent-scope atomic stores, which are performed
+// at the device's coherence point, waits for them to complete (publish), and
+// only then counts itself in.  A reader that has seen the count loads the
+// data with agent-scope atomic loads, served at the same coherence point.
 __device__ __forceinline__ void publish() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void put64(void* p, uint64_t v) {
-  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void put64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void put_f2(float2* p, float2 v) {
-  put64(p, (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32));
-}
-__device__ __forceinline__ void put_d(double* p, double v) {
-  put64(p, (uint64_t)__double_as_longlong(v));
-}
-__device__ __forceinline__ uint64_t get64(const void* p) {
+__device__ __forceinline__ uint64_t get64(const uint64_t* p) {
   return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float2 get_f2(const float2* p) {
-  const uint64_t v = get64(p);
-  return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
+__device__ __forceinline__ uint64_t pack2(float x, float y) {
+  return (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
 }
-__device__ __forceinline__ double get_d(const double* p) {
-  return __longlong_as_double((long long)get64(p));
-}
-__device__ __forceinline__ unsigned ticket(unsigned* p) {
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((unsigned)v); }
+__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((unsigned)(v >> 32)); }
+__device__ __forceinline__ unsigned fetch_add(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void put_u(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned get_u(unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ unsigned get_u(const unsigned* p) {
+  return __hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Orders what follows after an atomic whose result `v` is: the result has
+// returned, so the atomic has been performed, before any later access issues.
+__device__ __forceinline__ void after(unsigned v) { asm volatile("" ::"v"(v) : "memory"); }
+
+// Thread 0 polls a counter until it reaches `target`; gives up after
+// max_spin polls and flags the diagnostic word.
+__device__ void wait_count(const Args& a, const unsigned* w, unsigned target) {
+  unsigned n = 0;
+  while (get_u(w) < target) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++n > a.max_spin) {
+      atomicOr(&a.hdr[1], kDiagSpin);
+      return;
+    }
+  }
 }
 
-// ------------------------------------------------------------------ helpers
-__device__ __forceinline__ int64_t trow_off(const Args& a, int b, int i) {
-  return ((int64_t)b * (a.G + 1) + i) * a.V;
-}
-__device__ __forceinline__ int64_t drow_off(const Args& a, int b, int i) {
-  return ((int64_t)b * a.G + i) * a.V;
-}
-template <int DT>
-__device__ __forceinline__ const void* row_ptr(const void* base, int64_t off) {
-  return (const char*)base + off * Elt<DT>::kBytes;
-}
-enum { kRowTicket = 0, kDrawTicket = 1, kRowFlag = 2 };
-__device__ __forceinline__ unsigned* counter(const Args& a, int which, int b) {
-  return a.ctr_end - (int64_t)(b + 1) * kRowBlock + which * kCounterStride;
-}
-
-// The row's decision, shared through LDS.
+// ------------------------------------------------------------------ LDS
 struct Decision {
   int n;        // accepted drafts
   int dead;     // 1: data error, the row holds the sentinel
   int resid;    // 1: draw from the residual at n, 0: bonus draw from p_g
   float ustar;  // uniform of the draw
   float mt, st, md, sd;  // (max, exp-sum) of target row n and draft row n
-  int n_hit;    // final draw: broadcast slot for the index found
 };
-
-constexpr int kSubChunks = 4;  // final draw: sub-slice sums held per thread
 
 struct Lds {
-  double red_d[kWaves];
-  double subs[kMaxSubs];
-  double fin_base;
-  float red[2 * kWaves];
-  float m[2 * SPEC_GAMMA_MAX_LIMIT + 1];
-  float s[2 * SPEC_GAMMA_MAX_LIMIT + 1];
+  float wm[kMaxRows][kWaves];  // per-row wave partials: m (greedy: max)
+  float ws[kMaxRows][kWaves];  // S (greedy: argmax bits)
+  float M[kMaxRows];           // merged row statistics, row r = target i (r = i)
+  float S[kMaxRows];           //   or draft i (r = g + 1 + i); greedy: argmax bits
+  uint64_t stage[kStage];
+  double red_d[8 * kWaves];
   unsigned long long mask[kWaves];
   Decision dec;
-  unsigned flag;
-  int last;
+  double dbl;
+  int pick, last;
 };
 
-// Draw-side inputs of one position, read before the row's statistics are
-// complete (they are immutable inputs): lane i of wave 0 holds x_i, u_i and
-// the target and draft logits at x_i.
-struct Gathered {
-  int x;
-  float tv, dv, u;
-};
-
-template <int DT, int MODE>
-__device__ Gathered gather_inputs(const Args& a, int b, int g) {
-  Gathered r{-1, 0.f, 0.f, 0.f};
-  const int lane = threadIdx.x;
-  if (threadIdx.x >= 64) return r;
-  if (lane < g) {
-    r.x = a.tok[(int64_t)b * a.G + lane];
-    if (MODE == SPEC_MODE_SAMPLE && (unsigned)r.x < (unsigned)a.V) {
-      r.tv = Elt<DT>::one(a.tgt, trow_off(a, b, lane) + r.x);
-      r.dv = Elt<DT>::one(a.dft, drow_off(a, b, lane) + r.x);
-    }
-  }
-  if (MODE == SPEC_MODE_SAMPLE && lane <= g) r.u = a.uni[(int64_t)b * (a.G + 1) + lane];
-  return r;
-}
-
-// ------------------------------------------------------------------ decision
-// Merges the row's chunk statistics, runs every acceptance test at once and
-// finds the first rejection with a wave ballot.  Must be called by the whole
-// workgroup after an acquire; the result is in L.dec after the call.  With
-// write_out the row's outputs (all but the drawn token when sampling) and
-// probes are written.
-template <int DT, int MODE>
-__device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, bool write_out) {
-  constexpr bool kSample = MODE == SPEC_MODE_SAMPLE;
-  const int t = threadIdx.x, lane = t & 63;
-  const int nrows = kSample ? 2 * g + 1 : g + 1;
-  for (int r = t - 64; r >= 0 && r < nrows; r += kThreads - 64) {
-    const int slot = (r <= g) ? r : (a.G + 1 + (r - g - 1));
-    const float2* pp = a.part + ((int64_t)b * a.NR + slot) * a.NC;
-    if (kSample) {
-      float m = NEG_INF, s = 0.f;
-      for (int c = 0; c < a.NC; ++c) {
-        const float2 v = get_f2(&pp[c]);
-        ms_merge(m, s, v.x, v.y, a.k2);
-      }
-      L.m[slot] = m, L.s[slot] = s;
-    } else {
-      float v = NEG_INF;
-      int i = 0x7fffffff;
-      for (int c = 0; c < a.NC; ++c) {
-        const float2 q = get_f2(&pp[c]);
-        am_merge(v, i, q.x, __float_as_int(q.y));
-      }
-      L.m[slot] = v, L.s[slot] = __int_as_float(i);
-    }
-  }
+// ------------------------------------------------------------------ block helpers
+__device__ void block_sum_d(double& a, Lds& L) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a += shfl_xor(a, o);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
-  if (t < 64) {
-    if (write_out && a.pr_m) {
-      for (int r = lane; r < nrows; r += 64) {
-        const int slot = (r <= g) ? r : (a.G + 1 + (r - g - 1));
-        const float mm = L.m[slot];
-        a.pr_m[(int64_t)b * (2 * a.G + 1) + slot] = mm;
-        // sampling: S relative to the raw max, i.e. undo the rounding of R(m)
-        const float sv = kSample && mm != NEG_INF
-                             ? L.s[slot] * ex2(-fmaf(mm, a.k2, -ref_of(mm, a.k2)))
-                             : L.s[slot];
-        if (a.pr_s) a.pr_s[(int64_t)b * (2 * a.G + 1) + slot] = sv;
-      }
-    }
-    const bool valid = (unsigned)in.x < (unsigned)a.V;
-    bool fail = false;
-    if (lane < g) {
-      if (!valid) {
-        fail = true;
-      } else if (kSample) {
-        const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.m[lane], a.k2))) / L.s[lane];
-        const int ds = a.G + 1 + lane;
-        const float q = ex2(fmaf(in.dv, a.k2, -ref_of(L.m[ds], a.k2))) / L.s[ds];
-        if (write_out && a.pr_px) {
-          a.pr_px[(int64_t)b * a.G + lane] = p;
-          a.pr_qx[(int64_t)b * a.G + lane] = q;
-        }
-        fail = !(in.u * q < p);
-      } else {
-        fail = (in.x != __float_as_int(L.s[lane]));
-      }
-    }
-    const unsigned long long mask = __ballot(fail);
-    const int n = mask ? (__ffsll((long long)mask) - 1) : g;
-    const bool bad_token = mask && (__shfl(valid ? 1 : 0, n, 64) == 0);
-    // sampling: a row the walk uses must have a finite logit.  A dead p_i or
-    // q_i makes the test at i fail (NaN), so only the stop position can hold
-    // one; rows after the stop are never used.
-    const bool dead_n = kSample && (L.m[n] == NEG_INF || (n < g && L.m[a.G + 1 + n] == NEG_INF));
-    const bool sentinel = dead_n || bad_token;
-    const float ustar = __shfl(in.u, n < g ? n + 1 : g, 64);
-    if (write_out) {
-      // gamma_max <= 63, so lane i owns output position i (and holds x_i)
-      if (lane <= a.G && !(kSample && lane == n && !sentinel)) {
-        int v = -1;
-        if (!sentinel && lane < n)
-          v = in.x;
-        else if (!sentinel && lane == n)
-          v = __float_as_int(L.s[n]);  // greedy: the target's argmax at n
-        a.out_tok[(int64_t)b * (a.G + 1) + lane] = v;
-      }
-      if (lane == 0) {
-        const int kv = a.kv ? a.kv[b] : 0;
-        a.out_n[b] = sentinel ? -1 : n;
-        a.out_len[b] = sentinel ? kv : kv + n;
-      }
-    }
-    if (lane == 0) {
-      Decision d;
-      d.n = n, d.dead = sentinel, d.resid = n < g, d.ustar = ustar;
-      d.mt = L.m[n], d.st = L.s[n];
-      d.md = n < g ? L.m[a.G + 1 + n] : 0.f;
-      d.sd = n < g ? L.s[a.G + 1 + n] : 1.f;
-      L.dec = d;
-    }
-  }
+  if (lane == 0) L.red_d[w] = a;
+  __syncthreads();
+  a = L.red_d[0];
+  for (int k = 1; k < kWaves; ++k) a += L.red_d[k];
   __syncthreads();
 }
 
-__device__ void write_sentinel(const Args& a, int b) {
-  for (int i = threadIdx.x; i <= a.G; i += kThreads) a.out_tok[(int64_t)b * (a.G + 1) + i] = -1;
-  if (threadIdx.x == 0) {
-    a.out_n[b] = -1;
-    a.out_len[b] = a.kv ? a.kv[b] : 0;
-  }
-}
-
-// ------------------------------------------------------------------ draw
-// A slice of SL elements is cut into sub-slices of kSub elements.  A draw
-// item writes the fp64 weight sum of each of its sub-slices and of the whole
-// slice.  The row's last draw item then descends slices -> sub-slices ->
-// elements, at each level finding the first entry whose running sum exceeds
-// tau = u * Z with a block-wide fp64 prefix scan.
-
-template <int DT>
-__device__ __forceinline__ float weight_at(const DrawParams& d, const void* trow,
-                                           const void* drow, int j) {
-  return draw_weight(d, Elt<DT>::one(trow, j), d.kind == 1 ? Elt<DT>::one(drow, j) : 0.f);
-}
-
-template <int DT>
-__device__ void draw_slice(const Args& a, Lds& L, int b, int slot, const void* trow,
-                           const void* drow, const DrawParams& d) {
-  using E = Elt<DT>;
-  constexpr int kGroup = kSub / E::kVec;  // threads sharing one sub-slice
-  const int t = threadIdx.x;
-  const int lo = slot * a.SL, hi = min(a.V, lo + a.SL), len = hi - lo;
-  const int nsub = (len + kSub - 1) / kSub;
-  const bool two = d.kind == 1;
-  const bool vec = (((uintptr_t)((const char*)trow + (int64_t)lo * E::kBytes)) & 15u) == 0 &&
-                   (!two || (((uintptr_t)((const char*)drow + (int64_t)lo * E::kBytes)) & 15u) == 0);
-  if (vec) {
-    const uint4* tv = (const uint4*)((const char*)trow + (int64_t)lo * E::kBytes);
-    const uint4* dv = (const uint4*)((const char*)drow + (int64_t)lo * E::kBytes);
-    const int nfull = len / E::kVec;                       // whole 16-byte vectors
-    const int nround = (len + kThreads * E::kVec - 1) / (kThreads * E::kVec);
-    for (int r0 = 0; r0 < nround; r0 += 4) {
-      uint4 rt[4], rd[4];
+// Block totals of N doubles per thread at once; every thread gets them.
+template <int N>
+__device__ void block_sums_n(const double (&v)[N], double (&tot)[N], Lds& L) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double x[N];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = (r0 + u) * kThreads + t;
-        if (r0 + u < nround && k < nfull) {
-          rt[u] = tv[k];
-          if (two) rd[u] = dv[k];
-        }
-      }
+  for (int n = 0; n < N; ++n) {
+    x[n] = v[n];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + u;
-        if (r >= nround) break;
-        const int k = r * kThreads + t;
-        double ws = 0.0;
-        if (k < nfull) {
-          float ft[E::kVec], fd[E::kVec];
-          E::unpack(rt[u], ft);
-          if (two) E::unpack(rd[u], fd);
-#pragma unroll
-          for (int e = 0; e < E::kVec; ++e) ws += (double)draw_weight(d, ft[e], two ? fd[e] : 0.f);
-        } else {
-          for (int j = lo + k * E::kVec; j < min(hi, lo + (k + 1) * E::kVec); ++j)
-            ws += (double)weight_at<DT>(d, trow, drow, j);
-        }
-#pragma unroll
-        for (int o = kGroup / 2; o >= 1; o >>= 1) ws += shfl_xor(ws, o);
-        const int sidx = r * E::kVec + t / kGroup;
-        if ((t % kGroup) == 0 && sidx < nsub) L.subs[sidx] = ws;
-      }
-    }
-  } else {
-    // rows not 16-byte aligned here: one element per thread per sub-slice
-    for (int k = 0; k < nsub; ++k) {
-      const int j = lo + k * kSub + t;
-      double ws = j < hi ? (double)weight_at<DT>(d, trow, drow, j) : 0.0;
-      block_sum_d(ws, L.red_d);
-      if (t == 0) L.subs[k] = ws;
-    }
+    for (int o = 32; o >= 1; o >>= 1) x[n] += shfl_xor(x[n], o);
   }
   __syncthreads();
-  double* sub = a.sub + ((int64_t)b * a.ND + slot) * (a.SL / kSub);
-  if (t < nsub) put_d(&sub[t], L.subs[t]);
+  if (lane == 0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) L.red_d[n * kWaves + w] = x[n];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    double s = L.red_d[n * kWaves];
+    for (int k = 1; k < kWaves; ++k) s += L.red_d[n * kWaves + k];
+    tot[n] = s;
+  }
+  __syncthreads();
 }
 
 // Inclusive and exclusive block prefix sums of one double per thread, in a
-// fixed order (deterministic).  `total` is the sum over the block.
-__device__ void block_scan_d(double v, double* red, double& incl, double& excl, double& total) {
+// fixed order (deterministic); `total` is the sum over the block.
+__device__ void block_scan_d(double v, Lds& L, double& incl, double& excl, double& total) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   double x = v;
 #pragma unroll
@@ -662,20 +535,20 @@ __device__ void block_scan_d(double v, double* red, double& incl, double& excl, 
   double prev = __shfl_up(x, 1, 64);
   if (lane == 0) prev = 0.0;
   __syncthreads();
-  if (lane == 63) red[w] = x;
+  if (lane == 63) L.red_d[w] = x;
   __syncthreads();
   double off = 0.0, tot = 0.0;
   for (int k = 0; k < kWaves; ++k) {
-    if (k < w) off += red[k];
-    tot += red[k];
+    if (k < w) off += L.red_d[k];
+    tot += L.red_d[k];
   }
   incl = off + x;
   excl = off + prev;
   total = tot;
+  __syncthreads();
 }
 
-// Lowest (highest) thread index whose predicate holds, or -1: one wave
-// ballot per wave, then a scan of kWaves masks.
+// Lowest (highest) thread index whose predicate holds, or -1.
 __device__ int block_first(bool pred, Lds& L) {
   const unsigned long long m = __ballot(pred);
   if ((threadIdx.x & 63) == 0) L.mask[threadIdx.x >> 6] = m;
@@ -704,297 +577,611 @@ __device__ int block_last(bool pred, Lds& L) {
   return r;
 }
 
-// First index i in [0, count) with weight val(i) > 0 and tau < base + the
-// inclusive prefix at i (one entry per thread per chunk of kThreads).  On
-// success returns i and the exclusive prefix at i (base included) in
-// base_out.  If rounding leaves no such index, returns -(1 + the last index
-// with positive weight), or INT_MIN if there is none.
-template <class F>
-__device__ int block_find(int count, double base, double tau, F val, Lds& L, double& base_out) {
-  const int t = threadIdx.x;
-  double carry = base;
-  int lastpos = -1;
-  for (int c0 = 0; c0 < count; c0 += kThreads) {
-    const int i = c0 + t;
-    const double v = i < count ? val(i) : 0.0;
-    double incl, excl, tot;
-    block_scan_d(v, L.red_d, incl, excl, tot);
-    const bool pos = i < count && v > 0.0;
-    const int first = block_first(pos && tau < carry + incl, L);
-    if (first >= 0) {
-      if (t == first) L.fin_base = carry + excl;
-      __syncthreads();
-      base_out = L.fin_base;
-      __syncthreads();
-      return c0 + first;
-    }
-    const int last = block_last(pos, L);
-    if (last >= 0) lastpos = c0 + last;
-    carry += tot;
-  }
-  return lastpos >= 0 ? -(1 + lastpos) : (int)0x80000000;
-}
-
-__device__ __forceinline__ DrawParams draw_params(const Decision& dc, float k2) {
-  return DrawParams{ref_of(dc.mt, k2), 1.f / dc.st, ref_of(dc.md, k2), 1.f / dc.sd, k2,
-                    dc.resid ? 1 : 0};
-}
-
-// Number of sub-slices of slice s.
-__device__ __forceinline__ int subs_in_slice(const Args& a, int s) {
-  const int lo = s * a.SL;
-  return (min(a.V, lo + a.SL) - lo + kSub - 1) / kSub;
-}
-
-// Sum Z of the row's sub-slice weights and the first sub-slice whose running
-// sum exceeds tau = u * Z, over the flattened (slice, sub-slice) array with
-// every entry prefetched at once (count <= kThreads * kSubChunks).  Returns
-// the flat index, or -(1 + last positive entry) when rounding leaves no hit.
-template <class F>
-__device__ int find_sub_prefetched(int count, float u, F val, Lds& L, double& base_out,
-                                   double& z_out) {
-  const int t = threadIdx.x;
-  // thread t owns entries [t * kSubChunks, (t + 1) * kSubChunks)
-  double v[kSubChunks];
-  double mine = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSubChunks; ++e) {
-    const int i = t * kSubChunks + e;
-    v[e] = i < count ? val(i) : 0.0;
-  }
-#pragma unroll
-  for (int e = 0; e < kSubChunks; ++e) mine += v[e];
-  double incl, excl, z;
-  block_scan_d(mine, L.red_d, incl, excl, z);
-  z_out = z;
-  const double tau = (double)u * z;
-  // first entry, in order, whose running sum exceeds tau; last positive entry
-  double c = excl;
-  int hit = -1, lastpos = -1;
-  double hit_base = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSubChunks; ++e) {
-    const double nxt = c + v[e];
-    if (v[e] > 0.0) {
-      lastpos = t * kSubChunks + e;
-      if (hit < 0 && tau < nxt) hit = t * kSubChunks + e, hit_base = c;
-    }
-    c = nxt;
-  }
-  const int owner = block_first(hit >= 0, L);
-  if (owner >= 0) {
-    if (t == owner) L.fin_base = hit_base, L.dec.n_hit = hit;
-    __syncthreads();
-    base_out = L.fin_base;
-    const int r = L.dec.n_hit;
-    __syncthreads();
-    return r;
-  }
-  const int lo = block_last(lastpos >= 0, L);
-  if (lo >= 0) {
-    if (t == lo) L.dec.n_hit = lastpos;
-    __syncthreads();
-    const int r = L.dec.n_hit;
-    __syncthreads();
-    return -(1 + r);
-  }
-  return (int)0x80000000;
-}
-
-// Run by the row's last draw item; its own L.dec holds the row's decision.
+// ------------------------------------------------------------------ row access
 template <int DT>
-__device__ void final_draw(const Args& a, Lds& L, int b) {
-  const int t = threadIdx.x;
-  const int n = L.dec.n;
-  DrawParams d = draw_params(L.dec, a.k2);
-  const void* trow = row_ptr<DT>(a.tgt, trow_off(a, b, n));
-  const void* drow = L.dec.resid ? row_ptr<DT>(a.dft, drow_off(a, b, n)) : trow;
-  const int nsub_max = a.SL / kSub;
-  const double* sub = a.sub + (int64_t)b * a.ND * nsub_max;
-  // flattened (slice, sub-slice) entries; the last slice may hold fewer
-  auto sub_val = [&](int i) {
-    const int s = i / nsub_max, k = i % nsub_max;
-    return k < subs_in_slice(a, s) ? get_d(&sub[i]) : 0.0;
-  };
-  const int count = a.ND * nsub_max;
-  const auto pick = [](int r) { return r >= 0 ? r : (r == (int)0x80000000 ? 0 : -(r + 1)); };
-  double base = 0.0, z = 0.0, tau = 0.0;
-  int fs = 0;
-  bool fallback = false;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    if (count <= kThreads * kSubChunks) {
-      fs = find_sub_prefetched(count, L.dec.ustar, sub_val, L, base, z);
-      tau = (double)L.dec.ustar * z;
-    } else {
-      // long vocabularies: total first, then a chunked search
-      z = 0.0;
-      for (int c0 = 0; c0 < count; c0 += kThreads) {
-        const int i = c0 + t;
-        double incl, excl, tot;
-        block_scan_d(i < count ? sub_val(i) : 0.0, L.red_d, incl, excl, tot);
-        z += tot;
-      }
-      tau = (double)L.dec.ustar * z;
-      fs = block_find(count, 0.0, tau, sub_val, L, base);
-    }
-    if (z > 0.0 || d.kind != 1) break;
-    // rounding left the residual without mass: draw from p_n instead (slow
-    // path, one sub-slice per thread; exact arithmetic never gets here)
-    d.kind = 2;
-    for (int f = t; f < count; f += kThreads) {
-      const int s = f / nsub_max, k = f % nsub_max;
-      double acc = 0.0;
-      if (k < subs_in_slice(a, s)) {
-        const int j0 = s * a.SL + k * kSub, j1 = min(a.V, j0 + kSub);
-        for (int j = j0; j < j1; ++j) acc += (double)weight_at<DT>(d, trow, drow, j);
-      }
-      put_d(const_cast<double*>(&sub[f]), acc);
-    }
-    publish();
-    __syncthreads();
-    if (t == 0) atomicOr(&a.hdr[1], kDiagZeroResid);
-  }
-  if (a.pr_z && t == 0) a.pr_z[b] = (float)(d.kind == 0 ? z * (double)d.st_inv : z);
-  fallback = fs < 0;
-  fs = pick(fs);
-  // elements of that sub-slice: one per thread
-  const int s = fs / nsub_max, k = fs % nsub_max;
-  const int j0 = s * a.SL + k * kSub;
-  const int cnt = min(kSub, a.V - j0);
-  const double never = __builtin_inf();
-  int j = block_find(cnt, base, fallback ? never : tau,
-                     [&](int i) { return (double)weight_at<DT>(d, trow, drow, j0 + i); }, L, base);
-  j = pick(j);
-  if (t == 0) a.out_tok[(int64_t)b * (a.G + 1) + n] = j0 + j;
+__device__ __forceinline__ const char* row_of(const Args& a, int b, int g, int r) {
+  const int64_t off = r <= g ? ((int64_t)b * (a.G + 1) + r) * a.V
+                             : ((int64_t)b * a.G + (r - g - 1)) * a.V;
+  return (const char*)(r <= g ? a.tgt : a.dft) + off * Elt<DT>::kBytes;
 }
 
-// ------------------------------------------------------------------ kernel
-template <int DT, int MODE>
-__global__ __launch_bounds__(kThreads) void verify_kernel(Args a) {
+// Probe slot of row r: target rows 0..gamma_max, then draft rows.
+__device__ __forceinline__ int probe_slot(const Args& a, int g, int r) {
+  return r <= g ? r : a.G + 1 + (r - g - 1);
+}
+
+// ------------------------------------------------------------------ step 1
+// (m, S) of a wave's share of a slice, in every lane: the wave's largest
+// logit first, then one sum against it (no rescaling), four partial sums for
+// instruction-level parallelism, then the wave sum.
+template <int DT, int R>
+__device__ __forceinline__ void wave_slice_ms(const Slice<DT, R>& s, const Geom& g, float k2,
+                                              float& m, float& S) {
+  using E = Elt<DT>;
+  float mx = fmaxf(s.hd, s.tl);
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    float f[E::kVec];
+    E::unpack(vget(s, k, g), f);
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) mx = fmaxf(mx, f[e]);
+  }
+  mx = wave_max(mx);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (mx != NEG_INF) {  // uniform across the wave
+    const float Rf = ref_of(mx, k2);
+    acc[0] = ex2(fmaf(s.hd, k2, -Rf));
+    acc[1] = ex2(fmaf(s.tl, k2, -Rf));
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      float f[E::kVec];
+      E::unpack(vget(s, k, g), f);
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) acc[e & 3] += ex2(fmaf(f[e], k2, -Rf));
+    }
+  }
+  m = mx;
+  S = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+}
+
+// 16-byte vectors per thread kept in flight while streaming: rows of the
+// ring = kRingVectors / R.
+constexpr int kRingVectors = 12;
+
+// Streams this workgroup's slice of rows 0..nrows-1 and leaves each row's
+// slice pair in L.M / L.S (sampling: (m, S); greedy: (max, argmax bits)).
+// The loads of the next NB-1 rows are in flight while a row is reduced; the
+// ring is indexed at compile time (the row loop is unrolled by NB) and the
+// loads are unconditional -- past the last row they re-read it -- so the
+// waits stay counted exactly.
+template <int DT, int MODE, int R, bool AL>
+__device__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int lo, int len) {
   constexpr bool kSample = MODE == SPEC_MODE_SAMPLE;
-  __shared__ Lds L;
-  const int t = threadIdx.x;
-  const int64_t id = blockIdx.x;
-
-  // decode the workgroup id: rows 0..L-1 statistics, then [stats(L+k),
-  // draws(k)] blocks, then the remaining draws.
-  int b, slot;
-  bool is_draw;
-  {
-    const int64_t head = (int64_t)a.L * a.NP;
-    if (a.ND == 0 || id < head) {
-      b = (int)(id / a.NP), slot = (int)(id % a.NP), is_draw = false;
-    } else {
-      const int64_t blk = a.NP + a.ND;
-      const int64_t id2 = id - head;
-      const int64_t k = id2 / blk;
-      if (k < a.B - a.L) {
-        const int off = (int)(id2 % blk);
-        if (off < a.NP)
-          b = (int)(a.L + k), slot = off, is_draw = false;
-        else
-          b = (int)k, slot = off - a.NP, is_draw = true;
+  constexpr int NB = kRingVectors / R > 2 ? kRingVectors / R : 2;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  Slice<DT, R> buf[NB];
+  Geom geo[NB];
+  auto issue = [&](int r, Slice<DT, R>& sl, Geom& gg) {
+    const int rr = r < nrows ? r : nrows - 1;
+    const char* p = row_of<DT>(a, b, g, rr) + (int64_t)lo * Elt<DT>::kBytes;
+    gg = geom_of<DT, AL>(p, len);
+    load_slice<DT, R, AL>(p, gg, sl);
+  };
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j) issue(j, buf[j], geo[j]);
+  // whole groups of NB rows: no exit inside the unrolled body, whose rows
+  // past the end reduce a re-read of the last row and store nothing
+  for (int r0 = 0; r0 < nrows; r0 += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int r = r0 + j;
+      issue(r + NB - 1, buf[(j + NB - 1) % NB], geo[(j + NB - 1) % NB]);
+      if (kSample) {
+        float m, sm;
+        wave_slice_ms<DT, R>(buf[j], geo[j], a.k2, m, sm);
+        if (lane == 0 && r < nrows) L.wm[r][w] = m, L.ws[r][w] = sm;
       } else {
-        const int64_t id3 = id2 - (int64_t)(a.B - a.L) * blk;
-        b = (int)(a.B - a.L + id3 / a.ND), slot = (int)(id3 % a.ND), is_draw = true;
+        float v;
+        int ix;
+        slice_am<DT, R>(buf[j], geo[j], lo, v, ix);
+        wave_am_dpp(v, ix);
+        if (lane == 0 && r < nrows) L.wm[r][w] = v, L.ws[r][w] = __int_as_float(ix);
       }
     }
-  }
-  const int g = a.gam[b];
-  const bool gvalid = (g >= 0) && (g <= a.G);
-
-  if (!is_draw) {
-    if (!gvalid) {
-      if (slot == 0) {
-        write_sentinel(a, b);
-        if (kSample && t == 0) put_u(counter(a, kRowFlag, b), kFlagNone);
-      }
-      return;
-    }
-    const int nrows = kSample ? 2 * g + 1 : g + 1;
-    const int r = slot / a.NC, c = slot % a.NC;
-    if (r >= nrows) return;  // padding of a short row: no work, no ticket
-    const bool is_target = r <= g;
-    const int i = is_target ? r : r - g - 1;
-    const int pslot = is_target ? i : a.G + 1 + i;
-    const void* row = is_target ? row_ptr<DT>(a.tgt, trow_off(a, b, i))
-                                : row_ptr<DT>(a.dft, drow_off(a, b, i));
-    const int lo = c * a.CH, hi = min(a.V, lo + a.CH);
-    float2 res;
-    if (kSample) {
-      float m = NEG_INF, s = 0.f;
-      stats_range<DT>(row, lo, hi, a.k2, m, s);
-      block_ms(m, s, a.k2, L.red);
-      res = make_float2(m, s);
-    } else {
-      float v = NEG_INF;
-      int ix = 0x7fffffff;
-      argmax_range<DT>(row, lo, hi, v, ix);
-      block_am(v, ix, L.red);
-      res = make_float2(v, __int_as_float(ix));
-    }
-    if (t == 0) {
-      put_f2(&a.part[((int64_t)b * a.NR + pslot) * a.NC + c], res);
-      publish();
-      const unsigned tk = ticket(counter(a, kRowTicket, b));
-      L.last = (tk == (unsigned)(nrows * a.NC) - 1);
-      if (L.last) {
-        put_u(counter(a, kRowTicket, b), 0u);
-        // sampling: the row's draw items take the decision from here on
-        if (kSample) put_u(counter(a, kRowFlag, b), kFlagStats);
-      }
-    }
-    __syncthreads();
-    if (kSample || !L.last) return;
-    const Gathered in = gather_inputs<DT, MODE>(a, b, g);
-    decide<DT, MODE>(a, L, b, g, in, true);
-    return;
-  }
-
-  // ---------------- draw item (b, slot): sampling only
-  Gathered in{-1, 0.f, 0.f, 0.f};
-  if (gvalid) in = gather_inputs<DT, MODE>(a, b, g);  // immutable inputs: read while waiting
-  if (t == 0) {
-    unsigned f = get_u(counter(a, kRowFlag, b));
-    unsigned spins = 0;
-    while (f == 0u) {
-      __builtin_amdgcn_s_sleep(2);
-      f = get_u(counter(a, kRowFlag, b));
-      if (++spins > a.max_spin) {
-        atomicOr(&a.hdr[1], kDiagSpin);
-        f = kFlagNone;
-        break;
-      }
-    }
-    L.flag = f;
   }
   __syncthreads();
-  bool work = false;
-  if (L.flag == kFlagStats) {
-    decide<DT, MODE>(a, L, b, g, in, slot == 0);
-    work = !L.dec.dead;
+  for (int r = t; r < nrows; r += kThreads) {
+    float m = L.wm[r][0], s = L.ws[r][0];
+    for (int k = 1; k < kWaves; ++k) {
+      if (kSample) {
+        ms_merge(m, s, L.wm[r][k], L.ws[r][k], a.k2);
+      } else {
+        int i = __float_as_int(s);
+        am_merge(m, i, L.wm[r][k], __float_as_int(L.ws[r][k]));
+        s = __int_as_float(i);
+      }
+    }
+    L.M[r] = m, L.S[r] = s;
   }
-  if (work) {
-    const int n = L.dec.n;
-    const DrawParams d = draw_params(L.dec, a.k2);
-    const void* trow = row_ptr<DT>(a.tgt, trow_off(a, b, n));
-    const void* drow = L.dec.resid ? row_ptr<DT>(a.dft, drow_off(a, b, n)) : trow;
-    draw_slice<DT>(a, L, b, slot, trow, drow, d);
+  __syncthreads();
+}
+
+// Publishes this slice's pairs (entry r of the slice's record).  No written
+// word is zero: S >= 1 whenever m is finite, m = -inf has non-zero bits, and
+// the argmax is stored plus one.
+template <bool kSample>
+__device__ void publish_pairs(const Args& a, Lds& L, int b, int c, int nrows) {
+  uint64_t* rec = a.part + ((int64_t)b * a.NC + c) * a.NR;
+  for (int r = threadIdx.x; r < nrows; r += kThreads) {
+    const float s = kSample ? L.S[r] : __int_as_float(__float_as_int(L.S[r]) + 1);
+    put64(&rec[r], pack2(L.M[r], s));
   }
+  publish();
+  __syncthreads();
+}
+
+// Merges the group's published pairs into L.M / L.S, in the same fixed order
+// in every workgroup: per row, lane l takes slices l, l + 64, ... in turn,
+// then a butterfly across the wave.  Rows go to waves round-robin, staged
+// through LDS in batches.
+template <bool kSample>
+__device__ void merge_group(const Args& a, Lds& L, int b, int nrows) {
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int nc = a.NC;
+  const uint64_t* base = a.part + (int64_t)b * nc * a.NR;
+  const int per = kStage / nc > 0 ? kStage / nc : 1;
+  for (int r0 = 0; r0 < nrows; r0 += per) {
+    const int r1 = min(nrows, r0 + per);
+    const int cnt = (r1 - r0) * nc;
+    for (int k = t; k < cnt; k += kThreads) {
+      const int r = r0 + k / nc, c = k % nc;
+      L.stage[k] = get64(&base[(int64_t)c * a.NR + r]);
+    }
+    __syncthreads();
+    for (int r = r0 + w; r < r1; r += kWaves) {
+      const uint64_t* st = &L.stage[(r - r0) * nc];
+      if (kSample) {
+        float m = NEG_INF, s = 0.f;
+        for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
+        wave_ms_dpp(m, s, a.k2);
+        if (lane == 0) L.M[r] = m, L.S[r] = s;
+      } else {
+        float v = NEG_INF;
+        int i = 0x7fffffff;
+        for (int c = lane; c < nc; c += 64)
+          am_merge(v, i, lo_f(st[c]), (int)__float_as_uint(hi_f(st[c])) - 1);
+        wave_am_dpp(v, i);
+        if (lane == 0) L.M[r] = v, L.S[r] = __int_as_float(i);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ decision
+// Immutable per-position inputs, read at the start: lane i of wave 0 holds
+// x_i, u_i and the target and draft logits at x_i.
+struct Gathered {
+  int x;
+  float tv, dv, u;
+};
+
+// x_i and u_i: read at the start, before the row loads.
+template <int MODE>
+__device__ Gathered gather_small(const Args& a, int b, int g) {
+  Gathered r{-1, 0.f, 0.f, 0.f};
+  const int lane = threadIdx.x;
+  if (threadIdx.x >= 64) return r;
+  if (lane < g) r.x = a.tok[(int64_t)b * a.G + lane];
+  if (MODE == SPEC_MODE_SAMPLE && lane <= g) r.u = a.uni[(int64_t)b * (a.G + 1) + lane];
+  return r;
+}
+
+// t[x_i] and d[x_i]: issued once the row loads are done (they depend on x_i,
+// and waiting for them earlier would hold up the streaming).
+template <int DT>
+__device__ void gather_logits(const Args& a, int b, int g, Gathered& r) {
+  const int lane = threadIdx.x;
+  if (threadIdx.x < 64 && lane < g && (unsigned)r.x < (unsigned)a.V) {
+    r.tv = Elt<DT>::one(row_of<DT>(a, b, g, lane), r.x);
+    r.dv = Elt<DT>::one(row_of<DT>(a, b, g, g + 1 + lane), r.x);
+  }
+}
+
+// Runs every acceptance test at once from the merged statistics in L.M/L.S
+// and finds the first rejection with a wave ballot; the result is in L.dec.
+// With write_out the row's outputs (sampling: all but the drawn token) and
+// probes are written.
+template <int DT, int MODE>
+__device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, bool write_out) {
+  constexpr bool kSample = MODE == SPEC_MODE_SAMPLE;
+  const int t = threadIdx.x, lane = t & 63;
+  const int nrows = kSample ? 2 * g + 1 : g + 1;
+  if (t < 64) {
+    if (write_out && a.pr_m) {
+      for (int r = lane; r < nrows; r += 64) {
+        const int slot = probe_slot(a, g, r);
+        const float mm = L.M[r];
+        a.pr_m[(int64_t)b * (2 * a.G + 1) + slot] = mm;
+        // sampling: S relative to the raw max, i.e. undo the rounding of R(m)
+        const float sv = kSample && mm != NEG_INF
+                             ? L.S[r] * ex2(-fmaf(mm, a.k2, -ref_of(mm, a.k2)))
+                             : (kSample ? L.S[r] : (float)__float_as_int(L.S[r]));
+        if (a.pr_s) a.pr_s[(int64_t)b * (2 * a.G + 1) + slot] = sv;
+      }
+    }
+    const bool valid = (unsigned)in.x < (unsigned)a.V;
+    bool fail = false;
+    if (lane < g) {
+      if (!valid) {
+        fail = true;
+      } else if (kSample) {
+        const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.M[lane], a.k2))) / L.S[lane];
+        const int dr = g + 1 + lane;
+        const float q = ex2(fmaf(in.dv, a.k2, -ref_of(L.M[dr], a.k2))) / L.S[dr];
+        if (write_out && a.pr_px) {
+          a.pr_px[(int64_t)b * a.G + lane] = p;
+          a.pr_qx[(int64_t)b * a.G + lane] = q;
+        }
+        fail = !(in.u * q < p);
+      } else {
+        fail = (in.x != __float_as_int(L.S[lane]));
+      }
+    }
+    const unsigned long long mask = __ballot(fail);
+    const int n = mask ? (__ffsll((long long)mask) - 1) : g;
+    const bool bad_token = mask && (__shfl(valid ? 1 : 0, n, 64) == 0);
+    // sampling: a row the walk uses must have a finite logit.  A dead p_i or
+    // q_i makes the test at i fail (NaN), so only the stop position can hold
+    // one; rows after the stop are never used.
+    const bool dead_n = kSample && (L.M[n] == NEG_INF || (n < g && L.M[g + 1 + n] == NEG_INF));
+    const bool sentinel = dead_n || bad_token;
+    const float ustar = __shfl(in.u, n < g ? n + 1 : g, 64);
+    if (write_out) {
+      // gamma_max <= 63, so lane i owns output position i (and holds x_i)
+      if (lane <= a.G && !(kSample && lane == n && !sentinel)) {
+        int v = -1;
+        if (!sentinel && lane < n)
+          v = in.x;
+        else if (!sentinel && lane == n)
+          v = __float_as_int(L.S[n]);  // greedy: the target's argmax at n
+        a.out_tok[(int64_t)b * (a.G + 1) + lane] = v;
+      }
+      if (lane == 0) {
+        const int kv = a.kv ? a.kv[b] : 0;
+        a.out_n[b] = sentinel ? -1 : n;
+        a.out_len[b] = sentinel ? kv : kv + n;
+      }
+    }
+    if (lane == 0) {
+      Decision d;
+      d.n = n, d.dead = sentinel, d.resid = n < g, d.ustar = ustar;
+      d.mt = L.M[n], d.st = L.S[n];
+      d.md = n < g ? L.M[g + 1 + n] : 0.f;
+      d.sd = n < g ? L.S[g + 1 + n] : 1.f;
+      L.dec = d;
+    }
+  }
+  __syncthreads();
+}
+
+__device__ void write_sentinel(const Args& a, int b) {
+  for (int i = threadIdx.x; i <= a.G; i += kThreads) a.out_tok[(int64_t)b * (a.G + 1) + i] = -1;
+  if (threadIdx.x == 0) {
+    a.out_n[b] = -1;
+    a.out_len[b] = a.kv ? a.kv[b] : 0;
+  }
+}
+
+// ------------------------------------------------------------------ draw
+// Draw weights.  Residual after a rejection at n (RESID):
+// p_j = 2^((t_j - mt) k2) / St, q_j likewise, w_j = max(0, p_j - q_j).
+// Otherwise w_j = 2^((t_j - mt) k2) * scale: the bonus draw (scale 1, the
+// bonus row's own sum being the normaliser) or p_j for a residual that
+// rounding left without mass (scale 1/St).  Weights are fp32; their sums and
+// prefix sums are accumulated in fp64 so that the CDF is as exact as the fp32
+// weights allow.  Absent elements (-inf) weigh 0.
+struct DrawParams {
+  float rt, st_inv, rd, sd_inv, k2;  // references R(m) of target/draft row n, 1/S
+  float scale;                       // plain weights: 1 (bonus) or 1/St (fallback)
+};
+
+template <bool RESID>
+__device__ __forceinline__ float draw_weight(const DrawParams& d, float t, float q_logit) {
+  const float et = ex2(fmaf(t, d.k2, -d.rt));
+  if (RESID) {
+    const float p = et * d.st_inv;
+    const float q = ex2(fmaf(q_logit, d.k2, -d.rd)) * d.sd_inv;
+    return fmaxf(p - q, 0.f);
+  }
+  return et * d.scale;
+}
+
+template <int DT, bool RESID>
+__device__ __forceinline__ void vec_weights(const DrawParams& d, const uint4& vt, const uint4& vd,
+                                            float* w) {
+  using E = Elt<DT>;
+  float ft[E::kVec], fd[E::kVec];
+  E::unpack(vt, ft);
+  if (RESID) E::unpack(vd, fd);
+#pragma unroll
+  for (int e = 0; e < E::kVec; ++e) w[e] = draw_weight<RESID>(d, ft[e], RESID ? fd[e] : 0.f);
+}
+
+// This thread's weight sums by segment: [0] head, [1 + k] body round k,
+// [R + 1] tail (index order of the slice).
+template <int DT, int R, bool RESID>
+__device__ __forceinline__ void segment_sums(const DrawParams& d, const Slice<DT, R>& st,
+                                             const Slice<DT, R>& sd, const Geom& g,
+                                             double (&v)[R + 2]) {
+  using E = Elt<DT>;
+  v[0] = (double)draw_weight<RESID>(d, st.hd, sd.hd);
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    float w[E::kVec];
+    vec_weights<DT, RESID>(d, vget(st, k, g), vget(sd, k, g), w);
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) s += (double)w[e];
+    v[1 + k] = s;
+    __builtin_amdgcn_sched_barrier(0);  // one vector's weights live at a time
+  }
+  v[R + 1] = (double)draw_weight<RESID>(d, st.tl, sd.tl);
+}
+
+// Finds the slice holding tau = u * Z from the group's published slice sums
+// (one per thread).  Returns the slice and the sum of the slices before it
+// (base); z_out = Z.  When rounding leaves no slice whose running sum exceeds
+// tau, returns the last slice with positive weight and sets fallback; -1 if
+// no slice has weight.
+__device__ int find_owner(const uint64_t* ws, int nc, float u, Lds& L, double& base,
+                          double& z_out, bool& fallback) {
+  const int t = threadIdx.x;
+  const double v = t < nc ? __longlong_as_double((long long)~get64(&ws[t])) : 0.0;
+  double incl, excl, z;
+  block_scan_d(v, L, incl, excl, z);
+  z_out = z;
+  const double tau = (double)u * z;
+  int r = block_first(v > 0.0 && tau < incl, L);
+  fallback = r < 0;
+  if (r < 0) r = block_last(v > 0.0, L);
+  if (r < 0) {
+    base = 0.0;
+    return -1;
+  }
+  if (t == r) L.dbl = excl;
+  __syncthreads();
+  base = L.dbl;
+  __syncthreads();
+  return r;
+}
+
+// Inverse CDF inside the owner's slice: the first element of positive weight
+// whose running sum (base + the weights before it, in index order) exceeds
+// tau; if rounding leaves none, the last element with positive weight.
+// Returns its index in the row.
+template <int DT, int R, bool RESID>
+__device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const Slice<DT, R>& sd,
+                            const Geom& g, int lo, double base, double tau, Lds& L) {
+  using E = Elt<DT>;
+  constexpr int NS = R + 2;
+  const int t = threadIdx.x;
+  double v[NS], tot[NS];
+  segment_sums<DT, R, RESID>(d, st, sd, g, v);
+  block_sums_n<NS>(v, tot, L);
+  // the segment holding tau (all threads alike)
+  double carry = base;
+  int seg = -1, lastseg = -1;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (tot[s] > 0.0) lastseg = s;
+    if (seg < 0) {
+      if (tot[s] > 0.0 && tau < carry + tot[s])
+        seg = s;
+      else
+        carry += tot[s];
+    }
+  }
+  bool fb = false;
+  if (seg < 0) {
+    if (lastseg < 0) return lo;  // no mass in the slice (cannot happen for an owner)
+    fb = true;
+    seg = lastseg;
+    carry = base;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (s < seg) carry += tot[s];
+  }
+  double vs = 0.0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s == seg) vs = v[s];
+  double incl, excl, ts;
+  block_scan_d(vs, L, incl, excl, ts);
+  int th = fb ? -1 : block_first(vs > 0.0 && tau < carry + incl, L);
+  if (th < 0) {
+    fb = true;
+    th = block_last(vs > 0.0, L);
+  }
+  if (th < 0) th = 0;
+  if (t == th) {
+    Slice<DT, R> st2 = st, sd2 = sd;
+    opaque(st2), opaque(sd2);
+    int j;
+    if (seg == 0) {
+      j = lo + t;
+    } else if (seg == NS - 1) {
+      j = lo + g.jb + t;
+    } else {
+      // thread th scans its vector of round seg - 1
+      float w[E::kVec];
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+        if (k == seg - 1) vec_weights<DT, RESID>(d, vget(st2, k, g), vget(sd2, k, g), w);
+      double acc = carry + excl;
+      int pick = -1, lp = 0;
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) {
+        acc += (double)w[e];
+        if (w[e] > 0.f) {
+          lp = e;
+          if (pick < 0 && !fb && tau < acc) pick = e;
+        }
+      }
+      j = lo + g.head + ((seg - 1) * kThreads + t) * E::kVec + (pick >= 0 ? pick : lp);
+    }
+    L.pick = j;
+  }
+  __syncthreads();
+  const int j = L.pick;
+  __syncthreads();
+  return j;
+}
+
+// Step 3 of a live sampled row: every workgroup of the group sums its slice
+// of the drawn distribution and publishes the sum; the workgroup whose slice
+// holds tau = u * Z writes the token.
+template <int DT, int R, bool RESID, bool AL>
+__device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len,
+                     const Decision& dc) {
+  using E = Elt<DT>;
+  const int t = threadIdx.x;
+  unsigned* rc = a.ctr + (int64_t)b * kRowWords;
+  DrawParams d{ref_of(dc.mt, a.k2), 1.f / dc.st, ref_of(dc.md, a.k2), 1.f / dc.sd, a.k2, 1.f};
+  const int n = dc.n;
+  Slice<DT, R> st, sd;
+  const char* tp = row_of<DT>(a, b, g, n) + (int64_t)lo * E::kBytes;
+  const Geom gt = geom_of<DT, AL>(tp, len);
+  load_slice<DT, R, AL>(tp, gt, st);
+  if (RESID) {
+    // the weights pair element j of both rows: the draft slice takes the
+    // target slice's register layout
+    const char* dp = row_of<DT>(a, b, g, g + 1 + n) + (int64_t)lo * E::kBytes;
+    if (AL || geom_of<DT, AL>(dp, len).head == gt.head)
+      load_slice<DT, R, AL>(dp, gt, sd);
+    else
+      load_slice_as<DT, R>(dp, gt, sd);
+  } else {
+    sd = st;
+  }
+  uint64_t* ws = a.wsum + (int64_t)b * 2 * a.NC;
+  double base = 0.0, z = 0.0;
+  bool fallback = false;
+  // attempt 0: the weights of the call; attempt 1 (residual only): p_n, when
+  // rounding left the residual without mass (exact arithmetic never does)
+  auto publish_sum = [&](double acc, int attempt) {
+    block_sum_d(acc, L);
+    if (t == 0) {
+      put64(&ws[attempt * a.NC + c], ~(uint64_t)__double_as_longlong(acc));
+      publish();
+      fetch_add(rc + kArrive, 1u);
+      wait_count(a, rc + kArrive, (unsigned)((2 + attempt) * a.NC));
+    }
+    __syncthreads();
+    return find_owner(ws + attempt * a.NC, a.NC, dc.ustar, L, base, z, fallback);
+  };
+  double v[R + 2];
+  opaque(st), opaque(sd);
+  segment_sums<DT, R, RESID>(d, st, sd, gt, v);
+  double acc = 0.0;
+#pragma unroll
+  for (int s = 0; s < R + 2; ++s) acc += v[s];
+  int owner = publish_sum(acc, 0);
+  bool resid = RESID;
+  if (RESID && !(z > 0.0)) {
+    if (c == 0 && t == 0) atomicOr(&a.hdr[1], kDiagZeroResid);
+    resid = false;
+    d.scale = d.st_inv;
+    opaque(st);
+    segment_sums<DT, R, false>(d, st, st, gt, v);
+    acc = 0.0;
+#pragma unroll
+    for (int s = 0; s < R + 2; ++s) acc += v[s];
+    owner = publish_sum(acc, 1);
+  }
+  if (owner < 0) {  // no weight anywhere (cannot happen for a live row)
+    owner = 0;
+    fallback = true;
+  }
+  if (c != owner) return;
+  opaque(st), opaque(sd);
+  const double tau = fallback ? __builtin_inf() : (double)dc.ustar * z;
+  const int j = resid ? slice_search<DT, R, true>(d, st, sd, gt, lo, base, tau, L)
+                      : slice_search<DT, R, false>(d, st, st, gt, lo, base, tau, L);
   if (t == 0) {
-    publish();
-    const unsigned tk = ticket(counter(a, kDrawTicket, b));
-    L.last = (tk == (unsigned)a.ND - 1);
+    a.out_tok[(int64_t)b * (a.G + 1) + n] = j;
+    if (a.pr_z) a.pr_z[b] = (float)(RESID ? z : z * (double)d.st_inv);
+  }
+}
+
+// ------------------------------------------------------------------ exit
+// Clears a row's published pairs (rows 0..nrows-1 of every slice).
+__device__ void clear_pairs(const Args& a, int b, int nrows) {
+  uint64_t* base = a.part + (int64_t)b * a.NC * a.NR;
+  for (int k = threadIdx.x; k < nrows * a.NC; k += kThreads)
+    put64(&base[(int64_t)(k / nrows) * a.NR + k % nrows], 0);
+}
+
+// Every workgroup of a sampled row takes the row's exit ticket after its last
+// read of the row's entries; the last one clears them and the counters.
+__device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
+  unsigned* rc = a.ctr + (int64_t)b * kRowWords;
+  publish();  // this workgroup's loads and stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned tk = fetch_add(rc + kExit, 1u);
+    after(tk);
+    L.last = tk == (unsigned)a.NC - 1;
   }
   __syncthreads();
   if (!L.last) return;
-  if (work) {
-    final_draw<DT>(a, L, b);
+  clear_pairs(a, b, nrows);
+  uint64_t* ws = a.wsum + (int64_t)b * 2 * a.NC;
+  for (int k = threadIdx.x; k < 2 * a.NC; k += kThreads) put64(&ws[k], 0);
+  if (threadIdx.x == 0) put_u(rc + kArrive, 0u), put_u(rc + kExit, 0u);
+}
+
+// ------------------------------------------------------------------ kernel
+// Four waves per SIMD (four workgroups per CU) is what the sampling kernel's
+// registers allow without spilling.
+#ifndef SPEC_MIN_WAVES
+#define SPEC_MIN_WAVES 4
+#endif
+template <int DT, int MODE, int R, bool AL>
+__global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a) {
+  constexpr bool kSample = MODE == SPEC_MODE_SAMPLE;
+  using E = Elt<DT>;
+  __shared__ Lds L;
+  const int t = threadIdx.x;
+  const int b = (int)(blockIdx.x / (unsigned)a.NC), c = (int)(blockIdx.x % (unsigned)a.NC);
+  const int g = a.gam[b];
+  if (g < 0 || g > a.G) {
+    if (c == 0) write_sentinel(a, b);
+    return;
   }
+  const int nrows = kSample ? 2 * g + 1 : g + 1;
+  const int lo = c * a.CL;
+  const int len = min(a.V - lo, a.CL);
+  unsigned* rc = a.ctr + (int64_t)b * kRowWords;
+
+  Gathered in = gather_small<MODE>(a, b, g);
+  stream_rows<DT, MODE, R, AL>(a, L, b, g, nrows, lo, len);
+  publish_pairs<kSample>(a, L, b, c, nrows);
+  if (kSample) gather_logits<DT>(a, b, g, in);  // in flight during the wait
+
+  if (!kSample) {
+    // greedy: the last workgroup to arrive decides, writes the row and
+    // clears the row's entries
+    if (t == 0) {
+      const unsigned tk = fetch_add(rc + kArrive, 1u);
+      after(tk);
+      L.last = tk == (unsigned)a.NC - 1;
+    }
+    __syncthreads();
+    if (!L.last) return;
+    merge_group<false>(a, L, b, nrows);
+    decide<DT, MODE>(a, L, b, g, in, true);
+    clear_pairs(a, b, nrows);
+    if (t == 0) put_u(rc + kArrive, 0u);
+    return;
+  }
+
+  // sampling: wait for the group, merge, decide (every workgroup alike)
   if (t == 0) {
-    put_u(counter(a, kDrawTicket, b), 0u);
-    put_u(counter(a, kRowFlag, b), 0u);
+    fetch_add(rc + kArrive, 1u);
+    wait_count(a, rc + kArrive, (unsigned)a.NC);
   }
+  __syncthreads();
+  merge_group<true>(a, L, b, nrows);
+  decide<DT, MODE>(a, L, b, g, in, c == 0);
+  const Decision dc = L.dec;
+  if (!dc.dead) {
+    if (dc.resid)
+      draw<DT, R, true, AL>(a, L, b, c, g, lo, len, dc);
+    else
+      draw<DT, R, false, AL>(a, L, b, c, g, lo, len, dc);
+  }
+  row_exit(a, L, b, nrows);
 }
 
 // ------------------------------------------------------------------ probes
@@ -1040,6 +1227,24 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP -
 
 bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
+template <int DT, int MODE, bool AL>
+void launch_r(int R, dim3 grid, hipStream_t s, const Args& a) {
+  if (R == 1)
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 1, AL>), grid, dim3(kThreads), 0, s, a);
+  else if (R == 2)
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 2, AL>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <int DT, int MODE>
+void launch(int R, bool al, dim3 grid, hipStream_t s, const Args& a) {
+  if (al)
+    launch_r<DT, MODE, true>(R, grid, s, a);
+  else
+    launch_r<DT, MODE, false>(R, grid, s, a);
+}
+
 int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const int32_t* gam,
         const int32_t* kv, int B, int G, int V, int dtype, float T, int mode, int32_t* out_tok,
         int32_t* out_n, int32_t* out_len, void* ws, size_t ws_bytes, void* stream, float* px,
@@ -1066,25 +1271,28 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.pr_px = px, a.pr_qx = qx, a.pr_z = pz, a.pr_m = pm, a.pr_s = ps;
   char* w = (char*)ws;
   a.hdr = (unsigned*)w;
-  a.ctr_end = (unsigned*)(((uintptr_t)w + ws_bytes) & ~(uintptr_t)255);
-  a.part = (float2*)(w + p.off_part);
-  a.sub = (double*)(w + p.off_sub);
-  a.B = B, a.G = G, a.V = V, a.NR = p.NR, a.NC = p.NC, a.CH = p.CH, a.ND = p.ND, a.SL = p.SL;
-  a.L = p.L, a.NP = p.NP;
+  a.ctr = (unsigned*)(w + p.off_ctr);
+  a.part = (uint64_t*)(w + p.off_part);
+  a.wsum = (uint64_t*)(w + p.off_wsum);
+  a.B = B, a.G = G, a.V = V, a.NC = p.NC, a.CL = p.CL, a.NR = p.NR;
   a.k2 = sample ? (float)(1.4426950408889634 / (double)T) : 1.f;
-  a.max_spin = 1u << 24;
+  a.max_spin = 1u << 22;  // ~0.2 s of polling: far beyond any legitimate wait
   hipStream_t s = (hipStream_t)stream;
-  dim3 grid((unsigned)p.total), block(kThreads);
+  dim3 grid((unsigned)p.total);
+  // every row 16-byte aligned: both bases aligned and a row a whole number
+  // of 16-byte vectors
+  const bool al = aligned(tgt, 16) && (!sample || G == 0 || aligned(dft, 16)) &&
+                  ((size_t)V * e) % 16 == 0;
   if (dtype == SPEC_DTYPE_BF16) {
     if (sample)
-      hipLaunchKernelGGL((verify_kernel<SPEC_DTYPE_BF16, SPEC_MODE_SAMPLE>), grid, block, 0, s, a);
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_SAMPLE>(p.R, al, grid, s, a);
     else
-      hipLaunchKernelGGL((verify_kernel<SPEC_DTYPE_BF16, SPEC_MODE_GREEDY>), grid, block, 0, s, a);
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_GREEDY>(p.R, al, grid, s, a);
   } else {
     if (sample)
-      hipLaunchKernelGGL((verify_kernel<SPEC_DTYPE_F32, SPEC_MODE_SAMPLE>), grid, block, 0, s, a);
+      launch<SPEC_DTYPE_F32, SPEC_MODE_SAMPLE>(p.R, al, grid, s, a);
     else
-      hipLaunchKernelGGL((verify_kernel<SPEC_DTYPE_F32, SPEC_MODE_GREEDY>), grid, block, 0, s, a);
+      launch<SPEC_DTYPE_F32, SPEC_MODE_GREEDY>(p.R, al, grid, s, a);
   }
   return hip_status(hipGetLastError());
 }
@@ -1143,17 +1351,18 @@ int spec_verify_plan(int B, int gamma_max, int V, int dtype, int mode, int64_t* 
   Plan p;
   int st = make_plan(B, gamma_max, V, dtype, mode, &p);
   if (st != SPEC_OK) return st;
-  out[0] = p.total, out[1] = p.NC, out[2] = p.CH, out[3] = p.ND;
-  out[4] = p.SL, out[5] = p.L, out[6] = p.NR, out[7] = kThreads;
+  out[0] = p.total, out[1] = p.NC, out[2] = p.CL, out[3] = p.R;
+  out[4] = p.NR, out[5] = kThreads, out[6] = (int64_t)p.bytes, out[7] = g_tune.target_workgroups;
   return SPEC_OK;
 }
 
-int spec_verify_tune(int chunk_bytes, int slice_elems, int lag_rows) {
-  if (chunk_bytes < 0 || slice_elems < 0 || lag_rows < 0) return SPEC_ERR_ARG;
+int spec_verify_tune(int vectors, int target_workgroups, int reserved) {
+  if (reserved != 0) return SPEC_ERR_ARG;
+  if (vectors != 0 && vectors != 1 && vectors != 2 && vectors != 4) return SPEC_ERR_ARG;
+  if (target_workgroups < 0) return SPEC_ERR_ARG;
   Tuning t;
-  if (chunk_bytes) t.chunk_bytes = chunk_bytes;
-  if (slice_elems) t.slice_elems = slice_elems;
-  t.lag_rows = lag_rows;
+  t.vectors = vectors;
+  if (target_workgroups) t.target_workgroups = target_workgroups;
   g_tune = t;
   return SPEC_OK;
 }
@@ -1171,7 +1380,7 @@ const char* spec_verify_strerror(int status) {
     case SPEC_OK: return "ok";
     case SPEC_ERR_NULL: return "a required pointer is NULL";
     case SPEC_ERR_SHAPE: return "invalid shape (B, V or gamma_max out of range)";
-    case SPEC_ERR_ARG: return "invalid argument (mode, dtype or temperature)";
+    case SPEC_ERR_ARG: return "invalid argument (mode, dtype, temperature or tuning)";
     case SPEC_ERR_WORKSPACE: return "workspace missing or too small";
     case SPEC_ERR_ALIGN: return "misaligned pointer";
     default: break;
@@ -1180,7 +1389,7 @@ const char* spec_verify_strerror(int status) {
   return "unknown status";
 }
 
-int spec_verify_version(void) { return 100; }
+int spec_verify_version(void) { return 300; }
 
 int spec_probe_read_blocks(size_t bytes) {
   return (int)((bytes + kProbeBytesPerBlock - 1) / kProbeBytesPerBlock);

@@ -57,7 +57,8 @@ def _call(lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), sv.ERR_SHAPE), (dict(B=-3), sv.ERR_SHAPE), (dict(V=0), sv.ERR_SHAPE),
-    (dict(V=(1 << 30) + 1), sv.ERR_SHAPE), (dict(G=-1), sv.ERR_SHAPE), (dict(G=64), sv.ERR_SHAPE),
+    (dict(V=(1 << 30) + 1), sv.ERR_SHAPE), (dict(V=(1 << 20) + 1), sv.ERR_SHAPE),
+    (dict(G=-1), sv.ERR_SHAPE), (dict(G=64), sv.ERR_SHAPE),
     (dict(dtype=2), sv.ERR_ARG), (dict(mode=7), sv.ERR_ARG),
     (dict(tgt=None), sv.ERR_NULL), (dict(gam=None), sv.ERR_NULL), (dict(out_tok=None), sv.ERR_NULL),
     (dict(out_n=None), sv.ERR_NULL), (dict(out_len=None), sv.ERR_NULL), (dict(tok=None), sv.ERR_NULL),
@@ -91,30 +92,45 @@ def test_probe_pointer_pairing(lib):
 def test_workspace_bytes_and_plan(lib):
     assert sv.workspace_bytes(0, 4, 100, sv.BF16, sv.SAMPLE) == 0
     assert sv.workspace_bytes(4, 64, 100, sv.BF16, sv.SAMPLE) == 0
+    assert sv.workspace_bytes(4, 4, (1 << 20) + 1, sv.BF16, sv.SAMPLE) == 0
     small = sv.workspace_bytes(64, 4, 128256, sv.BF16, sv.SAMPLE)
     big = sv.workspace_bytes(256, 8, 151936, sv.BF16, sv.SAMPLE)
     assert 0 < small < big < 64 << 20
     assert sv.workspace_bytes(64, 4, 128256, sv.BF16, sv.GREEDY) < small
     p = sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)
-    assert p["vocab_rows"] == 9 and p["threads"] == 256
-    assert p["chunks"] * p["chunk_len"] >= 128256 > (p["chunks"] - 1) * p["chunk_len"]
-    assert p["chunk_len"] % 8 == 0
+    assert p["vocab_rows"] == 9 and p["threads"] == 256 and p["workspace_bytes"] == small
+    # slices cover the row, are whole 16-byte vectors, and fit the per-thread registers
     assert p["slices"] * p["slice_len"] >= 128256 > (p["slices"] - 1) * p["slice_len"]
-    assert p["workgroups"] == 64 * (p["vocab_rows"] * p["chunks"] + p["slices"])
+    assert p["slice_len"] % 8 == 0 and p["slice_len"] <= p["vectors"] * 256 * 8
+    assert p["workgroups"] == 64 * p["slices"]
+    # the benchmark workload: 16 slices of 4 vectors, one workgroup per CU slot
+    assert p["vectors"] == 4 and p["slices"] == 16
     g = sv.plan(64, 4, 128256, sv.BF16, sv.GREEDY)
-    assert g["slices"] == 0 and g["vocab_rows"] == 5
+    assert g["vocab_rows"] == 5 and g["workgroups"] == 64 * g["slices"]
     f = sv.plan(1, 4, 50257, sv.F32, sv.SAMPLE)
-    assert f["chunk_len"] % 4 == 0
+    assert f["slice_len"] % 4 == 0 and f["vectors"] == 1
+    # at most one slice per thread of the draw's slice scan, up to the largest vocabulary
+    for mode in (sv.SAMPLE, sv.GREEDY):
+        for dt in (sv.F32, sv.BF16):
+            for B in (1, 64, 4096):
+                q = sv.plan(B, 63, 1 << 20, dt, mode)
+                assert q["slices"] <= 256 and q["slices"] * q["slice_len"] >= 1 << 20
 
 
 def test_tune_changes_plan_and_restores(lib):
     base = sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)
     try:
-        sv.tune(chunk_bytes=262144, slice_elems=4096, lag_rows=3)
+        sv.tune(vectors=1)
         p = sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)
-        assert p["chunks"] < base["chunks"] and p["slice_len"] == 4096 and p["lag_rows"] == 3
-        with pytest.raises(sv.SpecVerifyError):
-            sv.tune(chunk_bytes=-1)
+        assert p["vectors"] == 1 and p["slices"] == 63
+        sv.tune(vectors=2)
+        assert sv.plan(64, 4, 128256, sv.BF16, sv.GREEDY)["vectors"] == 2
+        sv.tune(target_workgroups=4096)
+        assert sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE)["vectors"] == 1
+        for bad in (dict(vectors=3), dict(vectors=8), dict(vectors=-1), dict(target_workgroups=-5)):
+            with pytest.raises(sv.SpecVerifyError):
+                sv.tune(**bad)
+        assert lib.spec_verify_tune(0, 0, 1) == sv.ERR_ARG
     finally:
         sv.tune()
     assert sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE) == base

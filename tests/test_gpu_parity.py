@@ -198,14 +198,15 @@ def test_repeat_is_bit_identical(torch):
 
 
 def test_tuning_invariance(torch):
-    """Greedy is bit-identical for any chunk, slice and lag; sampling stays
-    within the parity bar for each of them."""
+    """Greedy is bit-identical for any slice size; sampling stays within the
+    parity bar for each of them."""
     cg = inputs.make_case(3, rnd=1, mode="greedy", B=16, V=40000)
     cs = inputs.make_case(3, rnd=1, B=16, V=40000)
     ref = run(cg, torch, probe=False)
     try:
-        for chunk, sl, lag in ((4096, 1024, 1), (16384, 4096, 2), (131072, 8192, 0), (2048, 512, 5)):
-            sv.tune(chunk, sl, lag)
+        for vectors in (1, 2, 4):
+            sv.tune(vectors)
+            print(f"tune vectors={vectors}", flush=True)
             got = run(cg, torch, probe=False)
             for x, y in zip(ref[:3], got[:3]):
                 np.testing.assert_array_equal(x, y)
@@ -219,17 +220,16 @@ def test_workspace_reuse_and_diagnostics(torch):
     nbytes = sv.workspace_bytes(16, big.G, 30000, sv.BF16, sv.SAMPLE)
     ws = sv.Workspace(nbytes)
     for cfg, kw in ((4, dict(B=16, V=30000)), (3, dict(B=5, V=1000)), (2, dict(B=16, V=30000)),
-                    (3, dict(B=3, V=20000, mode="greedy"))):
+                    (3, dict(B=3, V=20000, mode="greedy")), (1, dict(B=10, V=3000))):
         case = inputs.make_case(cfg, rnd=9, **kw)
         assert sv.workspace_bytes(case.B, case.G, case.V, 1 if case.target.dtype == np.uint16 else 0,
                                   sv.GREEDY if case.mode == "greedy" else sv.SAMPLE) <= nbytes
         _check(case, torch, workspace=ws)
+        # every call clears what it wrote (the diagnostic word aside)
+        body = ws.tensor[ws.offset: ws.offset + nbytes].cpu().numpy().copy()
+        body[4:8] = 0
+        assert not body.any(), f"cfg {cfg}: workspace not cleared"
     assert ws.diagnostics() == 0
-    # the counters (one block per row at the workspace's end) are back to zero
-    body = ws.tensor[ws.offset: ws.offset + nbytes].cpu().numpy()
-    assert not body[:256].any()
-    end = nbytes - (nbytes + ws.ptr) % 256 if (nbytes + ws.ptr) % 256 else nbytes
-    assert not body[end - 768 * 16: end].any()
 
 
 @pytest.mark.parametrize("mode", ["sample", "greedy"])
