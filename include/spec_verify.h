@@ -67,7 +67,7 @@ enum spec_status {
  * function of its arguments and of the tuning override).  Returns 0 for
  * sizes spec_verify would reject.
  *
- * The workspace holds two counters per batch row, the softmax statistics of
+ * The workspace holds one counter per batch row, the softmax statistics of
  * every vocabulary slice and the draw sums of every slice.  It must be
  * zero-filled once before its first use (spec_verify_workspace_reset, or any
  * zero fill).  Every call that completes clears everything it wrote, leaving

@@ -53,10 +53,10 @@ constexpr int kStage = 1024;          // LDS entries for staging a group's pairs
 constexpr int kMaxVocab = 1 << 20;
 constexpr int kDefaultTargetWorkgroups = 1024;
 constexpr unsigned kDiagSpin = 1u, kDiagZeroResid = 2u;
-// Per-row counters (arrivals, exits), each on its own 128-byte line.
+// Per-row exit counter, on its own 128-byte line.
 constexpr int kLine = 32;
-enum { kArrive = 0, kExit = kLine };
-constexpr int kRowWords = 2 * kLine;
+enum { kExit = 0 };
+constexpr int kRowWords = kLine;
 #define NEG_INF (-__builtin_inff())
 
 struct Tuning {
@@ -441,24 +441,25 @@ __device__ __forceinline__ unsigned fetch_add(unsigned* p, unsigned v) {
 __device__ __forceinline__ void put_u(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned get_u(const unsigned* p) {
-  return __hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Orders what follows after an atomic whose result `v` is: the result has
 // returned, so the atomic has been performed, before any later access issues.
 __device__ __forceinline__ void after(unsigned v) { asm volatile("" ::"v"(v) : "memory"); }
 
-// Thread 0 polls a counter until it reaches `target`; gives up after
-// max_spin polls and flags the diagnostic word.
-__device__ void wait_count(const Args& a, const unsigned* w, unsigned target) {
-  unsigned n = 0;
-  while (get_u(w) < target) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++n > a.max_spin) {
+// Waits (in the calling thread) for a published word: every published word
+// is non-zero and a completed call leaves the workspace zero, so the load
+// that returns non-zero returns the data.  Gives up after max_spin polls
+// and flags the diagnostic word.
+__device__ uint64_t poll64(const Args& a, const uint64_t* p) {
+  uint64_t v = get64(p);
+  for (unsigned n = 0; v == 0; ++n) {
+    if (n > a.max_spin) {
       atomicOr(&a.hdr[1], kDiagSpin);
-      return;
+      break;
     }
+    __builtin_amdgcn_s_sleep(4);
+    v = get64(p);
   }
+  return v;
 }
 
 // ------------------------------------------------------------------ LDS
@@ -688,7 +689,8 @@ __device__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int 
 
 // Publishes this slice's pairs (entry r of the slice's record).  No written
 // word is zero: S >= 1 whenever m is finite, m = -inf has non-zero bits, and
-// the argmax is stored plus one.
+// the argmax is stored plus one.  Nothing waits for the stores: readers poll
+// the words themselves.
 template <bool kSample>
 __device__ void publish_pairs(const Args& a, Lds& L, int b, int c, int nrows) {
   uint64_t* rec = a.part + ((int64_t)b * a.NC + c) * a.NR;
@@ -696,14 +698,12 @@ __device__ void publish_pairs(const Args& a, Lds& L, int b, int c, int nrows) {
     const float s = kSample ? L.S[r] : __int_as_float(__float_as_int(L.S[r]) + 1);
     put64(&rec[r], pack2(L.M[r], s));
   }
-  publish();
-  __syncthreads();
 }
 
-// Merges the group's published pairs into L.M / L.S, in the same fixed order
-// in every workgroup: per row, lane l takes slices l, l + 64, ... in turn,
-// then a butterfly across the wave.  Rows go to waves round-robin, staged
-// through LDS in batches.
+// Waits for the group's published pairs and merges them into L.M / L.S, in
+// the same fixed order in every workgroup: per row, lane l takes slices l,
+// l + 64, ... in turn, then a reduction across the wave.  Rows go to waves
+// round-robin, staged through LDS in batches.
 template <bool kSample>
 __device__ void merge_group(const Args& a, Lds& L, int b, int nrows) {
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
@@ -715,7 +715,7 @@ __device__ void merge_group(const Args& a, Lds& L, int b, int nrows) {
     const int cnt = (r1 - r0) * nc;
     for (int k = t; k < cnt; k += kThreads) {
       const int r = r0 + k / nc, c = k % nc;
-      L.stage[k] = get64(&base[(int64_t)c * a.NR + r]);
+      L.stage[k] = poll64(a, &base[(int64_t)c * a.NR + r]);
     }
     __syncthreads();
     for (int r = r0 + w; r < r1; r += kWaves) {
@@ -914,10 +914,10 @@ __device__ __forceinline__ void segment_sums(const DrawParams& d, const Slice<DT
 // (base); z_out = Z.  When rounding leaves no slice whose running sum exceeds
 // tau, returns the last slice with positive weight and sets fallback; -1 if
 // no slice has weight.
-__device__ int find_owner(const uint64_t* ws, int nc, float u, Lds& L, double& base,
-                          double& z_out, bool& fallback) {
+__device__ int find_owner(const Args& a, const uint64_t* ws, int nc, float u, Lds& L,
+                          double& base, double& z_out, bool& fallback) {
   const int t = threadIdx.x;
-  const double v = t < nc ? __longlong_as_double((long long)~get64(&ws[t])) : 0.0;
+  const double v = t < nc ? __longlong_as_double((long long)~poll64(a, &ws[t])) : 0.0;
   double incl, excl, z;
   block_scan_d(v, L, incl, excl, z);
   z_out = z;
@@ -1026,7 +1026,6 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
                      const Decision& dc) {
   using E = Elt<DT>;
   const int t = threadIdx.x;
-  unsigned* rc = a.ctr + (int64_t)b * kRowWords;
   DrawParams d{ref_of(dc.mt, a.k2), 1.f / dc.st, ref_of(dc.md, a.k2), 1.f / dc.sd, a.k2, 1.f};
   const int n = dc.n;
   Slice<DT, R> st, sd;
@@ -1049,16 +1048,12 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
   bool fallback = false;
   // attempt 0: the weights of the call; attempt 1 (residual only): p_n, when
   // rounding left the residual without mass (exact arithmetic never does)
+  // a slice sum is stored as the complement of its bits: never zero (the sum
+  // is non-negative, so its sign bit is clear)
   auto publish_sum = [&](double acc, int attempt) {
     block_sum_d(acc, L);
-    if (t == 0) {
-      put64(&ws[attempt * a.NC + c], ~(uint64_t)__double_as_longlong(acc));
-      publish();
-      fetch_add(rc + kArrive, 1u);
-      wait_count(a, rc + kArrive, (unsigned)((2 + attempt) * a.NC));
-    }
-    __syncthreads();
-    return find_owner(ws + attempt * a.NC, a.NC, dc.ustar, L, base, z, fallback);
+    if (t == 0) put64(&ws[attempt * a.NC + c], ~(uint64_t)__double_as_longlong(acc));
+    return find_owner(a, ws + attempt * a.NC, a.NC, dc.ustar, L, base, z, fallback);
   };
   double v[R + 2];
   opaque(st), opaque(sd);
@@ -1103,10 +1098,12 @@ __device__ void clear_pairs(const Args& a, int b, int nrows) {
 }
 
 // Every workgroup of a sampled row takes the row's exit ticket after its last
-// read of the row's entries; the last one clears them and the counters.
+// read of the row's entries (those loads have returned: their values were
+// used); the last one clears the entries and the counter.  Every entry was
+// seen by every workgroup before any of them got here, so no store of the
+// call can land after the clearing.
 __device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
   unsigned* rc = a.ctr + (int64_t)b * kRowWords;
-  publish();  // this workgroup's loads and stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned tk = fetch_add(rc + kExit, 1u);
@@ -1118,7 +1115,7 @@ __device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
   clear_pairs(a, b, nrows);
   uint64_t* ws = a.wsum + (int64_t)b * 2 * a.NC;
   for (int k = threadIdx.x; k < 2 * a.NC; k += kThreads) put64(&ws[k], 0);
-  if (threadIdx.x == 0) put_u(rc + kArrive, 0u), put_u(rc + kExit, 0u);
+  if (threadIdx.x == 0) put_u(rc + kExit, 0u);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -1142,7 +1139,6 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   const int nrows = kSample ? 2 * g + 1 : g + 1;
   const int lo = c * a.CL;
   const int len = min(a.V - lo, a.CL);
-  unsigned* rc = a.ctr + (int64_t)b * kRowWords;
 
   Gathered in = gather_small<MODE>(a, b, g);
   stream_rows<DT, MODE, R, AL>(a, L, b, g, nrows, lo, len);
@@ -1150,28 +1146,17 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   if (kSample) gather_logits<DT>(a, b, g, in);  // in flight during the wait
 
   if (!kSample) {
-    // greedy: the last workgroup to arrive decides, writes the row and
-    // clears the row's entries
-    if (t == 0) {
-      const unsigned tk = fetch_add(rc + kArrive, 1u);
-      after(tk);
-      L.last = tk == (unsigned)a.NC - 1;
-    }
-    __syncthreads();
-    if (!L.last) return;
+    // greedy: slice 0 waits for the group's pairs, decides, writes the row
+    // and clears the pairs (it is their only reader); the other slices are
+    // done
+    if (c != 0) return;
     merge_group<false>(a, L, b, nrows);
     decide<DT, MODE>(a, L, b, g, in, true);
     clear_pairs(a, b, nrows);
-    if (t == 0) put_u(rc + kArrive, 0u);
     return;
   }
 
   // sampling: wait for the group, merge, decide (every workgroup alike)
-  if (t == 0) {
-    fetch_add(rc + kArrive, 1u);
-    wait_count(a, rc + kArrive, (unsigned)a.NC);
-  }
-  __syncthreads();
   merge_group<true>(a, L, b, nrows);
   decide<DT, MODE>(a, L, b, g, in, c == 0);
   const Decision dc = L.dec;
