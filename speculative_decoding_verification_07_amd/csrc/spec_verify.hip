@@ -456,7 +456,7 @@ __device__ uint64_t poll64(const Args& a, const uint64_t* p) {
       atomicOr(&a.hdr[1], kDiagSpin);
       break;
     }
-    __builtin_amdgcn_s_sleep(4);
+    __builtin_amdgcn_s_sleep(1);
     v = get64(p);
   }
   return v;
@@ -1021,8 +1021,10 @@ __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const S
 // Step 3 of a live sampled row: every workgroup of the group sums its slice
 // of the drawn distribution and publishes the sum; the workgroup whose slice
 // holds tau = u * Z writes the token.
+__device__ void row_exit(const Args& a, Lds& L, int b, int nrows);
+
 template <int DT, int R, bool RESID, bool AL>
-__device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len,
+__device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
                      const Decision& dc) {
   using E = Elt<DT>;
   const int t = threadIdx.x;
@@ -1078,6 +1080,10 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
     owner = 0;
     fallback = true;
   }
+  // every read of the row's workspace entries is done: leave the row now, so
+  // that the exit ticket and the clearing overlap the owner's search (which
+  // uses only its registers)
+  row_exit(a, L, b, nrows);
   if (c != owner) return;
   opaque(st), opaque(sd);
   const double tau = fallback ? __builtin_inf() : (double)dc.ustar * z;
@@ -1162,11 +1168,12 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   const Decision dc = L.dec;
   if (!dc.dead) {
     if (dc.resid)
-      draw<DT, R, true, AL>(a, L, b, c, g, lo, len, dc);
+      draw<DT, R, true, AL>(a, L, b, c, g, lo, len, nrows, dc);
     else
-      draw<DT, R, false, AL>(a, L, b, c, g, lo, len, dc);
+      draw<DT, R, false, AL>(a, L, b, c, g, lo, len, nrows, dc);
+  } else {
+    row_exit(a, L, b, nrows);
   }
-  row_exit(a, L, b, nrows);
 }
 
 // ------------------------------------------------------------------ probes
