@@ -22,7 +22,7 @@ _SRC = os.path.join(_HERE, "spec_oracle.c")
 _LIB = os.path.join(_HERE, "libspec_oracle.so")
 
 F32, BF16 = 0, 1
-SAMPLE, GREEDY = 0, 1
+SAMPLE, GREEDY, POINT = 0, 1, 2
 FAULT_NONE, FAULT_NO_CLAMP, FAULT_UNSCALED_TAU, FAULT_RESAMPLE_P, FAULT_GREEDY_RULE = range(5)
 
 _lib = None
@@ -50,7 +50,7 @@ def _load():
                                       i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_verify.restype = i32
         lib.oracle_draw_cdf.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, ctypes.c_double,
-                                        i32, P]
+                                        i32, i32, P]
         lib.oracle_draw_cdf.restype = i32
         _lib = lib
     return _lib
@@ -91,7 +91,8 @@ def verify(target, draft, tokens, uniforms, gamma, kv_len=None, *, temperature=1
     """Run the oracle over a batch.
 
     target: [B, G+1, V] float32 or uint16 (bf16 bits); draft: [B, G, V] same
-    dtype (may be None in greedy mode); tokens: int32 [B, G]; uniforms:
+    dtype (may be None in greedy and point mode, which ignore it); tokens:
+    int32 [B, G]; uniforms:
     float32 [B, G+1] (may be None in greedy mode); gamma: int32 [B];
     kv_len: int32 [B] or None.  threads=0 uses the OpenMP default.
     """
@@ -100,6 +101,8 @@ def verify(target, draft, tokens, uniforms, gamma, kv_len=None, *, temperature=1
     B, G1, V = target.shape
     G = G1 - 1
     dt = _dtype_code(target)
+    if mode == POINT:
+        draft = None
     if draft is not None:
         draft = np.ascontiguousarray(draft, dtype=target.dtype)
         if draft.shape != (B, G, V):
@@ -130,19 +133,19 @@ def verify(target, draft, tokens, uniforms, gamma, kv_len=None, *, temperature=1
     return OracleResult(out_tokens, out_n, out_len, px, qx, z, m, s, pos, zr)
 
 
-def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0):
+def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0, mode=SAMPLE):
     """Normalised CDF (C_j / Z, float64 [V]) of the distribution the oracle
     drew row `row`'s last token from, and the position it was drawn at."""
     lib = _load()
     target = np.ascontiguousarray(target)
     B, G1, V = target.shape
     G = G1 - 1
-    draft = np.ascontiguousarray(draft, dtype=target.dtype)
+    draft = None if mode == POINT else np.ascontiguousarray(draft, dtype=target.dtype)
     tokens = _c(tokens, np.int32).reshape(B, G)
     uniforms = _c(uniforms, np.float32).reshape(B, G + 1)
     gamma = _c(gamma, np.int32).reshape(B)
     cdf = np.empty(V, np.float64)
     pos = lib.oracle_draw_cdf(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens),
                               _ptr(uniforms), _ptr(gamma), None, B, G, V, float(temperature),
-                              int(row), _ptr(cdf))
+                              int(mode), int(row), _ptr(cdf))
     return cdf, int(pos)

@@ -34,6 +34,13 @@
  *      and its code block).
  *   5. KV rollback: the new cache length is kv_len_in + n (mhtirogla step 5,
  *      "truncate the length").
+ *   6. Point-mass drafts (mode OR_POINT): the drafter proposes x_i outright
+ *      -- an n-gram / prompt-lookup match (mhtirogla "Variants" and
+ *      "Implementation notes"; tusharamrit "Self-speculation") or a greedy
+ *      draft (tokentrails code block) -- so q_i is the indicator of x_i and
+ *      no draft logits exist.  Steps 2-3 apply unchanged with that q_i: the
+ *      test becomes u_i * 1 < p_i(x_i), and the residual max(0, p_n - q_n)
+ *      is p_n with x_n removed.
  *
  * Readings where the pages are silent (each one is listed with its reason in
  * the design notes of the repository):
@@ -65,6 +72,7 @@
 #define OR_BF16 1
 #define OR_SAMPLE 0
 #define OR_GREEDY 1
+#define OR_POINT 2
 
 /* Mutations used only by negative-control tests, to show that the
  * statistical tests can detect the classic mistakes named on the pages
@@ -227,8 +235,8 @@ static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t*
     return;
   }
 
-  /* Sampling.  Diagnostics first: (max, exp-sum) of every row t_0..t_g,
-   * d_0..d_{g-1}; they play no part in the decisions. */
+  /* Sampling (and point-mass drafts).  Diagnostics first: (max, exp-sum) of
+   * every row t_0..t_g, d_0..d_{g-1}; they play no part in the decisions. */
   double* P = (double*)malloc(sizeof(double) * (size_t)(g + 1) * V);
   double* Q = (double*)malloc(sizeof(double) * (size_t)(g > 0 ? g : 1) * V);
   double* w = (double*)malloc(sizeof(double) * (size_t)V);
@@ -241,6 +249,13 @@ static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t*
     if (d->s) d->s[i] = s;
   }
   for (int i = 0; i < g; ++i) {
+    if (c->mode == OR_POINT) {
+      /* q_i = indicator of x_i (an out-of-range x_i is caught by the walk) */
+      double* q = Q + (size_t)i * V;
+      for (int j = 0; j < V; ++j) q[j] = (j == x[i]) ? 1.0 : 0.0;
+      live_q[i] = 1;
+      continue;
+    }
     double m, s;
     live_q[i] = softmax_row(c, c->draft, row_off(c, b, G, i), Q + (size_t)i * V, &m, &s);
     if (d->m) d->m[G + 1 + i] = m;
@@ -327,8 +342,9 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
   if (!target || !tokens || !gamma || !out_tokens || !out_n || !out_len) return -1;
   if (B < 0 || G < 0 || V <= 0) return -2;
   if (dtype != OR_F32 && dtype != OR_BF16) return -3;
-  if (mode != OR_SAMPLE && mode != OR_GREEDY) return -3;
-  if (mode == OR_SAMPLE && (!draft || !uniforms || !(T > 0.0) || !isfinite(T))) return -3;
+  if (mode != OR_SAMPLE && mode != OR_GREEDY && mode != OR_POINT) return -3;
+  if (mode == OR_SAMPLE && !draft) return -3;
+  if (mode != OR_GREEDY && (!uniforms || !(T > 0.0) || !isfinite(T))) return -3;
   oracle_ctx c = {target, draft, dtype, tokens, uniforms, gamma, kv_len, B, G, V, T, mode, fault};
   const size_t nr = (size_t)(2 * G + 1);
   if (out_px)
@@ -366,10 +382,12 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
  * data error). */
 int oracle_draw_cdf(const void* target, const void* draft, int dtype, const int32_t* tokens,
                     const float* uniforms, const int32_t* gamma, const int32_t* kv_len, int B,
-                    int G, int V, double T, int b, double* cdf) {
-  if (!target || !draft || !tokens || !uniforms || !gamma || !cdf) return -1;
+                    int G, int V, double T, int mode, int b, double* cdf) {
+  if (!target || !tokens || !uniforms || !gamma || !cdf) return -1;
+  if (mode != OR_SAMPLE && mode != OR_POINT) return -1;
+  if (mode == OR_SAMPLE && !draft) return -1;
   if (b < 0 || b >= B) return -1;
-  oracle_ctx c = {target, draft, dtype, tokens, uniforms, gamma, kv_len, B, G, V, T, OR_SAMPLE,
+  oracle_ctx c = {target, draft, dtype, tokens, uniforms, gamma, kv_len, B, G, V, T, mode,
                   OR_FAULT_NONE};
   int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)B * (G + 1));
   int32_t* nn = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);

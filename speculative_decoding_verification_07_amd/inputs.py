@@ -5,7 +5,10 @@ KV lengths.  It holds none of the verify step's arithmetic: it is the only
 module that both the GPU path's tests/benchmark and the CPU oracle's tests
 use.  The draft tokens are drawn the way a draft model would draw them (the
 draft step, upstream of verification): by the Gumbel-max trick from
-softmax(draft_logits / T) in sampling mode, by argmax in greedy mode.
+softmax(draft_logits / T) in sampling mode, by argmax in greedy mode and in
+point mode.  Point mode stands for a drafter that proposes tokens outright (a
+greedy draft model, an n-gram match): its draft logits only serve to pick
+those tokens and are not passed to verification.
 
 Workloads (vocabulary sizes of the models the pages discuss: GPT-2's 50257,
 a LLaMA-2-class 32000, Llama 3's 128256, Qwen's 151936; draft lengths in the
@@ -64,7 +67,7 @@ CONFIGS = {
 @dataclass
 class Case:
     config: Config
-    mode: str                 # "sample" or "greedy"
+    mode: str                 # "sample", "greedy" or "point"
     target: np.ndarray        # [B, G+1, V] float32, or uint16 holding bf16 bits
     draft: np.ndarray         # [B, G, V] same dtype
     tokens: np.ndarray        # int32 [B, G]
@@ -216,7 +219,7 @@ def make_case(cfg: int | Config, rnd: int = 0, mode: str = "sample", **overrides
     else:
         target, draft, extra = _gaussian_logits(c, rnd)
     gamma = _gamma(c, rnd)
-    if mode == "greedy":
+    if mode in ("greedy", "point"):
         tokens = argmax_tokens(draft, gamma)
     elif "q_cdf" in extra:
         tokens = _tokens_from_cdf(extra["q_cdf"], gamma, rng(c.cfg, rnd, 3))
@@ -243,7 +246,7 @@ def redraw_round(case: Case, rnd: int) -> Case:
     uniforms: one more verify round over fixed distributions."""
     c = case.config
     gamma = _gamma(c, rnd)
-    if case.mode == "greedy":
+    if case.mode in ("greedy", "point"):
         tokens = argmax_tokens(case.draft, gamma)
     elif "q_cdf" in case.extra:
         tokens = _tokens_from_cdf(case.extra["q_cdf"], gamma, rng(c.cfg, rnd, 3))
@@ -261,9 +264,9 @@ def fresh_uniforms(case: Case, rnd: int) -> Case:
 
 def algorithmic_bytes(case: Case) -> int:
     """Compulsory logit bytes one verify call must read: (2 g_b + 1) V e per
-    row when sampling, (g_b + 1) V e when greedy."""
+    row when sampling, (g_b + 1) V e when greedy or with point-mass drafts."""
     e = case.target.itemsize
     g = case.gamma.astype(np.int64)
     g = np.clip(g, 0, case.G)
-    rows = (g + 1) if case.mode == "greedy" else (2 * g + 1)
+    rows = (g + 1) if case.mode in ("greedy", "point") else (2 * g + 1)
     return int(rows.sum()) * case.V * e

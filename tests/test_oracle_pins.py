@@ -289,6 +289,85 @@ def test_data_errors_write_sentinel():
     assert list(rg.tokens[:, 0]) == [0, 0]
 
 
+# ---------------------------------------------------------------- point-mass drafts
+@pytest.mark.parametrize("cfg,dtype,G", [(1, "f32", 2), (3, "bf16", 4), (5, "f32", 8)])
+def test_point_mode_is_the_textbook_rule(cfg, dtype, G):
+    """q_i = indicator of x_i: accept while u_i < p_i(x_i); at the first
+    rejection draw from p_n with x_n removed (library softmax, numpy inverse
+    CDF); otherwise the bonus from p_g; Z = 1 - p_n(x_n)."""
+    case = inputs.make_case(cfg, rnd=11, mode="point", B=96, G=G, V=700, dtype=dtype)
+    r = oracle.verify(case.target, None, case.tokens, case.uniforms, case.gamma, case.kv_len,
+                      temperature=case.T, mode=oracle.POINT)
+    P = _probs(case.target, case.T)
+    seen = set()
+    for b in range(case.B):
+        g, x, u = int(case.gamma[b]), case.tokens[b], case.uniforms[b]
+        n = g
+        for i in range(g):
+            assert r.px[b, i] == pytest.approx(P[b, i, x[i]], rel=1e-12, abs=1e-300)
+            assert r.qx[b, i] == 1.0
+            if not np.float64(u[i]) < P[b, i, x[i]]:
+                n = i
+                break
+        assert r.n_accepted[b] == n
+        if n < g:
+            w = P[b, n].copy()
+            w[x[n]] = 0.0
+            want = _inverse_cdf(w, u[n + 1])
+            assert r.z[b] == pytest.approx(1.0 - P[b, n, x[n]], rel=1e-12)
+            assert r.tokens[b, n] != x[n]
+        else:
+            want = _inverse_cdf(P[b, g], u[g])
+        assert r.tokens[b, n] == want
+        np.testing.assert_array_equal(r.tokens[b, :n], x[:n])
+        assert np.all(r.tokens[b, n + 1:] == -1)
+        assert r.new_len[b] == case.kv_len[b] + n
+        seen.add("reject" if n < g else "full")
+    assert seen == {"reject", "full"}
+
+
+def test_point_mode_equals_sampling_with_one_hot_draft():
+    """A draft row whose logits are -inf except at x_i has q_i = indicator of
+    x_i exactly, so the general rule must give the same result bit for bit."""
+    case = inputs.make_case(2, rnd=12, mode="point", B=40, V=900)
+    one_hot = np.full(case.draft.shape, 0xFF80, np.uint16)   # bf16 -inf
+    for b in range(case.B):
+        for i in range(int(case.gamma[b])):
+            one_hot[b, i, case.tokens[b, i]] = 0x3F80             # bf16 1.0
+    pt = oracle.verify(case.target, None, case.tokens, case.uniforms, case.gamma, case.kv_len,
+                       temperature=case.T, mode=oracle.POINT)
+    gen = oracle.verify(case.target, one_hot, case.tokens, case.uniforms, case.gamma,
+                        case.kv_len, temperature=case.T)
+    np.testing.assert_array_equal(pt.tokens, gen.tokens)
+    np.testing.assert_array_equal(pt.n_accepted, gen.n_accepted)
+    np.testing.assert_array_equal(pt.z, gen.z)
+    np.testing.assert_array_equal(pt.px, gen.px)
+    assert np.all(pt.n_accepted < case.gamma) and np.any(pt.n_accepted > 0)
+
+
+def test_point_mode_data_errors_and_gamma0():
+    case = inputs.make_case(1, rnd=13, mode="point", B=5, V=300)
+    x = case.tokens.copy()
+    x[0, 0] = -1                                # tested token out of range
+    t = case.target.copy()
+    t[1, 0, :] = -np.inf                        # p_0 has no finite logit
+    g = case.gamma.copy()
+    g[2] = case.G + 1
+    r = oracle.verify(t, None, x, case.uniforms, g, case.kv_len, temperature=case.T,
+                      mode=oracle.POINT)
+    for b in range(3):
+        assert r.n_accepted[b] == -1 and np.all(r.tokens[b] == -1)
+        assert r.new_len[b] == case.kv_len[b]
+    assert np.all(r.n_accepted[3:] >= 0)
+    # gamma = 0 is plain inverse-CDF sampling from p_0, as in sampling mode
+    z = np.zeros(case.B, np.int32)
+    r0 = oracle.verify(case.target, None, case.tokens, case.uniforms, z, temperature=case.T,
+                       mode=oracle.POINT)
+    P = _probs(case.target[:, 0], case.T)
+    assert list(r0.tokens[:, 0]) == [_inverse_cdf(P[b], case.uniforms[b, 0])
+                                     for b in range(case.B)]
+
+
 # ---------------------------------------------------------------- closed forms
 def _rounds_to(value, printed, digits):
     return round(value, digits) == pytest.approx(printed, abs=1e-9)

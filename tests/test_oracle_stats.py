@@ -138,6 +138,65 @@ def test_expected_tokens_per_pass_on_fixed_overlap():
     assert checked >= 12
 
 
+# ---------------------------------------------------------------- point-mass drafts
+def _run_point(lt, x, rows, fault=oracle.FAULT_NONE, seed=31, chunk=200_000):
+    """`rows` rounds over fixed p with the same proposed tokens x every round."""
+    G1, V = lt.shape
+    G = G1 - 1
+    rng = np.random.default_rng(seed)
+    toks, ns = [], []
+    done = 0
+    while done < rows:
+        B = min(chunk, rows - done)
+        u = rng.random((B, G + 1)).astype(np.float32)
+        t = np.broadcast_to(lt, (B, G + 1, V))
+        xs = np.broadcast_to(np.asarray(x, np.int32), (B, G))
+        r = oracle.verify(t, None, xs, u, np.full(B, G, np.int32), temperature=1.0,
+                          mode=oracle.POINT, fault=fault)
+        toks.append(r.tokens)
+        ns.append(r.n_accepted)
+        done += B
+    return np.concatenate(toks), np.concatenate(ns)
+
+
+def _point_problem():
+    lt, _ = _fixed_problem(seed=77)
+    P = softmax(lt.astype(np.float64), axis=-1)
+    # the proposals: the most likely token at two positions, unlikely ones at the others
+    x = [int(np.argmax(P[0])), int(np.argsort(P[1])[2]), int(np.argmax(P[2])),
+         int(np.argsort(P[3])[4])]
+    return lt, P, x
+
+
+def _point_acceptance_stat(n, P, x):
+    """chi-square of the accepted count against prod_{i<k} p_i(x_i) (1 - p_k(x_k))."""
+    G = len(x)
+    a = np.array([P[i, x[i]] for i in range(G)])
+    probs = np.array([np.prod(a[:k]) * (1 - a[k]) for k in range(G)] + [np.prod(a)])
+    return _chi2_stat(np.bincount(n, minlength=G + 1), probs)
+
+
+def test_point_drafts_emit_target_tokens():
+    """A drafter that proposes fixed tokens (q_i = indicator of x_i) still
+    yields tokens distributed as p_k at every position, and accepts x_i with
+    probability p_i(x_i)."""
+    lt, P, x = _point_problem()
+    tokens, n = _run_point(lt, x, 1_000_000)
+    for k, (stat, df) in enumerate(_position_stats(tokens, n, P)):
+        assert stat < chi2.isf(PASS_P, df), (k, stat)
+    stat, df = _point_acceptance_stat(n, P, x)
+    assert stat < chi2.isf(PASS_P, df), stat
+
+
+@pytest.mark.parametrize("fault", [oracle.FAULT_UNSCALED_TAU, oracle.FAULT_RESAMPLE_P])
+def test_point_planted_mistakes_are_detected(fault):
+    lt, P, x = _point_problem()
+    tokens, n = _run_point(lt, x, 400_000, fault=fault, seed=32)
+    stats = [s for s, _ in _position_stats(tokens, n, P)]
+    sa, _ = _point_acceptance_stat(n, P, x)
+    assert max(stats + [sa]) > chi2.isf(FAIL_P, 7), (fault, stats, sa)
+
+
 # ---------------------------------------------------------------- toy context models
 class Bigram:
     """A context-dependent toy 'model': logits of the next token depend on
