@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
-    ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
+    ap.add_argument("--mode", default="sample", choices=["sample", "greedy", "point"])
     ap.add_argument("--rotate", type=int, default=0, help="device copies (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -78,7 +78,7 @@ def main():
     gen_s = time.time() - t0
     B, G, V = case.B, case.G, case.V
     dt = sv.BF16 if case.target.dtype == np.uint16 else sv.F32
-    mode = sv.GREEDY if args.mode == "greedy" else sv.SAMPLE
+    mode = {"sample": sv.SAMPLE, "greedy": sv.GREEDY, "point": sv.POINT}[args.mode]
     step_bytes = inputs.algorithmic_bytes(case)
     logit_bytes = case.target.nbytes + (case.draft.nbytes if mode == sv.SAMPLE else 0)
     rot = args.rotate or max(1, -(-ROTATE_BYTES // logit_bytes))
@@ -88,8 +88,11 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    tgt0, dft0 = logits(case.target), logits(case.draft)
-    sets = [(tgt0, dft0)] + [(tgt0.clone(), dft0.clone()) for _ in range(rot - 1)]
+    # point-mass drafts come without draft logits: none are passed
+    tgt0 = logits(case.target)
+    dft0 = logits(case.draft) if mode == sv.SAMPLE else None
+    sets = [(tgt0, dft0)] + [(tgt0.clone(), None if dft0 is None else dft0.clone())
+                             for _ in range(rot - 1)]
     tok = torch.from_numpy(case.tokens).to(dev)
     uni = torch.from_numpy(case.uniforms).to(dev)
     gam = torch.from_numpy(case.gamma).to(dev)
@@ -179,7 +182,8 @@ def main():
             c0 = time.perf_counter()
             oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
                           case.kv_len, temperature=case.T,
-                          mode=oracle.GREEDY if mode == sv.GREEDY else oracle.SAMPLE,
+                          mode={sv.SAMPLE: oracle.SAMPLE, sv.GREEDY: oracle.GREEDY,
+                                sv.POINT: oracle.POINT}[mode],
                           threads=threads)
             t_cpu += time.perf_counter() - c0
             reps += 1

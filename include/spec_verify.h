@@ -23,6 +23,12 @@
  *     with positive weight.
  *   GREEDY mode ignores T, q and u: g_i = lowest index of the largest
  *   target logit of row i; accept while x_i == g_i; emit x_0..x_{n-1}, g_n.
+ *   POINT mode is SAMPLE for a drafter that proposes tokens outright, with
+ *   no draft distribution (a greedy draft, an n-gram / prompt-lookup match:
+ *   mhtirogla.ai, "Variants" and "Implementation notes"; tusharamrit,
+ *   "Self-speculation"): q_i is the indicator of x_i, so x_i is accepted
+ *   while u_i < p_i(x_i), and after a rejection at n the draw is from p_n
+ *   with x_n removed (Z = 1 - p_n(x_n)).  Draft logits are not read.
  *   new_len[b] = kv_len_in[b] + n (the KV caches keep the accepted drafts;
  *   the emitted correction or bonus token has no cache entry yet).
  *
@@ -45,7 +51,7 @@
 extern "C" {
 #endif
 
-enum spec_mode { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1 };
+enum spec_mode { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1, SPEC_MODE_POINT = 2 };
 enum spec_dtype { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 };
 
 enum spec_status {
@@ -53,8 +59,8 @@ enum spec_status {
   SPEC_ERR_NULL = -1,      /* a required pointer is NULL                              */
   SPEC_ERR_SHAPE = -2,     /* B < 1, V < 1, V > 2^20, gamma_max outside [0, 63], or
                               more than 2^31 - 1 workgroups                          */
-  SPEC_ERR_ARG = -3,       /* unknown mode or dtype; T not finite and > 0 when
-                              sampling; a tuning value spec_verify_tune refuses      */
+  SPEC_ERR_ARG = -3,       /* unknown mode or dtype; T not finite and > 0 in SAMPLE
+                              or POINT mode; a tuning value spec_verify_tune refuses */
   SPEC_ERR_WORKSPACE = -4, /* workspace NULL or smaller than spec_verify_workspace_bytes */
   SPEC_ERR_ALIGN = -5,     /* logits not aligned to their element size, or an int32/float
                               array not 4-byte aligned                                 */
@@ -84,20 +90,22 @@ int spec_verify_workspace_reset(void* workspace, size_t bytes, void* stream);
 /* The verify step.  Device pointers unless stated; all arrays dense,
  * row-major, innermost index last:
  *   target_logits  [B, gamma_max+1, V] of dtype (fp32, or bf16 bit patterns)
- *   draft_logits   [B, gamma_max, V]   of dtype; may be NULL in GREEDY mode
+ *   draft_logits   [B, gamma_max, V]   of dtype; read in SAMPLE mode only
+ *                  (may be NULL otherwise)
  *   draft_tokens   int32 [B, gamma_max]; x_i for i < gamma_per_row[b]
  *   uniforms       fp32 [B, gamma_max+1] in [0, 1); may be NULL in GREEDY
  *   gamma_per_row  int32 [B]; each in [0, gamma_max]
  *   kv_len_in      int32 [B], or NULL for 0
- *   temperature    T > 0 (SAMPLE); ignored in GREEDY
+ *   temperature    T > 0 (SAMPLE, POINT); ignored in GREEDY
  *   out_tokens     int32 [B, gamma_max+1]: n+1 emitted tokens, then -1
  *   out_n_accepted int32 [B]: n
  *   out_new_len    int32 [B]: kv_len_in + n
  * Any 2-byte (bf16) or 4-byte (fp32) aligned logits base works; rows need
  * not be 16-byte aligned.  Logits must be finite or -inf.
  * Per-row data errors (gamma outside [0, gamma_max]; a tested draft token
- * outside [0, V); when sampling, a row the walk uses -- p_i and q_i of a
- * tested position, p_g for the bonus -- whose logits are all -inf) give
+ * outside [0, V); in SAMPLE and POINT mode, a row the walk uses -- p_i and
+ * (SAMPLE) q_i of a tested position, p_g for the bonus -- whose logits are
+ * all -inf) give
  * n_accepted = -1, tokens all -1 and new_len = kv_len_in for that row only.
  * Rows after the first rejection are never used. */
 int spec_verify(const void* target_logits, const void* draft_logits,
@@ -111,12 +119,13 @@ int spec_verify(const void* target_logits, const void* draft_logits,
  * arguments and semantics, slower).  Each probe pointer may be NULL:
  *   out_px, out_qx  fp32 [B, gamma_max]: p_i(x_i), q_i(x_i) for every
  *                   i < gamma_per_row[b] with a valid token (untouched
- *                   otherwise; sampling only)
+ *                   otherwise; SAMPLE and POINT only, q_i(x_i) = 1 in POINT)
  *   out_z           fp32 [B]: normaliser Z of the drawn distribution
  *   out_m, out_s    fp32 [B, 2*gamma_max+1]: per vocabulary row (target
  *                   rows 0..gamma_max, then draft rows 0..gamma_max-1) the
  *                   largest raw logit and S = sum_j exp((l_j - max) / T)
- *                   (GREEDY: out_m only, out_s holds the argmax as float) */
+ *                   (GREEDY: out_m only, out_s holds the argmax as float;
+ *                   GREEDY and POINT leave the draft slots untouched) */
 int spec_verify_probe(const void* target_logits, const void* draft_logits,
                       const int32_t* draft_tokens, const float* uniforms,
                       const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
@@ -146,7 +155,8 @@ int spec_verify_tune(int vectors, int target_workgroups, int reserved);
 /* Reads the workspace's diagnostic word (device -> host copy on `stream`,
  * synchronous): bit 0 set if a workgroup ever gave up waiting for the rest
  * of its batch row's workgroups (cannot happen in a correct launch), bit 1
- * set if a residual with zero mass fell back to p. */
+ * set if a residual with zero mass fell back to p (POINT: to x_n, the only
+ * token p_n then has). */
 int spec_verify_diagnostics(const void* workspace, uint32_t* out_flags, void* stream);
 
 const char* spec_verify_strerror(int status);

@@ -2,7 +2,8 @@
 
 Acceptance rule:
   * greedy: tokens, accepted counts and new lengths bit-exact;
-  * sampling: probabilities p_i(x_i), q_i(x_i) within 1e-5 relative (values
+  * sampling (and point-mass drafts, where q_i(x_i) = 1 and only target rows
+    have statistics): probabilities p_i(x_i), q_i(x_i) within 1e-5 relative (values
     below 1e-30 within 1e-35 absolute, where fp32 exp loses relative
     accuracy and no decision depends on them); every row whose tokens,
     count or new length differ must be attributable to rounding: its first
@@ -75,8 +76,11 @@ def _close(gpu, ref):
     return ok, rel
 
 
+_MODES = {"sample": oracle.SAMPLE, "greedy": oracle.GREEDY, "point": oracle.POINT}
+
+
 def run_oracle(case, threads=0):
-    mode = oracle.GREEDY if case.mode == "greedy" else oracle.SAMPLE
+    mode = _MODES[case.mode]
     return oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
                          case.kv_len, temperature=case.T, mode=mode, threads=threads)
 
@@ -109,7 +113,7 @@ def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) ->
                     if not ok:
                         rep.prob_errors.append((row_offset + b, i, what, float(gv), float(ov)))
             # per vocabulary row statistics: max exact, S within 1e-5 relative
-            nr = 2 * int(g[b]) + 1
+            nr = 2 * int(g[b]) + 1 if case.mode == "sample" else int(g[b]) + 1
             slots = list(range(int(g[b]) + 1)) + [case.G + 1 + i for i in range(int(g[b]))]
             for sl in slots[:nr]:
                 if probe["m"][b, sl] != np.float32(ref.m[b, sl]):
@@ -154,7 +158,7 @@ def _attribute(case, b, n_gpu, tok_gpu, ref):
     if not (0 <= jg < case.V):
         return None
     cdf, pos = oracle.draw_cdf(case.target, case.draft, case.tokens, case.uniforms, case.gamma, b,
-                               temperature=case.T)
+                               temperature=case.T, mode=_MODES[case.mode])
     if pos != n_or:
         return None
     us = u[n_or + 1] if n_or < case.gamma[b] else u[int(case.gamma[b])]

@@ -14,7 +14,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
-SAMPLE, GREEDY = 0, 1
+SAMPLE, GREEDY, POINT = 0, 1, 2
 F32, BF16 = 0, 1
 OK, ERR_NULL, ERR_SHAPE, ERR_ARG, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5, -100
 GAMMA_MAX_LIMIT = 63

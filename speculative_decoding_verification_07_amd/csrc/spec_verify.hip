@@ -80,11 +80,12 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int make_plan(int B, int G, int V, int dtype, int mode, Plan* p) {
   if (B < 1 || V < 1 || V > kMaxVocab || G < 0 || G > SPEC_GAMMA_MAX_LIMIT) return SPEC_ERR_SHAPE;
   if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return SPEC_ERR_ARG;
-  if (mode != SPEC_MODE_SAMPLE && mode != SPEC_MODE_GREEDY) return SPEC_ERR_ARG;
-  const bool sample = mode == SPEC_MODE_SAMPLE;
+  if (mode != SPEC_MODE_SAMPLE && mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_POINT)
+    return SPEC_ERR_ARG;
+  const bool draws = mode != SPEC_MODE_GREEDY;  // a token is drawn (sample, point)
   const int vec = dtype == SPEC_DTYPE_F32 ? 4 : 8;
   p->B = B, p->G = G, p->V = V, p->dtype = dtype, p->mode = mode;
-  p->NR = sample ? 2 * G + 1 : G + 1;
+  p->NR = mode == SPEC_MODE_SAMPLE ? 2 * G + 1 : G + 1;
   // a ring of rows in flight plus (sampling) the drawn rows' slices held in
   // registers: at most 4 vectors per thread and row
   const int rmax = 4;
@@ -115,7 +116,7 @@ int make_plan(int B, int G, int V, int dtype, int mode, Plan* p) {
   p->off_ctr = off; off = align256(off + sizeof(unsigned) * kRowWords * (size_t)B);
   p->off_part = off; off = align256(off + sizeof(uint64_t) * (size_t)B * p->NC * p->NR);
   p->off_wsum = off;
-  if (sample) off = align256(off + sizeof(uint64_t) * 2 * (size_t)B * p->NC);
+  if (draws) off = align256(off + sizeof(uint64_t) * 2 * (size_t)B * p->NC);
   p->bytes = off;
   return SPEC_OK;
 }
@@ -297,6 +298,42 @@ __device__ void load_slice_as(const char* p, const Geom& g, Slice<DT, R>& s) {
   s.tl = t < g.len - g.jb ? E::one(p, g.jb + t) : NEG_INF;
 }
 
+// Sets element `rel` of the slice (index relative to its start) to -inf in
+// the registers of the thread that holds it; nothing if rel is outside the
+// slice.  Weights recomputed from the slice then give that element 0.
+template <int DT, int R>
+__device__ __forceinline__ void knock_out(Slice<DT, R>& s, const Geom& g, int rel) {
+  using E = Elt<DT>;
+  const int t = threadIdx.x;
+  if (rel < 0 || rel >= g.len) return;
+  if (rel < g.head) {
+    if (t == rel) s.hd = NEG_INF;
+    return;
+  }
+  if (rel >= g.jb) {
+    if (t == rel - g.jb) s.tl = NEG_INF;
+    return;
+  }
+  const int q = (rel - g.head) / E::kVec, e = (rel - g.head) % E::kVec;
+  if (q % kThreads != t) return;
+  const int k = q / kThreads;
+  // the element's 32-bit word in the vector, and the bits it occupies there
+  // (bf16: element 2i is the low half of word i)
+  const int wi = DT == SPEC_DTYPE_F32 ? e : e >> 1;
+  const int sh = DT == SPEC_DTYPE_F32 ? 0 : (e & 1) * 16;
+  const uint32_t keep = DT == SPEC_DTYPE_F32 ? 0u : ~(0xffffu << sh);
+  const uint32_t ninf = DT == SPEC_DTYPE_F32 ? 0xff800000u : 0xff80u << sh;
+#pragma unroll
+  for (int kk = 0; kk < R; ++kk) {
+    if (kk != k) continue;
+    uint4& v = s.v[kk];
+    v.x = wi == 0 ? (v.x & keep) | ninf : v.x;
+    v.y = wi == 1 ? (v.y & keep) | ninf : v.y;
+    v.z = wi == 2 ? (v.z & keep) | ninf : v.z;
+    v.w = wi == 3 ? (v.w & keep) | ninf : v.w;
+  }
+}
+
 // ------------------------------------------------------------------ reductions
 // Softmax statistics are kept in the scaled domain z = l * k2 (k2 = log2(e)/T):
 // a pair (m, S) has m = the largest raw logit and S = sum_j 2^(l_j k2 - R(m)),
@@ -467,6 +504,7 @@ struct Decision {
   int n;        // accepted drafts
   int dead;     // 1: data error, the row holds the sentinel
   int resid;    // 1: draw from the residual at n, 0: bonus draw from p_g
+  int xn;       // x_n (point-mass drafts: the token the residual excludes)
   float ustar;  // uniform of the draw
   float mt, st, md, sd;  // (max, exp-sum) of target row n and draft row n
 };
@@ -637,7 +675,7 @@ constexpr int kRingVectors = 12;
 // waits stay counted exactly.
 template <int DT, int MODE, int R, bool AL>
 __device__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int lo, int len) {
-  constexpr bool kSample = MODE == SPEC_MODE_SAMPLE;
+  constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // softmax statistics
   constexpr int NB = kRingVectors / R > 2 ? kRingVectors / R : 2;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   Slice<DT, R> buf[NB];
@@ -753,18 +791,18 @@ __device__ Gathered gather_small(const Args& a, int b, int g) {
   const int lane = threadIdx.x;
   if (threadIdx.x >= 64) return r;
   if (lane < g) r.x = a.tok[(int64_t)b * a.G + lane];
-  if (MODE == SPEC_MODE_SAMPLE && lane <= g) r.u = a.uni[(int64_t)b * (a.G + 1) + lane];
+  if (MODE != SPEC_MODE_GREEDY && lane <= g) r.u = a.uni[(int64_t)b * (a.G + 1) + lane];
   return r;
 }
 
-// t[x_i] and d[x_i]: issued once the row loads are done (they depend on x_i,
-// and waiting for them earlier would hold up the streaming).
-template <int DT>
+// t[x_i] and (sampling) d[x_i]: issued once the row loads are done (they
+// depend on x_i, and waiting for them earlier would hold up the streaming).
+template <int DT, int MODE>
 __device__ void gather_logits(const Args& a, int b, int g, Gathered& r) {
   const int lane = threadIdx.x;
   if (threadIdx.x < 64 && lane < g && (unsigned)r.x < (unsigned)a.V) {
     r.tv = Elt<DT>::one(row_of<DT>(a, b, g, lane), r.x);
-    r.dv = Elt<DT>::one(row_of<DT>(a, b, g, g + 1 + lane), r.x);
+    if (MODE == SPEC_MODE_SAMPLE) r.dv = Elt<DT>::one(row_of<DT>(a, b, g, g + 1 + lane), r.x);
   }
 }
 
@@ -774,9 +812,10 @@ __device__ void gather_logits(const Args& a, int b, int g, Gathered& r) {
 // probes are written.
 template <int DT, int MODE>
 __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, bool write_out) {
-  constexpr bool kSample = MODE == SPEC_MODE_SAMPLE;
+  constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // a drawn token (sample, point)
+  constexpr bool kPoint = MODE == SPEC_MODE_POINT;
   const int t = threadIdx.x, lane = t & 63;
-  const int nrows = kSample ? 2 * g + 1 : g + 1;
+  const int nrows = MODE == SPEC_MODE_SAMPLE ? 2 * g + 1 : g + 1;
   if (t < 64) {
     if (write_out && a.pr_m) {
       for (int r = lane; r < nrows; r += 64) {
@@ -797,8 +836,9 @@ __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, 
         fail = true;
       } else if (kSample) {
         const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.M[lane], a.k2))) / L.S[lane];
+        // point-mass drafts: q_i is the indicator of x_i, so q_i(x_i) = 1
         const int dr = g + 1 + lane;
-        const float q = ex2(fmaf(in.dv, a.k2, -ref_of(L.M[dr], a.k2))) / L.S[dr];
+        const float q = kPoint ? 1.f : ex2(fmaf(in.dv, a.k2, -ref_of(L.M[dr], a.k2))) / L.S[dr];
         if (write_out && a.pr_px) {
           a.pr_px[(int64_t)b * a.G + lane] = p;
           a.pr_qx[(int64_t)b * a.G + lane] = q;
@@ -814,9 +854,11 @@ __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, 
     // sampling: a row the walk uses must have a finite logit.  A dead p_i or
     // q_i makes the test at i fail (NaN), so only the stop position can hold
     // one; rows after the stop are never used.
-    const bool dead_n = kSample && (L.M[n] == NEG_INF || (n < g && L.M[g + 1 + n] == NEG_INF));
+    const bool dead_n =
+        kSample && (L.M[n] == NEG_INF || (!kPoint && n < g && L.M[g + 1 + n] == NEG_INF));
     const bool sentinel = dead_n || bad_token;
     const float ustar = __shfl(in.u, n < g ? n + 1 : g, 64);
+    const int xn = __shfl(in.x, n < g ? n : 0, 64);
     if (write_out) {
       // gamma_max <= 63, so lane i owns output position i (and holds x_i)
       if (lane <= a.G && !(kSample && lane == n && !sentinel)) {
@@ -835,10 +877,10 @@ __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, 
     }
     if (lane == 0) {
       Decision d;
-      d.n = n, d.dead = sentinel, d.resid = n < g, d.ustar = ustar;
+      d.n = n, d.dead = sentinel, d.resid = n < g, d.xn = xn, d.ustar = ustar;
       d.mt = L.M[n], d.st = L.S[n];
-      d.md = n < g ? L.M[g + 1 + n] : 0.f;
-      d.sd = n < g ? L.S[g + 1 + n] : 1.f;
+      d.md = !kPoint && n < g ? L.M[g + 1 + n] : 0.f;
+      d.sd = !kPoint && n < g ? L.S[g + 1 + n] : 1.f;
       L.dec = d;
     }
   }
@@ -1020,10 +1062,12 @@ __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const S
 
 // Step 3 of a live sampled row: every workgroup of the group sums its slice
 // of the drawn distribution and publishes the sum; the workgroup whose slice
-// holds tau = u * Z writes the token.
+// holds tau = u * Z writes the token.  KNOCK (point-mass drafts, after a
+// rejection): the residual max(0, p_n - q_n) with q_n the indicator of x_n is
+// p_n without x_n, drawn as the plain weights of row n with x_n set to -inf.
 __device__ void row_exit(const Args& a, Lds& L, int b, int nrows);
 
-template <int DT, int R, bool RESID, bool AL>
+template <int DT, int R, bool RESID, bool KNOCK, bool AL>
 __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
                      const Decision& dc) {
   using E = Elt<DT>;
@@ -1045,6 +1089,7 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
   } else {
     sd = st;
   }
+  if (KNOCK) knock_out(st, gt, dc.xn - lo);
   uint64_t* ws = a.wsum + (int64_t)b * 2 * a.NC;
   double base = 0.0, z = 0.0;
   bool fallback = false;
@@ -1064,6 +1109,17 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
 #pragma unroll
   for (int s = 0; s < R + 2; ++s) acc += v[s];
   int owner = publish_sum(acc, 0);
+  if (KNOCK && !(z > 0.0)) {
+    // rounding left p_n without mass outside x_n: p_n is a point mass at x_n
+    // (the same published sums give every workgroup the same z)
+    if (c == 0 && t == 0) {
+      atomicOr(&a.hdr[1], kDiagZeroResid);
+      a.out_tok[(int64_t)b * (a.G + 1) + n] = dc.xn;
+      if (a.pr_z) a.pr_z[b] = 1.f;
+    }
+    row_exit(a, L, b, nrows);
+    return;
+  }
   bool resid = RESID;
   if (RESID && !(z > 0.0)) {
     if (c == 0 && t == 0) atomicOr(&a.hdr[1], kDiagZeroResid);
@@ -1132,7 +1188,7 @@ __device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
 #endif
 template <int DT, int MODE, int R, bool AL>
 __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a) {
-  constexpr bool kSample = MODE == SPEC_MODE_SAMPLE;
+  constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // a drawn token (sample, point)
   using E = Elt<DT>;
   __shared__ Lds L;
   const int t = threadIdx.x;
@@ -1142,14 +1198,14 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
     if (c == 0) write_sentinel(a, b);
     return;
   }
-  const int nrows = kSample ? 2 * g + 1 : g + 1;
+  const int nrows = MODE == SPEC_MODE_SAMPLE ? 2 * g + 1 : g + 1;
   const int lo = c * a.CL;
   const int len = min(a.V - lo, a.CL);
 
   Gathered in = gather_small<MODE>(a, b, g);
   stream_rows<DT, MODE, R, AL>(a, L, b, g, nrows, lo, len);
   publish_pairs<kSample>(a, L, b, c, nrows);
-  if (kSample) gather_logits<DT>(a, b, g, in);  // in flight during the wait
+  if (kSample) gather_logits<DT, MODE>(a, b, g, in);  // in flight during the wait
 
   if (!kSample) {
     // greedy: slice 0 waits for the group's pairs, decides, writes the row
@@ -1167,10 +1223,12 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   decide<DT, MODE>(a, L, b, g, in, c == 0);
   const Decision dc = L.dec;
   if (!dc.dead) {
-    if (dc.resid)
-      draw<DT, R, true, AL>(a, L, b, c, g, lo, len, nrows, dc);
+    if (dc.resid && MODE == SPEC_MODE_POINT)
+      draw<DT, R, false, true, AL>(a, L, b, c, g, lo, len, nrows, dc);
+    else if (dc.resid)
+      draw<DT, R, true, false, AL>(a, L, b, c, g, lo, len, nrows, dc);
     else
-      draw<DT, R, false, AL>(a, L, b, c, g, lo, len, nrows, dc);
+      draw<DT, R, false, false, AL>(a, L, b, c, g, lo, len, nrows, dc);
   } else {
     row_exit(a, L, b, nrows);
   }
@@ -1245,12 +1303,14 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   int st = make_plan(B, G, V, dtype, mode, &p);
   if (st != SPEC_OK) return st;
   const bool sample = mode == SPEC_MODE_SAMPLE;
+  const bool draws = mode != SPEC_MODE_GREEDY;
   if (!tgt || !gam || !out_tok || !out_n || !out_len) return SPEC_ERR_NULL;
   if (G > 0 && !tok) return SPEC_ERR_NULL;
-  if (sample && ((G > 0 && !dft) || !uni)) return SPEC_ERR_NULL;
-  if (sample && !(T > 0.f && isfinite(T))) return SPEC_ERR_ARG;
+  if ((sample && G > 0 && !dft) || (draws && !uni)) return SPEC_ERR_NULL;
+  if (draws && !(T > 0.f && isfinite(T))) return SPEC_ERR_ARG;
   if (!ws || ws_bytes < p.bytes) return SPEC_ERR_WORKSPACE;
   const size_t e = dtype == SPEC_DTYPE_F32 ? 4 : 2;
+  if (!sample) dft = nullptr;  // only sampling reads draft logits
   if (!aligned(tgt, e) || (dft && !aligned(dft, e))) return SPEC_ERR_ALIGN;
   const void* four[] = {tok, uni, gam, kv, out_tok, out_n, out_len, px, qx, pz, pm, ps};
   for (const void* q : four)
@@ -1267,7 +1327,7 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.part = (uint64_t*)(w + p.off_part);
   a.wsum = (uint64_t*)(w + p.off_wsum);
   a.B = B, a.G = G, a.V = V, a.NC = p.NC, a.CL = p.CL, a.NR = p.NR;
-  a.k2 = sample ? (float)(1.4426950408889634 / (double)T) : 1.f;
+  a.k2 = draws ? (float)(1.4426950408889634 / (double)T) : 1.f;
   a.max_spin = 1u << 22;  // ~0.2 s of polling: far beyond any legitimate wait
   hipStream_t s = (hipStream_t)stream;
   dim3 grid((unsigned)p.total);
@@ -1278,11 +1338,15 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   if (dtype == SPEC_DTYPE_BF16) {
     if (sample)
       launch<SPEC_DTYPE_BF16, SPEC_MODE_SAMPLE>(p.R, al, grid, s, a);
+    else if (draws)
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_POINT>(p.R, al, grid, s, a);
     else
       launch<SPEC_DTYPE_BF16, SPEC_MODE_GREEDY>(p.R, al, grid, s, a);
   } else {
     if (sample)
       launch<SPEC_DTYPE_F32, SPEC_MODE_SAMPLE>(p.R, al, grid, s, a);
+    else if (draws)
+      launch<SPEC_DTYPE_F32, SPEC_MODE_POINT>(p.R, al, grid, s, a);
     else
       launch<SPEC_DTYPE_F32, SPEC_MODE_GREEDY>(p.R, al, grid, s, a);
   }

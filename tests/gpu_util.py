@@ -4,6 +4,8 @@ import numpy as np
 
 import speculative_decoding_verification_07_amd as sv
 
+MODES = {"sample": sv.SAMPLE, "greedy": sv.GREEDY, "point": sv.POINT}
+
 
 def logits_to_dev(a, torch, offset=0):
     """numpy logits (float32 or bf16 bits) -> device tensor; `offset` > 0
@@ -23,7 +25,7 @@ def logits_to_dev(a, torch, offset=0):
 def case_to_dev(case, torch, offset=0):
     return dict(
         target=logits_to_dev(case.target, torch, offset),
-        draft=logits_to_dev(case.draft, torch, offset),
+        draft=None if case.mode == "point" else logits_to_dev(case.draft, torch, offset),
         tokens=torch.from_numpy(np.ascontiguousarray(case.tokens)).cuda(),
         uniforms=torch.from_numpy(np.ascontiguousarray(case.uniforms)).cuda(),
         gamma=torch.from_numpy(np.ascontiguousarray(case.gamma)).cuda(),
@@ -32,8 +34,10 @@ def case_to_dev(case, torch, offset=0):
 
 def run(case, torch, probe=True, workspace=None, dev=None, offset=0):
     d = dev if dev is not None else case_to_dev(case, torch, offset)
-    mode = sv.GREEDY if case.mode == "greedy" else sv.SAMPLE
-    res = sv.verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["gamma"], d["kv"],
+    mode = MODES[case.mode]
+    # point-mass drafts have no draft logits: pass none, so a read would fault loudly
+    draft = None if case.mode == "point" else d["draft"]
+    res = sv.verify(d["target"], draft, d["tokens"], d["uniforms"], d["gamma"], d["kv"],
                     temperature=case.T, mode=mode, workspace=workspace, probe=probe)
     torch.cuda.synchronize()
     out = [r.cpu().numpy() for r in res[:3]]

@@ -65,6 +65,7 @@ def _call(lib, **kw):
     (dict(dft=None), sv.ERR_NULL), (dict(uni=None), sv.ERR_NULL),
     (dict(T=0.0), sv.ERR_ARG), (dict(T=-1.0), sv.ERR_ARG), (dict(T=float("nan")), sv.ERR_ARG),
     (dict(T=float("inf")), sv.ERR_ARG),
+    (dict(mode=sv.POINT, uni=None), sv.ERR_NULL), (dict(mode=sv.POINT, T=0.0), sv.ERR_ARG),
     (dict(ws=None), sv.ERR_WORKSPACE), (dict(ws_bytes=16), sv.ERR_WORKSPACE),
     (dict(tgt=A + 1), sv.ERR_ALIGN), (dict(dtype=sv.F32, tgt=A + 2), sv.ERR_ALIGN),
     (dict(dft=A + 1), sv.ERR_ALIGN), (dict(tok=A + 2), sv.ERR_ALIGN), (dict(kv=A + 1), sv.ERR_ALIGN),
@@ -81,6 +82,9 @@ def test_null_tolerated_where_documented(lib):
     assert _call(lib, mode=sv.GREEDY, dft=None, uni=None, ws_bytes=1) == sv.ERR_WORKSPACE
     assert _call(lib, G=0, tok=None, dft=None, ws_bytes=1) == sv.ERR_WORKSPACE
     assert _call(lib, mode=sv.GREEDY, T=0.0, ws_bytes=1) == sv.ERR_WORKSPACE
+    # point-mass drafts never read draft logits: NULL or misaligned is fine
+    assert _call(lib, mode=sv.POINT, dft=None, ws_bytes=1) == sv.ERR_WORKSPACE
+    assert _call(lib, mode=sv.POINT, dft=A + 1, ws_bytes=1) == sv.ERR_WORKSPACE
 
 
 def test_probe_pointer_pairing(lib):
@@ -107,10 +111,14 @@ def test_workspace_bytes_and_plan(lib):
     assert p["vectors"] == 4 and p["slices"] == 16
     g = sv.plan(64, 4, 128256, sv.BF16, sv.GREEDY)
     assert g["vocab_rows"] == 5 and g["workgroups"] == 64 * g["slices"]
+    # point-mass drafts: target rows only, plus the draw sums greedy has no use for
+    pt = sv.plan(64, 4, 128256, sv.BF16, sv.POINT)
+    assert pt["vocab_rows"] == 5 and pt["slices"] == p["slices"]
+    assert g["workspace_bytes"] < pt["workspace_bytes"] < small
     f = sv.plan(1, 4, 50257, sv.F32, sv.SAMPLE)
     assert f["slice_len"] % 4 == 0 and f["vectors"] == 1
     # at most one slice per thread of the draw's slice scan, up to the largest vocabulary
-    for mode in (sv.SAMPLE, sv.GREEDY):
+    for mode in (sv.SAMPLE, sv.GREEDY, sv.POINT):
         for dt in (sv.F32, sv.BF16):
             for B in (1, 64, 4096):
                 q = sv.plan(B, 63, 1 << 20, dt, mode)

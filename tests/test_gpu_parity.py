@@ -1,7 +1,8 @@
 """GPU parity: the HIP verify (through the C ABI) against the CPU oracle on
-the same seeded inputs.
+the same seeded inputs, in the three modes (sampling, greedy, point-mass
+drafts).
 
-Bar (see oracle/parity.py): greedy bit-exact; sampling probabilities within
+Bar (see oracle/parity.py): greedy bit-exact; sampling and point-mass probabilities within
 1e-5 relative, tokens/counts/new lengths equal on >= 99.99% of rows with every
 mismatch attributable to a decision or CDF boundary within 1e-5.
 """
@@ -15,7 +16,7 @@ import oracle
 from oracle import parity
 from speculative_decoding_verification_07_amd import inputs
 
-from gpu_util import case_to_dev, run
+from gpu_util import MODES, case_to_dev, run
 
 pytestmark = pytest.mark.gpu
 FULL = os.environ.get("SPEC_FULL_PARITY") == "1"
@@ -47,6 +48,10 @@ SMALL = [
     (4, "sample", dict(B=12, V=9999)),
     (4, "greedy", dict(B=12, V=9999)),
     (5, "sample", dict(B=12, V=7777)),
+    (1, "point", dict(B=4, V=5003)),
+    (3, "point", dict(B=16, V=20011)),
+    (4, "point", dict(B=12, V=9999)),
+    (5, "point", dict(B=12, V=7777)),
 ]
 
 
@@ -60,7 +65,8 @@ def test_parity_small_shapes(torch, cfg, mode, kw):
 
 # ------------------------------------------------------------------ full sizes
 FULL_SIZES = [(1, "sample"), (1, "greedy"), (2, "sample"), (3, "sample"), (3, "greedy"),
-              (4, "sample"), (4, "greedy"), (5, "sample")]
+              (4, "sample"), (4, "greedy"), (5, "sample"), (1, "point"), (3, "point"),
+              (4, "point"), (5, "point")]
 
 
 @pytest.mark.parametrize("cfg,mode", FULL_SIZES)
@@ -113,6 +119,42 @@ def test_edge_gamma_zero_ragged_and_errors(torch):
         assert n[b] == -1 and np.all(tok[b] == -1) and ln[b] == case.kv_len[b]
 
 
+def test_edge_point_mode_errors_and_gamma_zero(torch):
+    case = inputs.make_case(1, rnd=13, mode="point", B=8, V=4099, dtype="bf16")
+    g = case.gamma.copy()
+    g[0] = 0
+    g[1] = -1              # data error
+    x = case.tokens.copy()
+    x[2, 0] = -3           # tested token out of range
+    x[3, 0] = case.V       # likewise
+    t = case.target.copy()
+    t[4, 0, :] = 0xFF80    # p_0 all -inf
+    # a dead bonus row is an error only where every draft is accepted
+    t[5, case.G, :] = 0xFF80
+    case.gamma, case.tokens, case.target = g, x, t
+    rep, tok, n, ln, pr = _check(case, torch)
+    for b in (1, 2, 3, 4):
+        assert n[b] == -1 and np.all(tok[b] == -1) and ln[b] == case.kv_len[b]
+    assert n[0] == 0 and 0 <= tok[0, 0] < case.V
+
+
+def test_edge_point_mode_certain_and_impossible_proposals(torch):
+    """p_i(x_i) = 1 (every other logit -inf): always accepted; p_i(x_i) = 0
+    (x_i's logit -inf): always rejected, and the draw never returns x_i."""
+    case = inputs.make_case(3, rnd=14, mode="point", B=12, V=3001)
+    t = case.target.copy()
+    for b in range(0, 12, 2):
+        for i in range(case.G):
+            t[b, i, :] = 0xFF80
+            t[b, i, case.tokens[b, i]] = 0x3F80
+    for b in range(1, 12, 2):
+        t[b, 0, case.tokens[b, 0]] = 0xFF80
+    case.target = t
+    rep, tok, n, ln, pr = _check(case, torch)
+    assert np.all(n[0::2] == case.gamma[0::2])
+    assert np.all(n[1::2] == 0) and np.all(tok[1::2, 0] != case.tokens[1::2, 0])
+
+
 def test_edge_dead_rows_after_the_stop(torch):
     """Rows the walk never reaches may hold no finite logit: the result is
     that of the same rows with ordinary logits."""
@@ -153,7 +195,7 @@ def test_edge_greedy_ties_and_dead_rows(torch):
 @pytest.mark.parametrize("V", [1, 2, 7, 9, 17, 257])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_edge_tiny_vocab(torch, V, dtype):
-    for mode in ("sample", "greedy"):
+    for mode in ("sample", "greedy", "point"):
         case = inputs.make_case(2, rnd=V, mode=mode, B=5, V=V, dtype=dtype)
         _check(case, torch)
 
@@ -162,7 +204,7 @@ def test_edge_tiny_vocab(torch, V, dtype):
 def test_edge_unaligned_rows(torch, dtype):
     """Base pointers one element past 16-byte alignment, and a vocabulary
     size that leaves every row at a different alignment."""
-    for mode in ("sample", "greedy"):
+    for mode in ("sample", "greedy", "point"):
         case = inputs.make_case(1, rnd=4, mode=mode, B=6, V=10007, dtype=dtype)
         for off in (1, 3):
             _check(case, torch, offset=off)
@@ -170,7 +212,7 @@ def test_edge_unaligned_rows(torch, dtype):
 
 def test_edge_gamma_limits(torch):
     # gamma_max = 0: plain sampling / argmax of one row
-    for mode in ("sample", "greedy"):
+    for mode in ("sample", "greedy", "point"):
         case = inputs.make_case(3, rnd=5, mode=mode, B=9, G=0, V=6007)
         _check(case, torch)
     # gamma_max = 63 (the ABI limit) at a small vocabulary
@@ -183,6 +225,18 @@ def test_edge_gamma_limits(torch):
                                                      case.gamma))
         _, tok, n, _, _ = _check(case, torch)
         assert np.all(n == 63)
+    # point-mass drafts at gamma_max = 63: proposals the target is sure of,
+    # except one late position
+    case = inputs.make_case(2, rnd=7, mode="point", B=3, G=63, V=517)
+    t = np.full(case.target.shape, 0xFF80, np.uint16)
+    for b in range(3):
+        for i in range(63):
+            t[b, i, case.tokens[b, i]] = 0x3F80
+    t[:, 63] = case.target[:, 63]
+    t[1, 50] = case.target[1, 50]
+    case.target = t
+    _, tok, n, _, _ = _check(case, torch)
+    assert n[0] == 63 and n[2] == 63 and n[1] >= 50
 
 
 # ------------------------------------------------------------------ determinism
@@ -220,10 +274,11 @@ def test_workspace_reuse_and_diagnostics(torch):
     nbytes = sv.workspace_bytes(16, big.G, 30000, sv.BF16, sv.SAMPLE)
     ws = sv.Workspace(nbytes)
     for cfg, kw in ((4, dict(B=16, V=30000)), (3, dict(B=5, V=1000)), (2, dict(B=16, V=30000)),
-                    (3, dict(B=3, V=20000, mode="greedy")), (1, dict(B=10, V=3000))):
+                    (3, dict(B=3, V=20000, mode="greedy")), (1, dict(B=10, V=3000)),
+                    (4, dict(B=16, V=30000, mode="point"))):
         case = inputs.make_case(cfg, rnd=9, **kw)
         assert sv.workspace_bytes(case.B, case.G, case.V, 1 if case.target.dtype == np.uint16 else 0,
-                                  sv.GREEDY if case.mode == "greedy" else sv.SAMPLE) <= nbytes
+                                  MODES[case.mode]) <= nbytes
         _check(case, torch, workspace=ws)
         # every call clears what it wrote (the diagnostic word aside)
         body = ws.tensor[ws.offset: ws.offset + nbytes].cpu().numpy().copy()
@@ -232,7 +287,7 @@ def test_workspace_reuse_and_diagnostics(torch):
     assert ws.diagnostics() == 0
 
 
-@pytest.mark.parametrize("mode", ["sample", "greedy"])
+@pytest.mark.parametrize("mode", ["sample", "greedy", "point"])
 def test_handoff_stress_alternating_data(torch, mode):
     """Cross-workgroup hand-off under load: two different full-size batches
     alternate on one workspace, so a workgroup that read a stale statistic,
@@ -241,8 +296,7 @@ def test_handoff_stress_alternating_data(torch, mode):
     of its batch bit for bit."""
     cases = [inputs.make_case(3, rnd=r, mode=mode) for r in (21, 22)]
     devs = [case_to_dev(c, torch) for c in cases]
-    ws = sv.Workspace(sv.workspace_bytes(64, 4, 128256, sv.BF16,
-                                         sv.GREEDY if mode == "greedy" else sv.SAMPLE))
+    ws = sv.Workspace(sv.workspace_bytes(64, 4, 128256, sv.BF16, MODES[mode]))
     refs = []
     for c, d in zip(cases, devs):
         r = run(c, torch, dev=d, workspace=ws)
