@@ -361,11 +361,6 @@ __device__ __forceinline__ void am_merge(float& v, int& i, float v2, int i2) {
   i = take ? i2 : i;
 }
 
-template <class T>
-__device__ __forceinline__ T shfl_xor(T v, int lane_mask) {
-  return __shfl_xor(v, lane_mask, 64);
-}
-
 // Wave-wide reductions on the DPP path (no LDS round trips): a butterfly
 // inside each row of 16 lanes, then row broadcasts that leave the total in
 // lane 63, which is read back as a wave-uniform value.  The order of the
@@ -407,14 +402,49 @@ __device__ __forceinline__ void wave_am_dpp(float& v, int& i) {
   v = M;
 }
 
-__device__ __forceinline__ void wave_ms(float& m, float& s, float k2) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ms_merge(m, s, shfl_xor(m, o), shfl_xor(s, o), k2);
+// Doubles on the DPP path: each half moves with its own DPP move, and lanes
+// without a source read 0 (the identity of +).  Shuffles of doubles through
+// the LDS crossbar (ds_bpermute) cost a round trip per step, which added up
+// to microseconds in the draw's reductions.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROWS, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
 }
 
-__device__ __forceinline__ void wave_am(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) am_merge(v, i, shfl_xor(v, o), shfl_xor(i, o));
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Wave total of a double in every lane (the butterfly and row broadcasts of
+// SPEC_WAVE_REDUCE; fixed order, so deterministic).
+__device__ __forceinline__ double wave_sum_d(double x) {
+  x += dpp_d<0xB1, 0xf>(x);   // quad_perm [1,0,3,2]
+  x += dpp_d<0x4E, 0xf>(x);   // quad_perm [2,3,0,1]
+  x += dpp_d<0x141, 0xf>(x);  // row_half_mirror
+  x += dpp_d<0x140, 0xf>(x);  // row_mirror
+  x += dpp_d<0x142, 0xa>(x);  // row_bcast:15
+  x += dpp_d<0x143, 0xc>(x);  // row_bcast:31
+  return readlane_d(x, 63);
+}
+
+// Inclusive prefix sum over the wave: shifts by 1, 2, 4 and 8 inside each row
+// of 16 lanes, then the row broadcasts carry each row's total into the rows
+// above it.  `excl` is the inclusive sum of the lane below (0 in lane 0).
+__device__ __forceinline__ double wave_scan_d(double x, double& excl) {
+  x += dpp_d<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_d<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_d<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_d<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_d<0x142, 0xa>(x);  // row_bcast:15
+  x += dpp_d<0x143, 0xc>(x);  // row_bcast:31
+  excl = dpp_d<0x138, 0xf>(x);  // wave_shr:1
+  return x;
 }
 
 // (max, lowest index of the max) of this thread's share; lo = the slice's
@@ -523,29 +553,13 @@ struct Lds {
 };
 
 // ------------------------------------------------------------------ block helpers
-__device__ void block_sum_d(double& a, Lds& L) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) a += shfl_xor(a, o);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) L.red_d[w] = a;
-  __syncthreads();
-  a = L.red_d[0];
-  for (int k = 1; k < kWaves; ++k) a += L.red_d[k];
-  __syncthreads();
-}
-
 // Block totals of N doubles per thread at once; every thread gets them.
 template <int N>
 __device__ void block_sums_n(const double (&v)[N], double (&tot)[N], Lds& L) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   double x[N];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    x[n] = v[n];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x[n] += shfl_xor(x[n], o);
-  }
+  for (int n = 0; n < N; ++n) x[n] = wave_sum_d(v[n]);
   __syncthreads();
   if (lane == 0) {
 #pragma unroll
@@ -565,14 +579,8 @@ __device__ void block_sums_n(const double (&v)[N], double (&tot)[N], Lds& L) {
 // fixed order (deterministic); `total` is the sum over the block.
 __device__ void block_scan_d(double v, Lds& L, double& incl, double& excl, double& total) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  double x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  double prev = __shfl_up(x, 1, 64);
-  if (lane == 0) prev = 0.0;
+  double prev;
+  const double x = wave_scan_d(v, prev);
   __syncthreads();
   if (lane == 63) L.red_d[w] = x;
   __syncthreads();
@@ -667,6 +675,21 @@ __device__ __forceinline__ void wave_slice_ms(const Slice<DT, R>& s, const Geom&
 // ring = kRingVectors / R.
 constexpr int kRingVectors = 12;
 
+// Streaming order: the rows a draw is most likely to read again come last, so
+// that they are still in the L2 when it does (a rejection at position i is
+// about as likely as the walk reaching i, so early positions are the likely
+// stops): t_g first, then (t_i, d_i) for i = g-1 down to 0 when sampling,
+// t_g down to t_0 with point-mass drafts.  Greedy draws nothing and streams
+// in index order.
+template <int MODE>
+__device__ __forceinline__ int stream_row(int k, int g) {
+  if (MODE == SPEC_MODE_GREEDY) return k;
+  if (MODE == SPEC_MODE_POINT) return g - k;
+  if (k == 0) return g;
+  const int j = (k - 1) >> 1;  // the pair of position g-1-j
+  return (k & 1) ? g - 1 - j : 2 * g - j;
+}
+
 // Streams this workgroup's slice of rows 0..nrows-1 and leaves each row's
 // slice pair in L.M / L.S (sampling: (m, S); greedy: (max, argmax bits)).
 // The loads of the next NB-1 rows are in flight while a row is reduced; the
@@ -681,7 +704,7 @@ __device__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int 
   Slice<DT, R> buf[NB];
   Geom geo[NB];
   auto issue = [&](int r, Slice<DT, R>& sl, Geom& gg) {
-    const int rr = r < nrows ? r : nrows - 1;
+    const int rr = stream_row<MODE>(r < nrows ? r : nrows - 1, g);
     const char* p = row_of<DT>(a, b, g, rr) + (int64_t)lo * Elt<DT>::kBytes;
     gg = geom_of<DT, AL>(p, len);
     load_slice<DT, R, AL>(p, gg, sl);
@@ -698,7 +721,10 @@ __device__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int 
       if (kSample) {
         float m, sm;
         wave_slice_ms<DT, R>(buf[j], geo[j], a.k2, m, sm);
-        if (lane == 0 && r < nrows) L.wm[r][w] = m, L.ws[r][w] = sm;
+        if (lane == 0 && r < nrows) {
+          const int rr = stream_row<MODE>(r, g);
+          L.wm[rr][w] = m, L.ws[rr][w] = sm;
+        }
       } else {
         float v;
         int ix;
@@ -981,16 +1007,15 @@ __device__ int find_owner(const Args& a, const uint64_t* ws, int nc, float u, Ld
 // Inverse CDF inside the owner's slice: the first element of positive weight
 // whose running sum (base + the weights before it, in index order) exceeds
 // tau; if rounding leaves none, the last element with positive weight.
-// Returns its index in the row.
+// v: this thread's segment sums, tot: their block totals (the ones the
+// slice's published sum was formed from).  Returns the index in the row.
 template <int DT, int R, bool RESID>
 __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const Slice<DT, R>& sd,
-                            const Geom& g, int lo, double base, double tau, Lds& L) {
+                            const Geom& g, int lo, const double (&v)[R + 2],
+                            const double (&tot)[R + 2], double base, double tau, Lds& L) {
   using E = Elt<DT>;
   constexpr int NS = R + 2;
   const int t = threadIdx.x;
-  double v[NS], tot[NS];
-  segment_sums<DT, R, RESID>(d, st, sd, g, v);
-  block_sums_n<NS>(v, tot, L);
   // the segment holding tau (all threads alike)
   double carry = base;
   int seg = -1, lastseg = -1;
@@ -1097,18 +1122,20 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
   // rounding left the residual without mass (exact arithmetic never does)
   // a slice sum is stored as the complement of its bits: never zero (the sum
   // is non-negative, so its sign bit is clear)
-  auto publish_sum = [&](double acc, int attempt) {
-    block_sum_d(acc, L);
+  // this thread's segment sums v and their block totals tot are kept for
+  // the search; the slice sum is the totals added in segment order
+  double v[R + 2], tot[R + 2];
+  auto publish_sum = [&](int attempt) {
+    block_sums_n<R + 2>(v, tot, L);
+    double acc = 0.0;
+#pragma unroll
+    for (int s = 0; s < R + 2; ++s) acc += tot[s];
     if (t == 0) put64(&ws[attempt * a.NC + c], ~(uint64_t)__double_as_longlong(acc));
     return find_owner(a, ws + attempt * a.NC, a.NC, dc.ustar, L, base, z, fallback);
   };
-  double v[R + 2];
   opaque(st), opaque(sd);
   segment_sums<DT, R, RESID>(d, st, sd, gt, v);
-  double acc = 0.0;
-#pragma unroll
-  for (int s = 0; s < R + 2; ++s) acc += v[s];
-  int owner = publish_sum(acc, 0);
+  int owner = publish_sum(0);
   if (KNOCK && !(z > 0.0)) {
     // rounding left p_n without mass outside x_n: p_n is a point mass at x_n
     // (the same published sums give every workgroup the same z)
@@ -1127,10 +1154,7 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
     d.scale = d.st_inv;
     opaque(st);
     segment_sums<DT, R, false>(d, st, st, gt, v);
-    acc = 0.0;
-#pragma unroll
-    for (int s = 0; s < R + 2; ++s) acc += v[s];
-    owner = publish_sum(acc, 1);
+    owner = publish_sum(1);
   }
   if (owner < 0) {  // no weight anywhere (cannot happen for a live row)
     owner = 0;
@@ -1143,8 +1167,8 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
   if (c != owner) return;
   opaque(st), opaque(sd);
   const double tau = fallback ? __builtin_inf() : (double)dc.ustar * z;
-  const int j = resid ? slice_search<DT, R, true>(d, st, sd, gt, lo, base, tau, L)
-                      : slice_search<DT, R, false>(d, st, st, gt, lo, base, tau, L);
+  const int j = resid ? slice_search<DT, R, true>(d, st, sd, gt, lo, v, tot, base, tau, L)
+                      : slice_search<DT, R, false>(d, st, st, gt, lo, v, tot, base, tau, L);
   if (t == 0) {
     a.out_tok[(int64_t)b * (a.G + 1) + n] = j;
     if (a.pr_z) a.pr_z[b] = (float)(RESID ? z : z * (double)d.st_inv);
