@@ -402,6 +402,40 @@ __device__ __forceinline__ void wave_am_dpp(float& v, int& i) {
   v = M;
 }
 
+// The same merges inside aligned groups of LPR lanes (LPR = 1, 2, 4, 8 or
+// 16): the butterfly steps of SPEC_WAVE_REDUCE that stay inside a group, so
+// every lane of a group ends with the group's result (same bits in each, the
+// merges being symmetric).
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp_mv(T x) {
+  return __builtin_bit_cast(
+      T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+template <int LPR, class T, class OP>
+__device__ __forceinline__ T group_reduce(T v, OP op) {
+  if constexpr (LPR >= 2) v = op(v, dpp_mv<0xB1>(v));   // quad_perm [1,0,3,2]
+  if constexpr (LPR >= 4) v = op(v, dpp_mv<0x4E>(v));   // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) v = op(v, dpp_mv<0x141>(v));  // row_half_mirror
+  if constexpr (LPR >= 16) v = op(v, dpp_mv<0x140>(v)); // row_mirror
+  return v;
+}
+
+template <int LPR>
+__device__ __forceinline__ void group_ms(float& m, float& s, float k2) {
+  const float M = group_reduce<LPR>(m, [](float x, float y) { return fmaxf(x, y); });
+  const float sc = (m == NEG_INF) ? 0.f : s * ex2(ref_of(m, k2) - ref_of(M, k2));
+  s = group_reduce<LPR>(sc, [](float x, float y) { return x + y; });
+  m = M;
+}
+
+template <int LPR>
+__device__ __forceinline__ void group_am(float& v, int& i) {
+  const float M = group_reduce<LPR>(v, [](float x, float y) { return fmaxf(x, y); });
+  i = group_reduce<LPR>(v == M ? i : 0x7fffffff, [](int x, int y) { return x < y ? x : y; });
+  v = M;
+}
+
 // Doubles on the DPP path: each half moves with its own DPP move, and lanes
 // without a source read 0 (the identity of +).  Shuffles of doubles through
 // the LDS crossbar (ds_bpermute) cost a round trip per step, which added up
@@ -539,6 +573,15 @@ struct Decision {
   float mt, st, md, sd;  // (max, exp-sum) of target row n and draft row n
 };
 
+// Result of the search over a row's slice sums: the slice holding tau (-1:
+// none has weight), whether rounding forced the fallback, the sum of the
+// slices before it, and the total Z.
+struct Owner {
+  int r;
+  int fallback;
+  double base, z;
+};
+
 struct Lds {
   float wm[kMaxRows][kWaves];  // per-row wave partials: m (greedy: max)
   float ws[kMaxRows][kWaves];  // S (greedy: argmax bits)
@@ -548,6 +591,7 @@ struct Lds {
   double red_d[8 * kWaves];
   unsigned long long mask[kWaves];
   Decision dec;
+  Owner own;
   double dbl;
   int pick, last;
 };
@@ -690,6 +734,16 @@ __device__ __forceinline__ int stream_row(int k, int g) {
   return (k & 1) ? g - 1 - j : 2 * g - j;
 }
 
+// The rows in flight while streaming: slot k % NB holds stream row k (the
+// row loaded k-th, see stream_row).  When the stream is done the slots hold
+// its last NB rows, which the draw uses instead of reading them again.
+template <int DT, int R>
+struct Ring {
+  static constexpr int NB = kRingVectors / R > 2 ? kRingVectors / R : 2;
+  Slice<DT, R> buf[NB];
+  Geom geo[NB];
+};
+
 // Streams this workgroup's slice of rows 0..nrows-1 and leaves each row's
 // slice pair in L.M / L.S (sampling: (m, S); greedy: (max, argmax bits)).
 // The loads of the next NB-1 rows are in flight while a row is reduced; the
@@ -697,14 +751,22 @@ __device__ __forceinline__ int stream_row(int k, int g) {
 // loads are unconditional -- past the last row they re-read it -- so the
 // waits stay counted exactly.
 template <int DT, int MODE, int R, bool AL>
-__device__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int lo, int len) {
+__device__ __forceinline__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int lo, int len,
+                            Ring<DT, R>& ring) {
   constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // softmax statistics
-  constexpr int NB = kRingVectors / R > 2 ? kRingVectors / R : 2;
+  constexpr int NB = Ring<DT, R>::NB;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   Slice<DT, R> buf[NB];
   Geom geo[NB];
+  // past the end, a slot loads the row it already holds (stream row k with
+  // k = r mod NB among the last NB rows), so the last NB rows stay in the ring
+  // for the draw; greedy draws nothing and re-reads the last row, which is
+  // the one most surely still cached
   auto issue = [&](int r, Slice<DT, R>& sl, Geom& gg) {
-    const int rr = stream_row<MODE>(r < nrows ? r : nrows - 1, g);
+    int k = r < nrows ? r : nrows - NB + (r - nrows) % NB;
+    k = k < 0 ? nrows - 1 : k;  // a slot no row of this call maps to
+    if (!kSample) k = r < nrows ? r : nrows - 1;
+    const int rr = stream_row<MODE>(k, g);
     const char* p = row_of<DT>(a, b, g, rr) + (int64_t)lo * Elt<DT>::kBytes;
     gg = geom_of<DT, AL>(p, len);
     load_slice<DT, R, AL>(p, gg, sl);
@@ -712,7 +774,7 @@ __device__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int 
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j) issue(j, buf[j], geo[j]);
   // whole groups of NB rows: no exit inside the unrolled body, whose rows
-  // past the end reduce a re-read of the last row and store nothing
+  // past the end reduce a reloaded row and store nothing
   for (int r0 = 0; r0 < nrows; r0 += NB) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -734,6 +796,8 @@ __device__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int 
       }
     }
   }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) ring.buf[j] = buf[j], ring.geo[j] = geo[j];
   __syncthreads();
   for (int r = t; r < nrows; r += kThreads) {
     float m = L.wm[r][0], s = L.ws[r][0];
@@ -764,13 +828,60 @@ __device__ void publish_pairs(const Args& a, Lds& L, int b, int c, int nrows) {
   }
 }
 
+// Merges the staged pairs of rows [r0, r1) (slice c of row r at
+// stage[(r - r0) * nc + c]) when a row has at most LPR slices: a wave takes
+// 64 / LPR rows at once, LPR lanes each.
+template <bool kSample, int LPR>
+__device__ void merge_rows_grouped(const Args& a, Lds& L, int r0, int r1, int nc) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int kRowsPerWave = 64 / LPR;
+  const int sub = lane / LPR, c = lane % LPR;
+  for (int rb = r0 + w * kRowsPerWave; rb < r1; rb += kWaves * kRowsPerWave) {
+    const int r = rb + sub;
+    const bool have = r < r1 && c < nc;
+    const uint64_t st = have ? L.stage[(r - r0) * nc + c] : 0;
+    if (kSample) {
+      float m = have ? lo_f(st) : NEG_INF, s = have ? hi_f(st) : 0.f;
+      group_ms<LPR>(m, s, a.k2);
+      if (c == 0 && r < r1) L.M[r] = m, L.S[r] = s;
+    } else {
+      float v = have ? lo_f(st) : NEG_INF;
+      int i = have ? (int)__float_as_uint(hi_f(st)) - 1 : 0x7fffffff;
+      group_am<LPR>(v, i);
+      if (c == 0 && r < r1) L.M[r] = v, L.S[r] = __int_as_float(i);
+    }
+  }
+}
+
+// The same with more than 16 slices per row: lane l takes slices l, l + 64,
+// ... of a row in turn, then a reduction across the wave; rows go to waves
+// round-robin.
+template <bool kSample>
+__device__ void merge_rows_wide(const Args& a, Lds& L, int r0, int r1, int nc) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int r = r0 + w; r < r1; r += kWaves) {
+    const uint64_t* st = &L.stage[(r - r0) * nc];
+    if (kSample) {
+      float m = NEG_INF, s = 0.f;
+      for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
+      wave_ms_dpp(m, s, a.k2);
+      if (lane == 0) L.M[r] = m, L.S[r] = s;
+    } else {
+      float v = NEG_INF;
+      int i = 0x7fffffff;
+      for (int c = lane; c < nc; c += 64)
+        am_merge(v, i, lo_f(st[c]), (int)__float_as_uint(hi_f(st[c])) - 1);
+      wave_am_dpp(v, i);
+      if (lane == 0) L.M[r] = v, L.S[r] = __int_as_float(i);
+    }
+  }
+}
+
 // Waits for the group's published pairs and merges them into L.M / L.S, in
-// the same fixed order in every workgroup: per row, lane l takes slices l,
-// l + 64, ... in turn, then a reduction across the wave.  Rows go to waves
-// round-robin, staged through LDS in batches.
+// the same fixed order in every workgroup, staged through LDS in batches.
 template <bool kSample>
 __device__ void merge_group(const Args& a, Lds& L, int b, int nrows) {
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int t = threadIdx.x;
   const int nc = a.NC;
   const uint64_t* base = a.part + (int64_t)b * nc * a.NR;
   const int per = kStage / nc > 0 ? kStage / nc : 1;
@@ -782,22 +893,14 @@ __device__ void merge_group(const Args& a, Lds& L, int b, int nrows) {
       L.stage[k] = poll64(a, &base[(int64_t)c * a.NR + r]);
     }
     __syncthreads();
-    for (int r = r0 + w; r < r1; r += kWaves) {
-      const uint64_t* st = &L.stage[(r - r0) * nc];
-      if (kSample) {
-        float m = NEG_INF, s = 0.f;
-        for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
-        wave_ms_dpp(m, s, a.k2);
-        if (lane == 0) L.M[r] = m, L.S[r] = s;
-      } else {
-        float v = NEG_INF;
-        int i = 0x7fffffff;
-        for (int c = lane; c < nc; c += 64)
-          am_merge(v, i, lo_f(st[c]), (int)__float_as_uint(hi_f(st[c])) - 1);
-        wave_am_dpp(v, i);
-        if (lane == 0) L.M[r] = v, L.S[r] = __int_as_float(i);
-      }
-    }
+    if (nc <= 4)
+      merge_rows_grouped<kSample, 4>(a, L, r0, r1, nc);
+    else if (nc <= 8)
+      merge_rows_grouped<kSample, 8>(a, L, r0, r1, nc);
+    else if (nc <= 16)
+      merge_rows_grouped<kSample, 16>(a, L, r0, r1, nc);
+    else
+      merge_rows_wide<kSample>(a, L, r0, r1, nc);
     __syncthreads();
   }
 }
@@ -876,15 +979,16 @@ __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, 
     }
     const unsigned long long mask = __ballot(fail);
     const int n = mask ? (__ffsll((long long)mask) - 1) : g;
-    const bool bad_token = mask && (__shfl(valid ? 1 : 0, n, 64) == 0);
+    const bool bad_token = mask && (__builtin_amdgcn_readlane(valid ? 1 : 0, n) == 0);
     // sampling: a row the walk uses must have a finite logit.  A dead p_i or
     // q_i makes the test at i fail (NaN), so only the stop position can hold
     // one; rows after the stop are never used.
     const bool dead_n =
         kSample && (L.M[n] == NEG_INF || (!kPoint && n < g && L.M[g + 1 + n] == NEG_INF));
     const bool sentinel = dead_n || bad_token;
-    const float ustar = __shfl(in.u, n < g ? n + 1 : g, 64);
-    const int xn = __shfl(in.x, n < g ? n : 0, 64);
+    // n is uniform (from the ballot): lane reads, not shuffles
+    const float ustar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in.u), n < g ? n + 1 : g));
+    const int xn = __builtin_amdgcn_readlane(in.x, n < g ? n : 0);
     if (write_out) {
       // gamma_max <= 63, so lane i owns output position i (and holds x_i)
       if (lane <= a.G && !(kSample && lane == n && !sentinel)) {
@@ -957,7 +1061,9 @@ __device__ __forceinline__ void vec_weights(const DrawParams& d, const uint4& vt
 }
 
 // This thread's weight sums by segment: [0] head, [1 + k] body round k,
-// [R + 1] tail (index order of the slice).
+// [R + 1] tail (index order of the slice).  A vector's weights are added in
+// fp32, in element order (a rounding of a few units in 1e-7 of the vector's
+// own sum), and the search within a vector repeats exactly those additions.
 template <int DT, int R, bool RESID>
 __device__ __forceinline__ void segment_sums(const DrawParams& d, const Slice<DT, R>& st,
                                              const Slice<DT, R>& sd, const Geom& g,
@@ -968,10 +1074,10 @@ __device__ __forceinline__ void segment_sums(const DrawParams& d, const Slice<DT
   for (int k = 0; k < R; ++k) {
     float w[E::kVec];
     vec_weights<DT, RESID>(d, vget(st, k, g), vget(sd, k, g), w);
-    double s = 0.0;
+    float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e) s += (double)w[e];
-    v[1 + k] = s;
+    for (int e = 0; e < E::kVec; ++e) s += w[e];
+    v[1 + k] = (double)s;
     __builtin_amdgcn_sched_barrier(0);  // one vector's weights live at a time
   }
   v[R + 1] = (double)draw_weight<RESID>(d, st.tl, sd.tl);
@@ -985,6 +1091,28 @@ __device__ __forceinline__ void segment_sums(const DrawParams& d, const Slice<DT
 __device__ int find_owner(const Args& a, const uint64_t* ws, int nc, float u, Lds& L,
                           double& base, double& z_out, bool& fallback) {
   const int t = threadIdx.x;
+  if (nc <= 64) {
+    // every slice sum fits one wave: wave 0 scans and searches, and hands the
+    // result to the others through LDS (one barrier instead of a block scan)
+    if (t < 64) {
+      const double v = t < nc ? __longlong_as_double((long long)~poll64(a, &ws[t])) : 0.0;
+      double excl;
+      const double incl = wave_scan_d(v, excl);
+      const double z = readlane_d(incl, 63);
+      const double tau = (double)u * z;
+      const unsigned long long hit = __ballot(v > 0.0 && tau < incl);
+      const unsigned long long pos = __ballot(v > 0.0);
+      const int r = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : -1);
+      const double bs = r >= 0 ? readlane_d(excl, r) : 0.0;
+      if (t == 0) L.own = Owner{r, hit == 0, bs, z};
+    }
+    __syncthreads();
+    const Owner o = L.own;
+    z_out = o.z;
+    fallback = o.fallback;
+    base = o.r >= 0 ? o.base : 0.0;
+    return o.r;
+  }
   const double v = t < nc ? __longlong_as_double((long long)~poll64(a, &ws[t])) : 0.0;
   double incl, excl, z;
   block_scan_d(v, L, incl, excl, z);
@@ -1065,14 +1193,15 @@ __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const S
 #pragma unroll
       for (int k = 0; k < R; ++k)
         if (k == seg - 1) vec_weights<DT, RESID>(d, vget(st2, k, g), vget(sd2, k, g), w);
-      double acc = carry + excl;
+      const double before = carry + excl;
+      float ps = 0.f;  // the vector's running sum, as segment_sums forms it
       int pick = -1, lp = 0;
 #pragma unroll
       for (int e = 0; e < E::kVec; ++e) {
-        acc += (double)w[e];
+        ps += w[e];
         if (w[e] > 0.f) {
           lp = e;
-          if (pick < 0 && !fb && tau < acc) pick = e;
+          if (pick < 0 && !fb && tau < before + (double)ps) pick = e;
         }
       }
       j = lo + g.head + ((seg - 1) * kThreads + t) * E::kVec + (pick >= 0 ? pick : lp);
@@ -1092,25 +1221,73 @@ __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const S
 // p_n without x_n, drawn as the plain weights of row n with x_n set to -inf.
 __device__ void row_exit(const Args& a, Lds& L, int b, int nrows);
 
+// Slot `k` of the ring, selected at run time (register by register, so that
+// the ring stays in registers).
+template <int DT, int R>
+__device__ __forceinline__ void ring_pick(const Ring<DT, R>& ring, int k, Slice<DT, R>& s,
+                                          Geom& g) {
+  s = ring.buf[0];
+  g = ring.geo[0];
+#pragma unroll
+  for (int j = 1; j < Ring<DT, R>::NB; ++j) {
+    const bool take = k == j;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      s.v[q].x = take ? ring.buf[j].v[q].x : s.v[q].x;
+      s.v[q].y = take ? ring.buf[j].v[q].y : s.v[q].y;
+      s.v[q].z = take ? ring.buf[j].v[q].z : s.v[q].z;
+      s.v[q].w = take ? ring.buf[j].v[q].w : s.v[q].w;
+    }
+    s.hd = take ? ring.buf[j].hd : s.hd;
+    s.tl = take ? ring.buf[j].tl : s.tl;
+    g.head = take ? ring.geo[j].head : g.head;
+    g.nv = take ? ring.geo[j].nv : g.nv;
+    g.jb = take ? ring.geo[j].jb : g.jb;
+    g.len = take ? ring.geo[j].len : g.len;
+  }
+}
+
 template <int DT, int R, bool RESID, bool KNOCK, bool AL>
-__device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
-                     const Decision& dc) {
+__device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
+                     const Decision& dc, const Ring<DT, R>& ring) {
   using E = Elt<DT>;
+  constexpr int NB = Ring<DT, R>::NB;
   const int t = threadIdx.x;
   DrawParams d{ref_of(dc.mt, a.k2), 1.f / dc.st, ref_of(dc.md, a.k2), 1.f / dc.sd, a.k2, 1.f};
   const int n = dc.n;
+  // stream indices of the rows drawn from (the inverse of stream_row): t_n
+  // and d_n at 2(g-1-n)+1 and +2 when sampling, t_n at g-n with point-mass
+  // drafts, t_g first of all for the bonus draw
+  const int kt = RESID ? 2 * (g - 1 - n) + 1 : (KNOCK ? g - n : 0);
+  const int kd = RESID ? kt + 1 : kt;
   Slice<DT, R> st, sd;
-  const char* tp = row_of<DT>(a, b, g, n) + (int64_t)lo * E::kBytes;
-  const Geom gt = geom_of<DT, AL>(tp, len);
-  load_slice<DT, R, AL>(tp, gt, st);
+  Geom gt;
+  // (the picks pass through opaque(): otherwise the optimiser merges "take
+  // from the ring" and "load from memory" into one load through a pointer,
+  // which sends the whole ring to scratch memory)
+  if (kt >= nrows - NB) {
+    ring_pick(ring, kt % NB, st, gt);
+    opaque(st);
+  } else {
+    const char* tp = row_of<DT>(a, b, g, n) + (int64_t)lo * E::kBytes;
+    gt = geom_of<DT, AL>(tp, len);
+    load_slice<DT, R, AL>(tp, gt, st);
+  }
   if (RESID) {
     // the weights pair element j of both rows: the draft slice takes the
     // target slice's register layout
-    const char* dp = row_of<DT>(a, b, g, g + 1 + n) + (int64_t)lo * E::kBytes;
-    if (AL || geom_of<DT, AL>(dp, len).head == gt.head)
-      load_slice<DT, R, AL>(dp, gt, sd);
-    else
-      load_slice_as<DT, R>(dp, gt, sd);
+    Geom gd;
+    if (kd >= nrows - NB) {
+      ring_pick(ring, kd % NB, sd, gd);
+      opaque(sd);
+    }
+    if (!(kd >= nrows - NB) || !(AL || gd.head == gt.head)) {
+      const char* dp = row_of<DT>(a, b, g, g + 1 + n) + (int64_t)lo * E::kBytes;
+      if (AL || geom_of<DT, AL>(dp, len).head == gt.head)
+        load_slice<DT, R, AL>(dp, gt, sd);
+      else
+        load_slice_as<DT, R>(dp, gt, sd);
+    }
   } else {
     sd = st;
   }
@@ -1227,7 +1404,8 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   const int len = min(a.V - lo, a.CL);
 
   Gathered in = gather_small<MODE>(a, b, g);
-  stream_rows<DT, MODE, R, AL>(a, L, b, g, nrows, lo, len);
+  Ring<DT, R> ring;
+  stream_rows<DT, MODE, R, AL>(a, L, b, g, nrows, lo, len, ring);
   publish_pairs<kSample>(a, L, b, c, nrows);
   if (kSample) gather_logits<DT, MODE>(a, b, g, in);  // in flight during the wait
 
@@ -1248,11 +1426,11 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   const Decision dc = L.dec;
   if (!dc.dead) {
     if (dc.resid && MODE == SPEC_MODE_POINT)
-      draw<DT, R, false, true, AL>(a, L, b, c, g, lo, len, nrows, dc);
+      draw<DT, R, false, true, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
     else if (dc.resid)
-      draw<DT, R, true, false, AL>(a, L, b, c, g, lo, len, nrows, dc);
+      draw<DT, R, true, false, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
     else
-      draw<DT, R, false, false, AL>(a, L, b, c, g, lo, len, nrows, dc);
+      draw<DT, R, false, false, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
   } else {
     row_exit(a, L, b, nrows);
   }
