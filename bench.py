@@ -26,7 +26,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 1 << 30  # at least this much distinct logit memory in rotation
-COUNTERS = os.path.join(ROOT, "profiles", "verify_kernel_c3_sample_counters.json")
+# HBM byte counters of the kernel per workload and mode (committed summaries of
+# rocprofv3 FETCH_SIZE / WRITE_SIZE runs); used only while the kernel source
+# still has the hash they were taken on
+COUNTERS = os.path.join(ROOT, "profiles", "verify_kernel_c{config}_{mode}_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_07_amd", "csrc",
                           "spec_verify.hip")
 
@@ -166,8 +169,9 @@ def main():
     del probe
 
     traffic = None
-    if os.path.exists(COUNTERS):
-        with open(COUNTERS) as f:
+    counters = COUNTERS.format(config=args.config, mode=args.mode)
+    if os.path.exists(counters):
+        with open(counters) as f:
             cnt = json.load(f)
         if cnt.get("source_sha256_16") == source_hash() and cnt.get("workload_config") == args.config \
                 and cnt.get("mode") == args.mode:

@@ -758,14 +758,16 @@ __device__ __forceinline__ void stream_rows(const Args& a, Lds& L, int b, int g,
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   Slice<DT, R> buf[NB];
   Geom geo[NB];
-  // past the end, a slot loads the row it already holds (stream row k with
-  // k = r mod NB among the last NB rows), so the last NB rows stay in the ring
-  // for the draw; greedy draws nothing and re-reads the last row, which is
-  // the one most surely still cached
+  // past the end, when sampling, a slot loads the row it already holds
+  // (stream row k with k = r mod NB among the last NB rows), so the last NB
+  // rows stay in the ring for the draw.  Otherwise it re-reads the last row,
+  // the one most surely still cached: greedy draws nothing, and with
+  // point-mass drafts the rows kept (t_2..t_0) are read again from memory by
+  // those reloads more often than the draw needs them.
   auto issue = [&](int r, Slice<DT, R>& sl, Geom& gg) {
     int k = r < nrows ? r : nrows - NB + (r - nrows) % NB;
     k = k < 0 ? nrows - 1 : k;  // a slot no row of this call maps to
-    if (!kSample) k = r < nrows ? r : nrows - 1;
+    if (MODE != SPEC_MODE_SAMPLE) k = r < nrows ? r : nrows - 1;
     const int rr = stream_row<MODE>(k, g);
     const char* p = row_of<DT>(a, b, g, rr) + (int64_t)lo * Elt<DT>::kBytes;
     gg = geom_of<DT, AL>(p, len);
@@ -1247,11 +1249,12 @@ __device__ __forceinline__ void ring_pick(const Ring<DT, R>& ring, int k, Slice<
   }
 }
 
-template <int DT, int R, bool RESID, bool KNOCK, bool AL>
+template <int DT, int R, bool RESID, bool KNOCK, bool RING, bool AL>
 __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
                      const Decision& dc, const Ring<DT, R>& ring) {
   using E = Elt<DT>;
-  constexpr int NB = Ring<DT, R>::NB;
+  // RING: the ring holds the last NB rows streamed (sampling)
+  constexpr int NB = RING ? Ring<DT, R>::NB : 0;
   const int t = threadIdx.x;
   DrawParams d{ref_of(dc.mt, a.k2), 1.f / dc.st, ref_of(dc.md, a.k2), 1.f / dc.sd, a.k2, 1.f};
   const int n = dc.n;
@@ -1265,8 +1268,8 @@ __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g,
   // (the picks pass through opaque(): otherwise the optimiser merges "take
   // from the ring" and "load from memory" into one load through a pointer,
   // which sends the whole ring to scratch memory)
-  if (kt >= nrows - NB) {
-    ring_pick(ring, kt % NB, st, gt);
+  if (RING && kt >= nrows - NB) {
+    ring_pick(ring, kt % Ring<DT, R>::NB, st, gt);
     opaque(st);
   } else {
     const char* tp = row_of<DT>(a, b, g, n) + (int64_t)lo * E::kBytes;
@@ -1277,11 +1280,12 @@ __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g,
     // the weights pair element j of both rows: the draft slice takes the
     // target slice's register layout
     Geom gd;
-    if (kd >= nrows - NB) {
-      ring_pick(ring, kd % NB, sd, gd);
+    const bool in_ring = RING && kd >= nrows - NB;
+    if (in_ring) {
+      ring_pick(ring, kd % Ring<DT, R>::NB, sd, gd);
       opaque(sd);
     }
-    if (!(kd >= nrows - NB) || !(AL || gd.head == gt.head)) {
+    if (!in_ring || !(AL || gd.head == gt.head)) {
       const char* dp = row_of<DT>(a, b, g, g + 1 + n) + (int64_t)lo * E::kBytes;
       if (AL || geom_of<DT, AL>(dp, len).head == gt.head)
         load_slice<DT, R, AL>(dp, gt, sd);
@@ -1425,12 +1429,13 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   decide<DT, MODE>(a, L, b, g, in, c == 0);
   const Decision dc = L.dec;
   if (!dc.dead) {
+    constexpr bool kRing = MODE == SPEC_MODE_SAMPLE;
     if (dc.resid && MODE == SPEC_MODE_POINT)
-      draw<DT, R, false, true, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, false, true, false, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
     else if (dc.resid)
-      draw<DT, R, true, false, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, true, false, kRing, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
     else
-      draw<DT, R, false, false, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, false, false, kRing, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
   } else {
     row_exit(a, L, b, nrows);
   }
