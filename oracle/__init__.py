@@ -23,7 +23,8 @@ _LIB = os.path.join(_HERE, "libspec_oracle.so")
 
 F32, BF16 = 0, 1
 SAMPLE, GREEDY, POINT = 0, 1, 2
-FAULT_NONE, FAULT_NO_CLAMP, FAULT_UNSCALED_TAU, FAULT_RESAMPLE_P, FAULT_GREEDY_RULE = range(5)
+(FAULT_NONE, FAULT_NO_CLAMP, FAULT_UNSCALED_TAU, FAULT_RESAMPLE_P, FAULT_GREEDY_RULE,
+ FAULT_FILTER_P_ONLY) = range(6)
 
 _lib = None
 
@@ -46,12 +47,15 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32 = ctypes.c_int
-        lib.oracle_verify.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, ctypes.c_double,
-                                      i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
+        D = ctypes.c_double
+        lib.oracle_verify.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, D,
+                                      i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i32, D, P]
         lib.oracle_verify.restype = i32
-        lib.oracle_draw_cdf.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, ctypes.c_double,
-                                        i32, i32, P]
+        lib.oracle_draw_cdf.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, D,
+                                        i32, i32, P, i32, D]
         lib.oracle_draw_cdf.restype = i32
+        lib.oracle_filter_row.argtypes = [P, i32, i32, D, i32, D, P, P]
+        lib.oracle_filter_row.restype = i32
         _lib = lib
     return _lib
 
@@ -80,6 +84,7 @@ class OracleResult:
     s: np.ndarray           # float64 [B, 2G+1]; sum exp((l - m) / T)
     draw_pos: np.ndarray    # int32 [B]; position drawn from, -1 if none
     zero_resid: np.ndarray  # int32 [B]; 1 where the residual mass was exactly 0
+    fmargin: np.ndarray     # float64 [B]; smallest top-p margin (relative mass) of the rows
 
 
 def _c(a, dt):
@@ -87,14 +92,15 @@ def _c(a, dt):
 
 
 def verify(target, draft, tokens, uniforms, gamma, kv_len=None, *, temperature=1.0,
-           mode=SAMPLE, fault=FAULT_NONE, threads=0) -> OracleResult:
+           mode=SAMPLE, fault=FAULT_NONE, threads=0, top_k=0, top_p=1.0) -> OracleResult:
     """Run the oracle over a batch.
 
     target: [B, G+1, V] float32 or uint16 (bf16 bits); draft: [B, G, V] same
     dtype (may be None in greedy and point mode, which ignore it); tokens:
     int32 [B, G]; uniforms:
     float32 [B, G+1] (may be None in greedy mode); gamma: int32 [B];
-    kv_len: int32 [B] or None.  threads=0 uses the OpenMP default.
+    kv_len: int32 [B] or None.  threads=0 uses the OpenMP default.  top_k
+    (0: off) and top_p (1: off) filter p and q alike before the walk.
     """
     lib = _load()
     target = np.ascontiguousarray(target)
@@ -123,17 +129,19 @@ def verify(target, draft, tokens, uniforms, gamma, kv_len=None, *, temperature=1
     s = np.empty((B, 2 * G + 1), np.float64)
     pos = np.empty(B, np.int32)
     zr = np.empty(B, np.int32)
+    fm = np.empty(B, np.float64)
     rc = lib.oracle_verify(_ptr(target), _ptr(draft), dt, _ptr(tokens), _ptr(uniforms),
                            _ptr(gamma), _ptr(kv_len), B, G, V, float(temperature), int(mode),
                            int(fault), int(threads), _ptr(out_tokens), _ptr(out_n),
                            _ptr(out_len), _ptr(px), _ptr(qx), _ptr(z), _ptr(m), _ptr(s),
-                           _ptr(pos), _ptr(zr))
+                           _ptr(pos), _ptr(zr), int(top_k), float(top_p), _ptr(fm))
     if rc != 0:
         raise ValueError(f"oracle refused its arguments (code {rc})")
-    return OracleResult(out_tokens, out_n, out_len, px, qx, z, m, s, pos, zr)
+    return OracleResult(out_tokens, out_n, out_len, px, qx, z, m, s, pos, zr, fm)
 
 
-def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0, mode=SAMPLE):
+def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0, mode=SAMPLE,
+             top_k=0, top_p=1.0):
     """Normalised CDF (C_j / Z, float64 [V]) of the distribution the oracle
     drew row `row`'s last token from, and the position it was drawn at."""
     lib = _load()
@@ -147,5 +155,20 @@ def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0, mo
     cdf = np.empty(V, np.float64)
     pos = lib.oracle_draw_cdf(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens),
                               _ptr(uniforms), _ptr(gamma), None, B, G, V, float(temperature),
-                              int(mode), int(row), _ptr(cdf))
+                              int(mode), int(row), _ptr(cdf), int(top_k), float(top_p))
     return cdf, int(pos)
+
+
+def filter_row(logits, *, temperature=1.0, top_k=0, top_p=1.0):
+    """The filtered distribution softmax(l/T) restricted to top-k then top-p
+    (float64 [V]) of one stored logit row, and its logit threshold."""
+    lib = _load()
+    logits = np.ascontiguousarray(logits)
+    prob = np.empty(logits.shape[-1], np.float64)
+    tau = ctypes.c_double(0.0)
+    rc = lib.oracle_filter_row(_ptr(logits), _dtype_code(logits), logits.shape[-1],
+                               float(temperature), int(top_k), float(top_p), _ptr(prob),
+                               ctypes.byref(tau))
+    if rc != 0:
+        raise ValueError("oracle refused the row or its arguments")
+    return prob, tau.value

@@ -34,7 +34,14 @@
  *      and its code block).
  *   5. KV rollback: the new cache length is kv_len_in + n (mhtirogla step 5,
  *      "truncate the length").
- *   6. Point-mass drafts (mode OR_POINT): the drafter proposes x_i outright
+ *   6. Filtering (top-k, top-p): the same processing applied to p and q
+ *      (mhtirogla "Implementation notes"; tusharamrit, the caveat after the
+ *      proof).  With logits l and temperature T, top-k keeps every l_j at or
+ *      above the k-th largest value (ties kept), then top-p keeps, among those,
+ *      the smallest set of largest values whose mass under softmax(l/T)
+ *      reaches top_p of the top-k-kept mass (all elements of a value
+ *      together).  The kept entries are renormalised; the rest get 0.
+ *   7. Point-mass drafts (mode OR_POINT): the drafter proposes x_i outright
  *      -- an n-gram / prompt-lookup match (mhtirogla "Variants" and
  *      "Implementation notes"; tusharamrit "Self-speculation") or a greedy
  *      draft (tokentrails code block) -- so q_i is the indicator of x_i and
@@ -82,6 +89,7 @@
 #define OR_FAULT_UNSCALED_TAU 2  /* threshold u instead of u * Z             */
 #define OR_FAULT_RESAMPLE_P 3    /* after a rejection draw from p, not residual */
 #define OR_FAULT_GREEDY_RULE 4   /* accept iff x == argmax p while sampling   */
+#define OR_FAULT_FILTER_P_ONLY 5 /* top-k / top-p applied to p but not to q    */
 
 typedef struct {
   const void* target;
@@ -95,6 +103,8 @@ typedef struct {
   double T;
   int mode;
   int fault;
+  int top_k;      /* 0: off */
+  double top_p;   /* 1: off */
 } oracle_ctx;
 
 /* Exact widening of one stored logit to double. */
@@ -111,10 +121,66 @@ static size_t row_off(const oracle_ctx* c, int b, int rows, int i) {
   return ((size_t)b * (size_t)rows + (size_t)i) * (size_t)c->V;
 }
 
-/* p = softmax(logits / T) in double.  Writes the raw-logit maximum and the
- * sum S = sum_j exp((l_j - max)/T).  Returns 0 when every logit is -inf. */
+static int cmp_desc(const void* a, const void* b) {
+  const double x = *(const double*)a, y = *(const double*)b;
+  return (x < y) - (x > y);
+}
+
+/* Filtering threshold of one row whose largest logit is m (finite): the
+ * filtered distribution keeps exactly the entries with l_j >= tau; -inf when
+ * nothing is cut.  top-k: tau_k = the k-th largest value.  top-p: walking the
+ * distinct values from the largest, tau_p = the first value at which the mass
+ * of everything at or above it reaches top_p * W, W the mass at or above
+ * tau_k (masses exp((l - m)/T), summed in that descending order).
+ * margin_out: how far that crossing is from top_p * W, relative to W (the
+ * smaller of the gaps just before and at the chosen value); +inf when top-p
+ * cuts nothing. */
+static double filter_threshold(const oracle_ctx* c, const void* base, size_t off, double m,
+                               double* margin_out) {
+  const int V = c->V;
+  if (margin_out) *margin_out = INFINITY;
+  const int use_k = c->top_k > 0 && c->top_k < V;
+  const int use_p = c->top_p < 1.0;
+  if (!use_k && !use_p) return -INFINITY;
+  double* v = (double*)malloc(sizeof(double) * (size_t)V);
+  for (int j = 0; j < V; ++j) v[j] = widen(c, base, off + j);
+  qsort(v, (size_t)V, sizeof(double), cmp_desc);
+  double tau = -INFINITY;
+  int n = V;  /* entries kept by top-k: a prefix of v */
+  if (use_k) {
+    tau = v[c->top_k - 1];
+    while (n > 0 && v[n - 1] < tau) --n;
+  }
+  if (use_p) {
+    double w_all = 0.0;
+    for (int i = 0; i < n; ++i) w_all += exp((v[i] - m) / c->T);
+    const double target = c->top_p * w_all;
+    double cum = 0.0;
+    int i = 0;
+    while (i < n) {
+      const double val = v[i];
+      const double before = cum;
+      while (i < n && v[i] == val) cum += exp((v[i++] - m) / c->T);
+      if (cum >= target) {
+        if (val > tau) tau = val;
+        if (margin_out) {
+          const double gap = fmin(cum - target, target - before);
+          *margin_out = w_all > 0.0 ? gap / w_all : INFINITY;
+        }
+        break;
+      }
+    }
+  }
+  free(v);
+  return tau;
+}
+
+/* p = softmax(logits / T) in double over the entries with l_j >= tau (the
+ * others get 0; tau = -inf keeps all).  Writes the raw-logit maximum and the
+ * sum S = sum_{kept j} exp((l_j - max)/T).  Returns 0 when every logit is
+ * -inf.  margin_out (optional): the top-p margin of filter_threshold. */
 static int softmax_row(const oracle_ctx* c, const void* base, size_t off,
-                       double* prob, double* m_out, double* s_out) {
+                       double* prob, double* m_out, double* s_out, double* margin_out) {
   const int V = c->V;
   double m = -INFINITY;
   for (int j = 0; j < V; ++j) {
@@ -122,14 +188,16 @@ static int softmax_row(const oracle_ctx* c, const void* base, size_t off,
     if (l > m) m = l;
   }
   if (m_out) *m_out = m;
+  if (margin_out) *margin_out = INFINITY;
   if (m == -INFINITY) {
     if (s_out) *s_out = 0.0;
     return 0;
   }
+  const double tau = filter_threshold(c, base, off, m, margin_out);
   double s = 0.0;
   for (int j = 0; j < V; ++j) {
     double l = widen(c, base, off + j);
-    double e = exp((l - m) / c->T);
+    double e = l >= tau ? exp((l - m) / c->T) : 0.0;
     prob[j] = e;
     s += e;
   }
@@ -184,6 +252,7 @@ typedef struct {
   int32_t* draw_pos;   /* [1] position whose distribution was drawn from (-1: none) */
   int32_t* zero_resid; /* [1] 1 when the residual mass was exactly 0         */
   double* cdf;      /* [V] normalised CDF of the drawn distribution, or NULL */
+  double* fmargin;  /* [1] smallest top-p margin over the rows the walk used */
 } row_diag;
 
 static void write_sentinel(const oracle_ctx* c, int b, int32_t* tok, int32_t* n_out,
@@ -242,11 +311,13 @@ static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t*
   double* w = (double*)malloc(sizeof(double) * (size_t)V);
   int* live_p = (int*)malloc(sizeof(int) * (size_t)(g + 1));
   int* live_q = (int*)malloc(sizeof(int) * (size_t)(g > 0 ? g : 1));
+  double fmargin = INFINITY;  /* smallest top-p margin over the rows */
   for (int i = 0; i <= g; ++i) {
-    double m, s;
-    live_p[i] = softmax_row(c, c->target, row_off(c, b, G + 1, i), P + (size_t)i * V, &m, &s);
+    double m, s, mg;
+    live_p[i] = softmax_row(c, c->target, row_off(c, b, G + 1, i), P + (size_t)i * V, &m, &s, &mg);
     if (d->m) d->m[i] = m;
     if (d->s) d->s[i] = s;
+    fmargin = fmin(fmargin, mg);
   }
   for (int i = 0; i < g; ++i) {
     if (c->mode == OR_POINT) {
@@ -256,11 +327,15 @@ static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t*
       live_q[i] = 1;
       continue;
     }
-    double m, s;
-    live_q[i] = softmax_row(c, c->draft, row_off(c, b, G, i), Q + (size_t)i * V, &m, &s);
+    double m, s, mg;
+    oracle_ctx cq = *c;
+    if (c->fault == OR_FAULT_FILTER_P_ONLY) cq.top_k = 0, cq.top_p = 1.0;
+    live_q[i] = softmax_row(&cq, c->draft, row_off(c, b, G, i), Q + (size_t)i * V, &m, &s, &mg);
     if (d->m) d->m[G + 1 + i] = m;
     if (d->s) d->s[G + 1 + i] = s;
+    fmargin = fmin(fmargin, mg);
   }
+  if (d->fmargin) *d->fmargin = fmargin;
 
   /* Walk left to right.  A row the walk uses (p_i, q_i at a tested
    * position, p_g for the bonus) with no finite logit, or a tested token out
@@ -338,14 +413,19 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
                   int G, int V, double T, int mode, int fault, int threads,
                   int32_t* out_tokens, int32_t* out_n, int32_t* out_len, double* out_px,
                   double* out_qx, double* out_z, double* out_m, double* out_s,
-                  int32_t* out_draw_pos, int32_t* out_zero_resid) {
+                  int32_t* out_draw_pos, int32_t* out_zero_resid, int top_k, double top_p,
+                  double* out_fmargin) {
   if (!target || !tokens || !gamma || !out_tokens || !out_n || !out_len) return -1;
   if (B < 0 || G < 0 || V <= 0) return -2;
   if (dtype != OR_F32 && dtype != OR_BF16) return -3;
   if (mode != OR_SAMPLE && mode != OR_GREEDY && mode != OR_POINT) return -3;
   if (mode == OR_SAMPLE && !draft) return -3;
   if (mode != OR_GREEDY && (!uniforms || !(T > 0.0) || !isfinite(T))) return -3;
-  oracle_ctx c = {target, draft, dtype, tokens, uniforms, gamma, kv_len, B, G, V, T, mode, fault};
+  if (top_k < 0 || !(top_p > 0.0 && top_p <= 1.0)) return -3;
+  /* greedy: filtering keeps the largest logit, so it changes nothing */
+  if (mode == OR_GREEDY) top_k = 0, top_p = 1.0;
+  oracle_ctx c = {target, draft, dtype, tokens, uniforms, gamma, kv_len, B, G, V, T, mode, fault,
+                  top_k, top_p};
   const size_t nr = (size_t)(2 * G + 1);
   if (out_px)
     for (size_t k = 0; k < (size_t)B * G; ++k) out_px[k] = NAN;
@@ -357,6 +437,8 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
     for (size_t k = 0; k < (size_t)B * nr; ++k) out_m[k] = NAN;
   if (out_s)
     for (size_t k = 0; k < (size_t)B * nr; ++k) out_s[k] = NAN;
+  if (out_fmargin)
+    for (int b = 0; b < B; ++b) out_fmargin[b] = INFINITY;
 #ifdef _OPENMP
   if (threads > 0) omp_set_num_threads(threads);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -369,7 +451,8 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
                   out_s ? out_s + (size_t)b * nr : NULL,
                   out_draw_pos ? out_draw_pos + b : NULL,
                   out_zero_resid ? out_zero_resid + b : NULL,
-                  NULL};
+                  NULL,
+                  out_fmargin ? out_fmargin + b : NULL};
     verify_row(&c, b, out_tokens, out_n, out_len, &d);
   }
   (void)threads;
@@ -382,19 +465,38 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
  * data error). */
 int oracle_draw_cdf(const void* target, const void* draft, int dtype, const int32_t* tokens,
                     const float* uniforms, const int32_t* gamma, const int32_t* kv_len, int B,
-                    int G, int V, double T, int mode, int b, double* cdf) {
+                    int G, int V, double T, int mode, int b, double* cdf, int top_k,
+                    double top_p) {
   if (!target || !tokens || !uniforms || !gamma || !cdf) return -1;
   if (mode != OR_SAMPLE && mode != OR_POINT) return -1;
   if (mode == OR_SAMPLE && !draft) return -1;
   if (b < 0 || b >= B) return -1;
+  if (top_k < 0 || !(top_p > 0.0 && top_p <= 1.0)) return -1;
   oracle_ctx c = {target, draft, dtype, tokens, uniforms, gamma, kv_len, B, G, V, T, mode,
-                  OR_FAULT_NONE};
+                  OR_FAULT_NONE, top_k, top_p};
   int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)B * (G + 1));
   int32_t* nn = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
   int32_t* ln = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
   int32_t pos = -1;
-  row_diag d = {NULL, NULL, NULL, NULL, NULL, &pos, NULL, cdf};
+  row_diag d = {NULL, NULL, NULL, NULL, NULL, &pos, NULL, cdf, NULL};
   verify_row(&c, b, tok, nn, ln, &d);
   free(tok), free(nn), free(ln);
   return pos;
+}
+
+/* The filtered distribution of one stored logit row (what a drafter that
+ * applies the same top-k / top-p would sample from): prob[0..V) and the
+ * threshold tau (entries with l >= tau kept).  Returns 0, or -1 for refused
+ * arguments or a row with no finite logit. */
+int oracle_filter_row(const void* logits, int dtype, int V, double T, int top_k, double top_p,
+                      double* prob, double* tau_out) {
+  if (!logits || !prob || V <= 0 || !(T > 0.0) || !isfinite(T)) return -1;
+  if (dtype != OR_F32 && dtype != OR_BF16) return -1;
+  if (top_k < 0 || !(top_p > 0.0 && top_p <= 1.0)) return -1;
+  oracle_ctx c = {logits, NULL, dtype, NULL, NULL, NULL, NULL, 1, 0, V, T, OR_SAMPLE,
+                  OR_FAULT_NONE, top_k, top_p};
+  double m, s;
+  if (!softmax_row(&c, logits, 0, prob, &m, &s, NULL)) return -1;
+  if (tau_out) *tau_out = filter_threshold(&c, logits, 0, m, NULL);
+  return 0;
 }

@@ -368,6 +368,112 @@ def test_point_mode_data_errors_and_gamma0():
                                      for b in range(case.B)]
 
 
+# ---------------------------------------------------------------- top-k / top-p
+def _row_logits(rng, V, dtype, ties=False):
+    x = rng.normal(0, 2.5, size=V).astype(np.float32)
+    if ties:  # repeated values around the middle and at the top
+        x[rng.choice(V, size=V // 4, replace=False)] = np.float32(0.5)
+        x[rng.choice(V, size=3, replace=False)] = x.max()
+    return inputs.store(x, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ties", [False, True])
+def test_filter_top_k_is_the_kth_largest_value(dtype, ties):
+    rng = np.random.default_rng(31)
+    for k in (1, 2, 7, 50, 399):
+        row = _row_logits(rng, 400, dtype, ties)
+        l = inputs.widen(row).astype(np.float64)
+        prob, tau = oracle.filter_row(row, temperature=0.8, top_k=k)
+        kth = np.partition(l, -k)[-k]          # numpy's k-th largest value
+        assert tau == kth
+        kept = l >= kth
+        assert kept.sum() >= k and (l > kth).sum() < k
+        ref = softmax(np.where(kept, l / 0.8, -np.inf))
+        np.testing.assert_allclose(prob, ref, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_filter_top_p_keeps_the_smallest_sufficient_set(dtype):
+    rng = np.random.default_rng(32)
+    for top_p in (1e-9, 0.3, 0.9, 0.999):
+        for ties in (False, True):
+            row = _row_logits(rng, 600, dtype, ties)
+            l = inputs.widen(row).astype(np.float64)
+            prob, tau = oracle.filter_row(row, temperature=1.3, top_p=top_p)
+            full = softmax(l / 1.3)                 # library softmax, unfiltered
+            kept = l >= tau
+            assert full[kept].sum() >= top_p * (1 - 1e-12)
+            # dropping the smallest kept value (all its copies) falls short
+            smaller = l > tau
+            assert full[smaller].sum() < top_p
+            np.testing.assert_allclose(prob, np.where(kept, full, 0) / full[kept].sum(),
+                                       rtol=1e-12, atol=1e-300)
+            if top_p == 1e-9:
+                assert tau == l.max()
+
+
+def test_filter_top_p_applies_to_the_top_k_distribution():
+    rng = np.random.default_rng(33)
+    row = _row_logits(rng, 500, "f32")
+    l = row.astype(np.float64)
+    k, top_p = 40, 0.6
+    _, tau_k = oracle.filter_row(row, top_k=k)
+    prob, tau = oracle.filter_row(row, top_k=k, top_p=top_p)
+    pk = softmax(np.where(l >= tau_k, l, -np.inf))   # renormalised top-k distribution
+    assert tau >= tau_k
+    assert pk[l >= tau].sum() >= top_p and pk[l > tau].sum() < top_p
+
+
+def test_filter_off_is_bit_identical_and_greedy_ignores_it():
+    case = inputs.make_case(2, rnd=14, B=12, V=700)
+    a = oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
+                      case.kv_len, temperature=case.T)
+    b = oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
+                      case.kv_len, temperature=case.T, top_k=700, top_p=1.0)
+    for f in ("tokens", "n_accepted", "px", "qx", "z", "s"):
+        np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
+    assert np.all(np.isinf(b.fmargin))
+    g = inputs.make_case(3, rnd=14, mode="greedy", B=8, V=700)
+    r0 = oracle.verify(g.target, None, g.tokens, None, g.gamma, mode=oracle.GREEDY)
+    r1 = oracle.verify(g.target, None, g.tokens, None, g.gamma, mode=oracle.GREEDY,
+                       top_k=1, top_p=0.01)
+    np.testing.assert_array_equal(r0.tokens, r1.tokens)
+    with pytest.raises(ValueError):
+        oracle.verify(g.target, None, g.tokens, None, g.gamma, mode=oracle.GREEDY, top_k=-1)
+    with pytest.raises(ValueError):
+        oracle.verify(g.target, None, g.tokens, None, g.gamma, mode=oracle.GREEDY, top_p=0.0)
+
+
+@pytest.mark.parametrize("mode", ["sample", "point"])
+def test_filtered_verify_is_the_rule_on_filtered_distributions(mode):
+    """With filtering, the probabilities the walk tests are those of the
+    filtered rows (numpy check), the drawn token has positive filtered weight,
+    and k = 1 reduces sampling to accepting exactly the argmax tokens."""
+    case = inputs.make_case(3, rnd=15, mode=mode, B=24, V=900)
+    m = oracle.POINT if mode == "point" else oracle.SAMPLE
+    k, top_p = 30, 0.8
+    r = oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
+                      case.kv_len, temperature=case.T, mode=m, top_k=k, top_p=top_p)
+    for b in range(case.B):
+        n, g = int(r.n_accepted[b]), int(case.gamma[b])
+        for i in range(min(n + 1, g)):
+            pf, _ = oracle.filter_row(case.target[b, i], temperature=case.T, top_k=k, top_p=top_p)
+            assert r.px[b, i] == pytest.approx(pf[case.tokens[b, i]], rel=1e-12, abs=1e-300)
+            if mode == "sample":
+                qf, _ = oracle.filter_row(case.draft[b, i], temperature=case.T, top_k=k,
+                                          top_p=top_p)
+                assert r.qx[b, i] == pytest.approx(qf[case.tokens[b, i]], rel=1e-12, abs=1e-300)
+        pn, _ = oracle.filter_row(case.target[b, n], temperature=case.T, top_k=k, top_p=top_p)
+        assert pn[r.tokens[b, n]] > 0
+    one = oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
+                        case.kv_len, temperature=case.T, mode=m, top_k=1)
+    for b in range(case.B):
+        n = int(one.n_accepted[b])
+        am = [int(np.argmax(inputs.widen(case.target[b, i]))) for i in range(n + 1)]
+        assert list(one.tokens[b, :n + 1]) == am[: n + 1]
+
+
 # ---------------------------------------------------------------- closed forms
 def _rounds_to(value, printed, digits):
     return round(value, digits) == pytest.approx(printed, abs=1e-9)

@@ -197,6 +197,56 @@ def test_point_planted_mistakes_are_detected(fault):
     assert max(stats + [sa]) > chi2.isf(FAIL_P, 7), (fault, stats, sa)
 
 
+# ---------------------------------------------------------------- filtered sampling
+def _filtered(l, k, top_p):
+    return np.stack([oracle.filter_row(np.ascontiguousarray(r), top_k=k, top_p=top_p)[0]
+                     for r in l])
+
+
+def _run_filtered(lt, ld, rows, k, top_p, fault=oracle.FAULT_NONE, seed=41, chunk=200_000):
+    """Rounds over fixed filtered p' and q'; drafts drawn from q' (the drafter
+    applies the same filter)."""
+    G1, V = lt.shape
+    G = G1 - 1
+    Pf, Qf = _filtered(lt, k, top_p), _filtered(ld, k, top_p)
+    rng = np.random.default_rng(seed)
+    toks, ns = [], []
+    done = 0
+    while done < rows:
+        B = min(chunk, rows - done)
+        x = _draft_tokens(np.broadcast_to(Qf, (B, G, V)), rng.random((B, G)))
+        u = rng.random((B, G + 1)).astype(np.float32)
+        r = oracle.verify(np.broadcast_to(lt, (B, G + 1, V)), np.broadcast_to(ld, (B, G, V)), x, u,
+                          np.full(B, G, np.int32), temperature=1.0, fault=fault, top_k=k,
+                          top_p=top_p)
+        toks.append(r.tokens)
+        ns.append(r.n_accepted)
+        done += B
+    return np.concatenate(toks), np.concatenate(ns), Pf, Qf
+
+
+def test_filtered_sampling_emits_the_filtered_target():
+    """Top-k = 5 and top-p = 0.9 applied to p and q alike at V = 8: the k-th
+    emitted token follows p'_k and the accepted count follows the product of
+    sum min(p', q')."""
+    lt, ld = _fixed_problem(seed=91)
+    tokens, n, Pf, Qf = _run_filtered(lt, ld, 1_000_000, 5, 0.9)
+    assert np.all((Pf > 0).sum(-1) < 8)        # the filter cuts something
+    for k, (stat, df) in enumerate(_position_stats(tokens, n, Pf)):
+        assert stat < chi2.isf(PASS_P, df), (k, stat)
+    (stat, df), _ = _acceptance_stat(n, Pf, Qf)
+    assert stat < chi2.isf(PASS_P, df), stat
+
+
+def test_filtering_only_p_is_detected():
+    lt, ld = _fixed_problem(seed=91)
+    tokens, n, Pf, Qf = _run_filtered(lt, ld, 400_000, 5, 0.9, fault=oracle.FAULT_FILTER_P_ONLY,
+                                      seed=42)
+    stats = [s_ for s_, _ in _position_stats(tokens, n, Pf)]
+    (sa, _), _ = _acceptance_stat(n, Pf, Qf)
+    assert max(stats + [sa]) > chi2.isf(FAIL_P, 7), (stats, sa)
+
+
 # ---------------------------------------------------------------- toy context models
 class Bigram:
     """A context-dependent toy 'model': logits of the next token depend on
