@@ -74,10 +74,12 @@ enum spec_status {
  * sizes spec_verify would reject.
  *
  * The workspace holds one counter per batch row, the softmax statistics of
- * every vocabulary slice and the draw sums of every slice.  It must be
- * zero-filled once before its first use (spec_verify_workspace_reset, or any
- * zero fill).  Every call that completes clears everything it wrote, leaving
- * the workspace all zero again (the diagnostic word aside), so one workspace
+ * every vocabulary slice, the draw sums of every slice and (SAMPLE, POINT)
+ * one filter threshold per vocabulary row.  It must be zero-filled once
+ * before its first use (spec_verify_workspace_reset, or any zero fill).
+ * Every call that completes clears everything it wrote, leaving the
+ * workspace all zero again (the diagnostic word and the thresholds aside:
+ * a filtered call writes all the thresholds it reads), so one workspace
  * serves any sequence of stream-ordered calls, of any shapes, whose
  * spec_verify_workspace_bytes does not exceed its size.  A call that gave up
  * waiting (diagnostic bit 0) may leave it dirty: zero-fill it again. */
@@ -133,6 +135,59 @@ int spec_verify_probe(const void* target_logits, const void* draft_logits,
                       int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_new_len,
                       void* workspace, size_t workspace_bytes, void* stream, float* out_px,
                       float* out_qx, float* out_z, float* out_m, float* out_s);
+
+/* spec_verify with the same top-k / top-p filtering applied to p and q
+ * before the walk (sources: mhtirogla.ai "Implementation notes";
+ * tusharamrit, the caveat after the proof: the draft and the target must
+ * process their logits identically).  For each vocabulary row the verify
+ * uses, with logits l and temperature T:
+ *   top-k (top_k > 0): keep every l_j at or above the k-th largest value of
+ *     the row (ties at that value all kept);
+ *   top-p (top_p < 1): then keep, among those, the smallest set of largest
+ *     values whose mass under softmax(l / T) reaches top_p of the mass kept
+ *     by top-k, all copies of a value together;
+ *   the kept entries are renormalised and the others have probability 0;
+ *   the walk, residual and draw are then those of spec_verify on the
+ *   filtered rows (x_i should come from the filtered q; a token the filter
+ *   cuts from q_i has q_i(x_i) = 0 and is accepted iff p_i(x_i) > 0).
+ * top_k = 0 and top_p = 1 turn a filter off; with both off this is
+ * spec_verify.  GREEDY ignores both (the filters keep the largest logit).
+ * POINT filters p only (there is no q).  Masses are compared in fixed point
+ * (units of 2^-42 of the row's largest weight), so a row whose top-p cut lies
+ * within about 1e-12 of its mass from the boundary may cut one value apart
+ * from an exact computation.  Two launches on `stream`: the thresholds (into
+ * the workspace), then the verify.  Errors: those of spec_verify, and
+ * SPEC_ERR_ARG for top_k < 0 or top_p outside (0, 1]. */
+int spec_verify_filtered(const void* target_logits, const void* draft_logits,
+                         const int32_t* draft_tokens, const float* uniforms,
+                         const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
+                         int gamma_max, int V, int dtype, float temperature, int mode, int top_k,
+                         float top_p, int32_t* out_tokens, int32_t* out_n_accepted,
+                         int32_t* out_new_len, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* spec_verify_filtered plus the probes of spec_verify_probe (of the filtered
+ * rows: out_s holds the filtered S). */
+int spec_verify_filtered_probe(const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_tokens, const float* uniforms,
+                               const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
+                               int gamma_max, int V, int dtype, float temperature, int mode,
+                               int top_k, float top_p, int32_t* out_tokens,
+                               int32_t* out_n_accepted, int32_t* out_new_len, void* workspace,
+                               size_t workspace_bytes, void* stream, float* out_px, float* out_qx,
+                               float* out_z, float* out_m, float* out_s);
+
+/* The thresholds alone: out_thr fp32 [B, 2*gamma_max+1] (device; target rows
+ * 0..gamma_max, then draft rows 0..gamma_max-1), the value tau of each
+ * vocabulary row the walk may use such that the filtered row keeps exactly
+ * the entries with l >= tau; -inf where nothing is cut, for rows beyond
+ * gamma_per_row[b] (and draft rows in POINT mode), and for rows with no
+ * finite logit.  mode: SAMPLE or POINT.  Asynchronous on `stream`; needs no
+ * workspace. */
+int spec_filter_thresholds(const void* target_logits, const void* draft_logits,
+                           const int32_t* gamma_per_row, int B, int gamma_max, int V, int dtype,
+                           float temperature, int mode, int top_k, float top_p, float* out_thr,
+                           void* stream);
 
 /* Launch plan of a call with these sizes (host only).  Each batch row is
  * served by `slices` workgroups; workgroup c owns elements [c * slice_len,

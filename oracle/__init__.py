@@ -54,7 +54,7 @@ def _load():
         lib.oracle_draw_cdf.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, D,
                                         i32, i32, P, i32, D]
         lib.oracle_draw_cdf.restype = i32
-        lib.oracle_filter_row.argtypes = [P, i32, i32, D, i32, D, P, P]
+        lib.oracle_filter_row.argtypes = [P, i32, i32, D, i32, D, P, P, P]
         lib.oracle_filter_row.restype = i32
         _lib = lib
     return _lib
@@ -159,16 +159,19 @@ def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0, mo
     return cdf, int(pos)
 
 
-def filter_row(logits, *, temperature=1.0, top_k=0, top_p=1.0):
+def filter_row(logits, *, temperature=1.0, top_k=0, top_p=1.0, margin=False):
     """The filtered distribution softmax(l/T) restricted to top-k then top-p
-    (float64 [V]) of one stored logit row, and its logit threshold."""
+    (float64 [V]) of one stored logit row, and its logit threshold (and, with
+    margin=True, how far the top-p crossing is from the cut, relative to the
+    kept mass; +inf when top-p cuts nothing)."""
     lib = _load()
     logits = np.ascontiguousarray(logits)
     prob = np.empty(logits.shape[-1], np.float64)
     tau = ctypes.c_double(0.0)
+    mg = ctypes.c_double(0.0)
     rc = lib.oracle_filter_row(_ptr(logits), _dtype_code(logits), logits.shape[-1],
                                float(temperature), int(top_k), float(top_p), _ptr(prob),
-                               ctypes.byref(tau))
+                               ctypes.byref(tau), ctypes.byref(mg))
     if rc != 0:
         raise ValueError("oracle refused the row or its arguments")
-    return prob, tau.value
+    return (prob, tau.value, mg.value) if margin else (prob, tau.value)

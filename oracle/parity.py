@@ -79,10 +79,19 @@ def _close(gpu, ref):
 _MODES = {"sample": oracle.SAMPLE, "greedy": oracle.GREEDY, "point": oracle.POINT}
 
 
+FILTER_MARGIN = 1e-6   # top-p cuts closer than this (relative mass) may differ by one value
+
+
+def _filters(case):
+    return case.extra.get("top_k", 0), case.extra.get("top_p", 1.0)
+
+
 def run_oracle(case, threads=0):
     mode = _MODES[case.mode]
+    k, p = _filters(case)
     return oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
-                         case.kv_len, temperature=case.T, mode=mode, threads=threads)
+                         case.kv_len, temperature=case.T, mode=mode, threads=threads,
+                         top_k=k, top_p=p)
 
 
 def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) -> Report:
@@ -98,10 +107,11 @@ def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) ->
                 rep.mismatched.append((row_offset + b, "greedy differs"))
         return rep
 
+    near_cut = ref.fmargin < FILTER_MARGIN
     if probe is not None:
         g = case.gamma
         for b in range(case.B):
-            if ref.n_accepted[b] < 0:
+            if ref.n_accepted[b] < 0 or near_cut[b]:
                 continue
             for i in range(int(g[b])):
                 if np.isnan(ref.px[b, i]):
@@ -135,7 +145,8 @@ def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) ->
         if same:
             continue
         rep.mismatched.append((row_offset + b, "sample differs"))
-        why = _attribute(case, b, int(n_acc[b]), tokens[b], ref)
+        why = (f"top-p cut within {ref.fmargin[b]:.1e} of the boundary" if near_cut[b]
+               else _attribute(case, b, int(n_acc[b]), tokens[b], ref))
         if why:
             rep.attributed.append((row_offset + b, why))
     return rep
@@ -157,8 +168,9 @@ def _attribute(case, b, n_gpu, tok_gpu, ref):
     jg, jo = int(tok_gpu[n_or]), int(ref.tokens[b, n_or])
     if not (0 <= jg < case.V):
         return None
+    k, p = _filters(case)
     cdf, pos = oracle.draw_cdf(case.target, case.draft, case.tokens, case.uniforms, case.gamma, b,
-                               temperature=case.T, mode=_MODES[case.mode])
+                               temperature=case.T, mode=_MODES[case.mode], top_k=k, top_p=p)
     if pos != n_or:
         return None
     us = u[n_or + 1] if n_or < case.gamma[b] else u[int(case.gamma[b])]

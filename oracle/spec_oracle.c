@@ -489,14 +489,14 @@ int oracle_draw_cdf(const void* target, const void* draft, int dtype, const int3
  * threshold tau (entries with l >= tau kept).  Returns 0, or -1 for refused
  * arguments or a row with no finite logit. */
 int oracle_filter_row(const void* logits, int dtype, int V, double T, int top_k, double top_p,
-                      double* prob, double* tau_out) {
+                      double* prob, double* tau_out, double* margin_out) {
   if (!logits || !prob || V <= 0 || !(T > 0.0) || !isfinite(T)) return -1;
   if (dtype != OR_F32 && dtype != OR_BF16) return -1;
   if (top_k < 0 || !(top_p > 0.0 && top_p <= 1.0)) return -1;
   oracle_ctx c = {logits, NULL, dtype, NULL, NULL, NULL, NULL, 1, 0, V, T, OR_SAMPLE,
                   OR_FAULT_NONE, top_k, top_p};
   double m, s;
-  if (!softmax_row(&c, logits, 0, prob, &m, &s, NULL)) return -1;
+  if (!softmax_row(&c, logits, 0, prob, &m, &s, margin_out)) return -1;
   if (tau_out) *tau_out = filter_threshold(&c, logits, 0, m, NULL);
   return 0;
 }

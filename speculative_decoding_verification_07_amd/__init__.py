@@ -20,7 +20,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ARG, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = 0, -1, -2,
 GAMMA_MAX_LIMIT = 63
 
 EXPORTS = (
-    "spec_verify", "spec_verify_probe", "spec_verify_workspace_bytes",
+    "spec_verify", "spec_verify_probe", "spec_verify_filtered", "spec_verify_filtered_probe",
+    "spec_filter_thresholds", "spec_verify_workspace_bytes",
     "spec_verify_workspace_reset", "spec_verify_plan", "spec_verify_tune",
     "spec_verify_diagnostics", "spec_verify_strerror", "spec_verify_version",
     "spec_probe_read", "spec_probe_read_blocks", "spec_probe_copy",
@@ -49,6 +50,13 @@ def load():
     lib.spec_verify.restype = i32
     lib.spec_verify_probe.argtypes = verify_args + [P, P, P, P, P]
     lib.spec_verify_probe.restype = i32
+    filtered_args = verify_args[:12] + [i32, f32] + verify_args[12:]
+    lib.spec_verify_filtered.argtypes = filtered_args
+    lib.spec_verify_filtered.restype = i32
+    lib.spec_verify_filtered_probe.argtypes = filtered_args + [P, P, P, P, P]
+    lib.spec_verify_filtered_probe.restype = i32
+    lib.spec_filter_thresholds.argtypes = [P, P, P, i32, i32, i32, i32, f32, i32, i32, f32, P, P]
+    lib.spec_filter_thresholds.restype = i32
     lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.spec_verify_workspace_bytes.restype = sz
     lib.spec_verify_workspace_reset.argtypes = [P, sz, P]
@@ -175,10 +183,15 @@ def _shape_check(target, draft, tokens, uniforms, gamma, kv_len, mode):
     return B, G, V
 
 
+def _filtering(top_k, top_p) -> bool:
+    return top_k != 0 or top_p != 1.0
+
+
 def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in=None,
            *, temperature: float = 1.0, mode: int = SAMPLE, workspace: Workspace | None = None,
-           out=None, stream=None, probe: bool = False):
-    """Run spec_verify on torch device tensors.
+           out=None, stream=None, probe: bool = False, top_k: int = 0, top_p: float = 1.0):
+    """Run spec_verify (spec_verify_filtered when top_k or top_p filter) on
+    torch device tensors.
 
     Returns (tokens [B, G+1] int32, n_accepted [B] int32, new_len [B] int32),
     plus a dict of probe tensors (px, qx, z, m, s) when probe=True.  `out`
@@ -198,12 +211,17 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, k
                torch.empty(B, dtype=torch.int32, device=dev),
                torch.empty(B, dtype=torch.int32, device=dev))
     tok, nacc, nlen = out
-    args = [_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
-            _ptr(gamma_per_row), _ptr(kv_len_in), B, G, V, dt, float(temperature), int(mode),
-            _ptr(tok), _ptr(nacc), _ptr(nlen), ctypes.c_void_p(workspace.ptr),
+    filt = _filtering(top_k, top_p)
+    head = [_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
+            _ptr(gamma_per_row), _ptr(kv_len_in), B, G, V, dt, float(temperature), int(mode)]
+    tail = [_ptr(tok), _ptr(nacc), _ptr(nlen), ctypes.c_void_p(workspace.ptr),
             workspace.nbytes, _stream_handle(stream)]
+    args = head + ([int(top_k), float(top_p)] if filt else []) + tail
     if not probe:
-        _check(lib.spec_verify(*args), "spec_verify")
+        if filt:
+            _check(lib.spec_verify_filtered(*args), "spec_verify_filtered")
+        else:
+            _check(lib.spec_verify(*args), "spec_verify")
         return tok, nacc, nlen
     nan = float("nan")
     pr = {
@@ -213,9 +231,27 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, k
         "m": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
         "s": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
     }
-    _check(lib.spec_verify_probe(*args, _ptr(pr["px"]), _ptr(pr["qx"]), _ptr(pr["z"]),
-                                 _ptr(pr["m"]), _ptr(pr["s"])), "spec_verify_probe")
+    fn = lib.spec_verify_filtered_probe if filt else lib.spec_verify_probe
+    _check(fn(*args, _ptr(pr["px"]), _ptr(pr["qx"]), _ptr(pr["z"]), _ptr(pr["m"]),
+              _ptr(pr["s"])), "spec_verify_probe")
     return tok, nacc, nlen, pr
+
+
+def filter_thresholds(target_logits, draft_logits, gamma_per_row, *, temperature: float = 1.0,
+                      mode: int = SAMPLE, top_k: int = 0, top_p: float = 1.0, out=None,
+                      stream=None):
+    """spec_filter_thresholds: fp32 [B, 2G+1] device tensor of per-row
+    thresholds (-inf where nothing is cut)."""
+    torch = _torch()
+    B, G, V = _shape_check(target_logits, draft_logits, None, None, gamma_per_row, None, mode)
+    if out is None:
+        out = torch.empty((B, 2 * G + 1), dtype=torch.float32, device=target_logits.device)
+    _check(load().spec_filter_thresholds(_ptr(target_logits), _ptr(draft_logits),
+                                         _ptr(gamma_per_row), B, G, V,
+                                         _dtype_code(target_logits), float(temperature),
+                                         int(mode), int(top_k), float(top_p), _ptr(out),
+                                         _stream_handle(stream)), "spec_filter_thresholds")
+    return out
 
 
 class Prepared:
@@ -227,7 +263,7 @@ class Prepared:
 
     def __init__(self, target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row,
                  kv_len_in=None, *, temperature: float = 1.0, mode: int = SAMPLE,
-                 workspace: Workspace, out, stream=None):
+                 workspace: Workspace, out, stream=None, top_k: int = 0, top_p: float = 1.0):
         B, G, V = _shape_check(target_logits, draft_logits, draft_tokens, uniforms,
                                gamma_per_row, kv_len_in, mode)
         dt = _dtype_code(target_logits)
@@ -236,11 +272,14 @@ class Prepared:
         self._keep = (target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row,
                       kv_len_in, workspace, out)
         tok, nacc, nlen = out
-        self._fn = load().spec_verify
-        self._args = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
-                      _ptr(uniforms), _ptr(gamma_per_row), _ptr(kv_len_in), B, G, V, dt,
-                      ctypes.c_float(temperature), int(mode), _ptr(tok), _ptr(nacc), _ptr(nlen),
-                      ctypes.c_void_p(workspace.ptr), workspace.nbytes, _stream_handle(stream))
+        filt = _filtering(top_k, top_p)
+        self._fn = load().spec_verify_filtered if filt else load().spec_verify
+        self._args = ((_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
+                       _ptr(uniforms), _ptr(gamma_per_row), _ptr(kv_len_in), B, G, V, dt,
+                       ctypes.c_float(temperature), int(mode))
+                      + ((int(top_k), ctypes.c_float(top_p)) if filt else ())
+                      + (_ptr(tok), _ptr(nacc), _ptr(nlen), ctypes.c_void_p(workspace.ptr),
+                         workspace.nbytes, _stream_handle(stream)))
 
     def __call__(self):
         rc = self._fn(*self._args)

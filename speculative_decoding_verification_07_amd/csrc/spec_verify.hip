@@ -72,7 +72,7 @@ struct Plan {
   int CL, NC;  // slice length (elements), slices per vocabulary row
   int NR;      // vocabulary rows per batch row at gamma_max
   int64_t total;
-  size_t off_ctr, off_part, off_wsum, bytes;
+  size_t off_ctr, off_part, off_wsum, off_thr, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -117,6 +117,8 @@ int make_plan(int B, int G, int V, int dtype, int mode, Plan* p) {
   p->off_part = off; off = align256(off + sizeof(uint64_t) * (size_t)B * p->NC * p->NR);
   p->off_wsum = off;
   if (draws) off = align256(off + sizeof(uint64_t) * 2 * (size_t)B * p->NC);
+  p->off_thr = off;  // filter thresholds, written by the filtered calls only
+  if (draws) off = align256(off + sizeof(float) * (size_t)B * (2 * G + 1));
   p->bytes = off;
   return SPEC_OK;
 }
@@ -141,6 +143,7 @@ struct Args {
   unsigned* ctr;   // [B][kRowWords]
   uint64_t* part;  // [B][NC][NR] pairs of each slice: (m, S) or (max, argmax + 1)
   uint64_t* wsum;  // [B][2][NC] draw weight sums of each slice (two attempts)
+  const float* thr;  // [B][2G+1] filter thresholds (entries below are cut), or null
   int B, G, V, NC, CL, NR;
   float k2;        // log2(e) / T
   unsigned max_spin;
@@ -334,6 +337,32 @@ __device__ __forceinline__ void knock_out(Slice<DT, R>& s, const Geom& g, int re
   }
 }
 
+// Sets every element of the slice below tau to -inf (the filter's cut), in
+// registers.
+template <int DT, int R>
+__device__ __forceinline__ void mask_slice(Slice<DT, R>& s, float tau) {
+  auto cut = [&](float x) { return x >= tau ? x : NEG_INF; };
+  s.hd = cut(s.hd);
+  s.tl = cut(s.tl);
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    uint32_t* wd = &s.v[k].x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = (&s.v[k].x)[q];
+      uint32_t o;
+      if (DT == SPEC_DTYPE_F32) {
+        o = __float_as_uint(cut(__uint_as_float(w)));
+      } else {
+        const uint32_t lo = __float_as_uint(cut(__uint_as_float(w << 16))) >> 16;
+        const uint32_t hi = __float_as_uint(cut(__uint_as_float(w & 0xffff0000u))) & 0xffff0000u;
+        o = hi | lo;
+      }
+      wd[q] = o;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ reductions
 // Softmax statistics are kept in the scaled domain z = l * k2 (k2 = log2(e)/T):
 // a pair (m, S) has m = the largest raw logit and S = sum_j 2^(l_j k2 - R(m)),
@@ -481,6 +510,26 @@ __device__ __forceinline__ double wave_scan_d(double x, double& excl) {
   return x;
 }
 
+// The same prefix scan on unsigned 64-bit integers (exact, so the order of
+// the additions does not matter).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xf, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t x, uint64_t& excl) {
+  x += dpp_u64<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_u64<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_u64<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_u64<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_u64<0x142, 0xa>(x);  // row_bcast:15
+  x += dpp_u64<0x143, 0xc>(x);  // row_bcast:31
+  excl = dpp_u64<0x138, 0xf>(x);  // wave_shr:1
+  return x;
+}
+
 // (max, lowest index of the max) of this thread's share; lo = the slice's
 // first index.  Only present elements count, so a slice of -inf yields its
 // lowest present index.
@@ -585,6 +634,7 @@ struct Owner {
 struct Lds {
   float wm[kMaxRows][kWaves];  // per-row wave partials: m (greedy: max)
   float ws[kMaxRows][kWaves];  // S (greedy: argmax bits)
+  float tau[kMaxRows];         // filter threshold of each vocabulary row (filtered calls)
   float M[kMaxRows];           // merged row statistics, row r = target i (r = i)
   float S[kMaxRows];           //   or draft i (r = g + 1 + i); greedy: argmax bits
   uint64_t stage[kStage];
@@ -640,19 +690,23 @@ __device__ void block_scan_d(double v, Lds& L, double& incl, double& excl, doubl
 }
 
 // Lowest (highest) thread index whose predicate holds, or -1.
-__device__ int block_first(bool pred, Lds& L) {
+// (kW waves per workgroup; mask: kW words of LDS.)
+template <int kW>
+__device__ int block_first_m(bool pred, unsigned long long* mask) {
   const unsigned long long m = __ballot(pred);
-  if ((threadIdx.x & 63) == 0) L.mask[threadIdx.x >> 6] = m;
+  if ((threadIdx.x & 63) == 0) mask[threadIdx.x >> 6] = m;
   __syncthreads();
   int r = -1;
-  for (int k = 0; k < kWaves; ++k)
-    if (L.mask[k]) {
-      r = k * 64 + __ffsll((long long)L.mask[k]) - 1;
+  for (int k = 0; k < kW; ++k)
+    if (mask[k]) {
+      r = k * 64 + __ffsll((long long)mask[k]) - 1;
       break;
     }
   __syncthreads();
   return r;
 }
+
+__device__ int block_first(bool pred, Lds& L) { return block_first_m<kWaves>(pred, L.mask); }
 
 __device__ int block_last(bool pred, Lds& L) {
   const unsigned long long m = __ballot(pred);
@@ -685,9 +739,11 @@ __device__ __forceinline__ int probe_slot(const Args& a, int g, int r) {
 // (m, S) of a wave's share of a slice, in every lane: the wave's largest
 // logit first, then one sum against it (no rescaling), four partial sums for
 // instruction-level parallelism, then the wave sum.
-template <int DT, int R>
+// FILT: entries below tau are cut (they weigh 0; the raw maximum, which a
+// filter always keeps, is unchanged).
+template <int DT, int R, bool FILT>
 __device__ __forceinline__ void wave_slice_ms(const Slice<DT, R>& s, const Geom& g, float k2,
-                                              float& m, float& S) {
+                                              float tau, float& m, float& S) {
   using E = Elt<DT>;
   float mx = fmaxf(s.hd, s.tl);
 #pragma unroll
@@ -701,14 +757,15 @@ __device__ __forceinline__ void wave_slice_ms(const Slice<DT, R>& s, const Geom&
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (mx != NEG_INF) {  // uniform across the wave
     const float Rf = ref_of(mx, k2);
-    acc[0] = ex2(fmaf(s.hd, k2, -Rf));
-    acc[1] = ex2(fmaf(s.tl, k2, -Rf));
+    auto cut = [&](float x) { return FILT && !(x >= tau) ? NEG_INF : x; };
+    acc[0] = ex2(fmaf(cut(s.hd), k2, -Rf));
+    acc[1] = ex2(fmaf(cut(s.tl), k2, -Rf));
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       float f[E::kVec];
       E::unpack(vget(s, k, g), f);
 #pragma unroll
-      for (int e = 0; e < E::kVec; ++e) acc[e & 3] += ex2(fmaf(f[e], k2, -Rf));
+      for (int e = 0; e < E::kVec; ++e) acc[e & 3] += ex2(fmaf(cut(f[e]), k2, -Rf));
     }
   }
   m = mx;
@@ -750,12 +807,17 @@ struct Ring {
 // ring is indexed at compile time (the row loop is unrolled by NB) and the
 // loads are unconditional -- past the last row they re-read it -- so the
 // waits stay counted exactly.
-template <int DT, int MODE, int R, bool AL>
+template <int DT, int MODE, int R, bool AL, bool FILT>
 __device__ __forceinline__ void stream_rows(const Args& a, Lds& L, int b, int g, int nrows, int lo, int len,
                             Ring<DT, R>& ring) {
   constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // softmax statistics
   constexpr int NB = Ring<DT, R>::NB;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  if (FILT) {
+    for (int r = t; r < nrows; r += kThreads)
+      L.tau[r] = a.thr[(int64_t)b * (2 * a.G + 1) + probe_slot(a, g, r)];
+    __syncthreads();
+  }
   Slice<DT, R> buf[NB];
   Geom geo[NB];
   // past the end, when sampling, a slot loads the row it already holds
@@ -784,7 +846,8 @@ __device__ __forceinline__ void stream_rows(const Args& a, Lds& L, int b, int g,
       issue(r + NB - 1, buf[(j + NB - 1) % NB], geo[(j + NB - 1) % NB]);
       if (kSample) {
         float m, sm;
-        wave_slice_ms<DT, R>(buf[j], geo[j], a.k2, m, sm);
+        const float tau = FILT ? L.tau[stream_row<MODE>(r < nrows ? r : nrows - 1, g)] : NEG_INF;
+        wave_slice_ms<DT, R, FILT>(buf[j], geo[j], a.k2, tau, m, sm);
         if (lane == 0 && r < nrows) {
           const int rr = stream_row<MODE>(r, g);
           L.wm[rr][w] = m, L.ws[rr][w] = sm;
@@ -928,12 +991,17 @@ __device__ Gathered gather_small(const Args& a, int b, int g) {
 
 // t[x_i] and (sampling) d[x_i]: issued once the row loads are done (they
 // depend on x_i, and waiting for them earlier would hold up the streaming).
-template <int DT, int MODE>
+template <int DT, int MODE, bool FILT>
 __device__ void gather_logits(const Args& a, int b, int g, Gathered& r) {
   const int lane = threadIdx.x;
   if (threadIdx.x < 64 && lane < g && (unsigned)r.x < (unsigned)a.V) {
     r.tv = Elt<DT>::one(row_of<DT>(a, b, g, lane), r.x);
     if (MODE == SPEC_MODE_SAMPLE) r.dv = Elt<DT>::one(row_of<DT>(a, b, g, g + 1 + lane), r.x);
+    if (FILT) {  // a token the filter cuts has probability 0
+      const float* th = a.thr + (int64_t)b * (2 * a.G + 1);
+      if (!(r.tv >= th[lane])) r.tv = NEG_INF;
+      if (MODE == SPEC_MODE_SAMPLE && !(r.dv >= th[a.G + 1 + lane])) r.dv = NEG_INF;
+    }
   }
 }
 
@@ -1249,7 +1317,7 @@ __device__ __forceinline__ void ring_pick(const Ring<DT, R>& ring, int k, Slice<
   }
 }
 
-template <int DT, int R, bool RESID, bool KNOCK, bool RING, bool AL>
+template <int DT, int R, bool RESID, bool KNOCK, bool RING, bool FILT, bool AL>
 __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
                      const Decision& dc, const Ring<DT, R>& ring) {
   using E = Elt<DT>;
@@ -1294,6 +1362,11 @@ __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g,
     }
   } else {
     sd = st;
+  }
+  if (FILT) {  // the filtered rows: cut entries weigh 0
+    const float* th = a.thr + (int64_t)b * (2 * a.G + 1);
+    mask_slice(st, th[n]);
+    if (RESID) mask_slice(sd, th[a.G + 1 + n]);
   }
   if (KNOCK) knock_out(st, gt, dc.xn - lo);
   uint64_t* ws = a.wsum + (int64_t)b * 2 * a.NC;
@@ -1391,7 +1464,7 @@ __device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
 #ifndef SPEC_MIN_WAVES
 #define SPEC_MIN_WAVES 4
 #endif
-template <int DT, int MODE, int R, bool AL>
+template <int DT, int MODE, int R, bool AL, bool FILT>
 __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a) {
   constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // a drawn token (sample, point)
   using E = Elt<DT>;
@@ -1409,9 +1482,9 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
 
   Gathered in = gather_small<MODE>(a, b, g);
   Ring<DT, R> ring;
-  stream_rows<DT, MODE, R, AL>(a, L, b, g, nrows, lo, len, ring);
+  stream_rows<DT, MODE, R, AL, FILT>(a, L, b, g, nrows, lo, len, ring);
   publish_pairs<kSample>(a, L, b, c, nrows);
-  if (kSample) gather_logits<DT, MODE>(a, b, g, in);  // in flight during the wait
+  if (kSample) gather_logits<DT, MODE, FILT>(a, b, g, in);  // in flight during the wait
 
   if (!kSample) {
     // greedy: slice 0 waits for the group's pairs, decides, writes the row
@@ -1431,17 +1504,236 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   if (!dc.dead) {
     constexpr bool kRing = MODE == SPEC_MODE_SAMPLE;
     if (dc.resid && MODE == SPEC_MODE_POINT)
-      draw<DT, R, false, true, false, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, false, true, false, FILT, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
     else if (dc.resid)
-      draw<DT, R, true, false, kRing, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, true, false, kRing, FILT, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
     else
-      draw<DT, R, false, false, kRing, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, false, false, kRing, FILT, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
   } else {
     row_exit(a, L, b, nrows);
   }
 }
 
+// ------------------------------------------------------------------ filtering
+// Top-k / top-p thresholds (the same processing for p and q: "Speculative
+// decoding", mhtirogla.ai, "Implementation notes"; tusharamrit, the caveat
+// after the proof).  One workgroup per vocabulary row finds tau such that the
+// filtered row keeps exactly the entries with l >= tau:
+//   top-k: tau_k = the k-th largest value (ties kept);
+//   top-p: among the entries kept by top-k, the largest value tau_p such that
+//          the entries at or above it carry at least top_p of their mass
+//          under softmax(l / T) (all copies of a value together).
+// Values are ordered through sortable keys (the float's bits with the sign
+// bit flipped, all bits flipped when negative; larger value, larger key) and
+// selected by most significant digits, one histogram per level over the
+// entries that match the digits chosen so far: 12 bits, then 4 for bf16
+// (whose keys carry nothing below bit 16) or 12 and 8 for fp32.  Masses are
+// 2^fma(l, k2, -R(max)) (the weights of the verify) in fixed point, units of
+// 2^-42, so their sums are exact integers whatever the order of the additions.
+constexpr int kFThreads = 256;
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kFBins = 4096;
+constexpr double kMassUnit = 4398046511104.0;  // 2^42
+
+struct FArgs {
+  const void* tgt;
+  const void* dft;
+  const int32_t* gam;
+  float* thr;  // [B][2G+1]: target rows 0..G, then draft rows 0..G-1
+  int B, G, V, NR2, top_k;  // NR2 = 2G+1 slots per batch row
+  int drafts;               // 1: draft rows are filtered (sampling), 0: -inf there
+  float k2, top_p;
+};
+
+struct FLds {
+  unsigned long long h[kFBins];
+  unsigned long long red[kFWaves];
+  unsigned long long mask[kFWaves];
+  float fmax[kFWaves];
+  int pick;
+  unsigned long long above;
+};
+
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float funkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Digit levels: shift and width of level lv.
+template <int DT>
+struct FLevels {
+  static constexpr int N = DT == SPEC_DTYPE_BF16 ? 2 : 3;
+  __device__ static int shift(int lv) {
+    return DT == SPEC_DTYPE_BF16 ? (lv == 0 ? 20 : 16) : (lv == 0 ? 20 : lv == 1 ? 8 : 0);
+  }
+  __device__ static int bits(int lv) {
+    return DT == SPEC_DTYPE_BF16 ? (lv == 0 ? 12 : 4) : (lv == 2 ? 8 : 12);
+  }
+};
+
+__device__ float fblock_max(float v, FLds& L) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) L.fmax[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = L.fmax[0];
+  for (int k = 1; k < kFWaves; ++k) m = fmaxf(m, L.fmax[k]);
+  __syncthreads();
+  return m;
+}
+
+// Inclusive / exclusive prefix sums over the workgroup's threads and the
+// total (unsigned 64-bit, exact).
+__device__ void fblock_scan(uint64_t v, FLds& L, uint64_t& incl, uint64_t& excl, uint64_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint64_t prev;
+  const uint64_t x = wave_scan_u64(v, prev);
+  if (lane == 63) L.red[w] = x;
+  __syncthreads();
+  uint64_t off = 0, tot = 0;
+  for (int k = 0; k < kFWaves; ++k) {
+    if (k < w) off += L.red[k];
+    tot += L.red[k];
+  }
+  incl = off + x;
+  excl = off + prev;
+  total = tot;
+  __syncthreads();
+}
+
+// Walking the digits of L.h[0..nb) from the largest down, the first digit at
+// which the running sum reaches `need`; `above` = the sum of the digits above
+// it, `total` = the sum of all.  need <= total is the caller's guarantee; if
+// it did not hold, the lowest non-empty digit is returned.
+__device__ int find_cross(FLds& L, int nb, uint64_t need, uint64_t& above, uint64_t& total) {
+  const int t = threadIdx.x;
+  const int per = nb > kFThreads ? nb / kFThreads : 1;
+  const int top = nb - 1 - t * per;  // this thread's digits: top, top-1, ..., top-per+1
+  uint64_t s = 0;
+  for (int i = 0; i < per; ++i)
+    if (top - i >= 0) s += L.h[top - i];
+  uint64_t incl, excl;
+  fblock_scan(s, L, incl, excl, total);
+  int th = block_first_m<kFWaves>(s > 0 && incl >= need, L.mask);
+  const bool fallback = th < 0;
+  if (fallback) {
+    // (cannot happen with need <= total) the last thread holding weight
+    const unsigned long long m = __ballot(s > 0);
+    if ((t & 63) == 0) L.mask[t >> 6] = m;
+    __syncthreads();
+    for (int k = kFWaves - 1; k >= 0; --k)
+      if (L.mask[k]) {
+        th = k * 64 + 63 - __clzll((long long)L.mask[k]);
+        break;
+      }
+    __syncthreads();
+  }
+  if (t == th) {
+    uint64_t c = excl;
+    int d = -1;
+    uint64_t at = 0;
+    for (int i = 0; i < per && top - i >= 0; ++i) {
+      const uint64_t hv = L.h[top - i];
+      if (hv == 0) continue;
+      if (fallback || c + hv >= need) {
+        d = top - i;
+        at = c;
+        if (!fallback) break;
+      }
+      c += hv;
+    }
+    L.pick = d;
+    L.above = at;
+  }
+  __syncthreads();
+  const int d = L.pick;
+  above = L.above;
+  __syncthreads();
+  return d;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
+  using E = Elt<DT>;
+  using Lv = FLevels<DT>;
+  __shared__ FLds L;
+  const int t = threadIdx.x;
+  const int b = (int)(blockIdx.x / (unsigned)a.NR2), slot = (int)(blockIdx.x % (unsigned)a.NR2);
+  const int g = a.gam[b];
+  float* out = a.thr + (int64_t)b * (2 * a.G + 1) + slot;
+  const bool is_t = slot <= a.G;
+  const bool used =
+      g >= 0 && g <= a.G && (is_t ? slot <= g : (a.drafts && slot - a.G - 1 < g));
+  if (!used) {
+    if (t == 0) *out = NEG_INF;
+    return;
+  }
+  const char* row = is_t ? (const char*)a.tgt + ((int64_t)b * (a.G + 1) + slot) * a.V * E::kBytes
+                         : (const char*)a.dft + ((int64_t)b * a.G + (slot - a.G - 1)) * a.V * E::kBytes;
+  float mx = NEG_INF;
+  for (int j = t; j < a.V; j += kFThreads) mx = fmaxf(mx, E::one(row, j));
+  mx = fblock_max(mx, L);
+  if (mx == NEG_INF) {  // a dead row: the walk reports it
+    if (t == 0) *out = NEG_INF;
+    return;
+  }
+  const bool use_k = a.top_k > 0 && a.top_k < a.V;
+  const bool use_p = a.top_p < 1.f;
+  // radix selection: `mass` weighs each entry by its fixed-point mass, else 1;
+  // only entries with key >= floor_key take part
+  auto select = [&](bool mass, uint64_t need, uint32_t floor_key) -> uint32_t {
+    const float R = ref_of(mx, a.k2);
+    uint32_t prefix = 0, pmask = 0;
+    for (int lv = 0; lv < Lv::N; ++lv) {
+      const int sh = Lv::shift(lv), nb = 1 << Lv::bits(lv);
+      for (int i = t; i < nb; i += kFThreads) L.h[i] = 0;
+      __syncthreads();
+      for (int j = t; j < a.V; j += kFThreads) {
+        const float l = E::one(row, j);
+        const uint32_t k = fkey(l);
+        if (k >= floor_key && (k & pmask) == prefix) {
+          const unsigned long long w =
+              mass ? (unsigned long long)((double)ex2(fmaf(l, a.k2, -R)) * kMassUnit) : 1ull;
+          if (w) atomicAdd(&L.h[(k >> sh) & (nb - 1)], w);
+        }
+      }
+      __syncthreads();
+      uint64_t above, total;
+      if (mass && lv == 0) {
+        // the target: top_p of the mass kept so far, rounded up to a unit
+        uint64_t sum = 0, incl, excl;
+        for (int i = t; i < nb; i += kFThreads) sum += L.h[i];
+        fblock_scan(sum, L, incl, excl, total);
+        need = (uint64_t)ceil((double)a.top_p * (double)total);
+        if (need < 1) need = 1;
+        if (need > total) need = total;
+      }
+      const int d = find_cross(L, nb, need, above, total);
+      need -= above;
+      prefix |= (uint32_t)d << sh;
+      pmask |= (uint32_t)(nb - 1) << sh;
+    }
+    return prefix;
+  };
+  uint32_t key = 0;
+  if (use_k) key = select(false, (uint64_t)a.top_k, 0u);
+  if (use_p) {
+    const uint32_t kp = select(true, 0, key);
+    key = kp > key ? kp : key;
+  }
+  // a bf16 key's low 16 bits: zero for positive values, all ones for negative
+  if (DT == SPEC_DTYPE_BF16) key |= (key & 0x80000000u) ? 0u : 0xffffu;
+  if (t == 0) *out = (use_k || use_p) ? funkey(key) : NEG_INF;
+}
+
 // ------------------------------------------------------------------ probes
+__global__ __launch_bounds__(kThreads) void fill_ninf_kernel(float* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) p[i] = NEG_INF;
+}
+
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail,
                                                              int ntail) {
   size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
@@ -1484,33 +1776,70 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP -
 
 bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
-template <int DT, int MODE, bool AL>
+template <int DT, int MODE, bool AL, bool FILT>
 void launch_r(int R, dim3 grid, hipStream_t s, const Args& a) {
   if (R == 1)
-    hipLaunchKernelGGL((verify_kernel<DT, MODE, 1, AL>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 1, AL, FILT>), grid, dim3(kThreads), 0, s, a);
   else if (R == 2)
-    hipLaunchKernelGGL((verify_kernel<DT, MODE, 2, AL>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 2, AL, FILT>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL, FILT>), grid, dim3(kThreads), 0, s, a);
 }
 
+// greedy never filters (the filters keep the largest logit)
 template <int DT, int MODE>
-void launch(int R, bool al, dim3 grid, hipStream_t s, const Args& a) {
-  if (al)
-    launch_r<DT, MODE, true>(R, grid, s, a);
+void launch(int R, bool al, bool filt, dim3 grid, hipStream_t s, const Args& a) {
+  constexpr bool kCanFilter = MODE != SPEC_MODE_GREEDY;
+  if (kCanFilter && filt) {
+    if (al)
+      launch_r<DT, MODE, true, kCanFilter>(R, grid, s, a);
+    else
+      launch_r<DT, MODE, false, kCanFilter>(R, grid, s, a);
+  } else {
+    if (al)
+      launch_r<DT, MODE, true, false>(R, grid, s, a);
+    else
+      launch_r<DT, MODE, false, false>(R, grid, s, a);
+  }
+}
+
+bool filter_args_ok(int top_k, float top_p) { return top_k >= 0 && top_p > 0.f && top_p <= 1.f; }
+
+// Whether a call filters at all (greedy never does: the filters keep the
+// largest logit).
+bool filters(int mode, int V, int top_k, float top_p) {
+  return mode != SPEC_MODE_GREEDY && ((top_k > 0 && top_k < V) || top_p < 1.f);
+}
+
+void launch_filter(const FArgs& f, int dtype, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)f.B * f.NR2));
+  if (dtype == SPEC_DTYPE_BF16)
+    hipLaunchKernelGGL((filter_kernel<SPEC_DTYPE_BF16>), grid, dim3(kFThreads), 0, s, f);
   else
-    launch_r<DT, MODE, false>(R, grid, s, a);
+    hipLaunchKernelGGL((filter_kernel<SPEC_DTYPE_F32>), grid, dim3(kFThreads), 0, s, f);
+}
+
+FArgs filter_args(const void* tgt, const void* dft, const int32_t* gam, float* thr, int B, int G,
+                  int V, float T, int mode, int top_k, float top_p) {
+  FArgs f;
+  f.tgt = tgt, f.dft = dft ? dft : tgt, f.gam = gam, f.thr = thr;
+  f.B = B, f.G = G, f.V = V, f.NR2 = 2 * G + 1, f.drafts = mode == SPEC_MODE_SAMPLE;
+  f.top_k = top_k, f.top_p = top_p;
+  f.k2 = (float)(1.4426950408889634 / (double)T);
+  return f;
 }
 
 int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const int32_t* gam,
-        const int32_t* kv, int B, int G, int V, int dtype, float T, int mode, int32_t* out_tok,
-        int32_t* out_n, int32_t* out_len, void* ws, size_t ws_bytes, void* stream, float* px,
-        float* qx, float* pz, float* pm, float* ps) {
+        const int32_t* kv, int B, int G, int V, int dtype, float T, int mode, int top_k,
+        float top_p, int32_t* out_tok, int32_t* out_n, int32_t* out_len, void* ws,
+        size_t ws_bytes, void* stream, float* px, float* qx, float* pz, float* pm, float* ps) {
   Plan p;
   int st = make_plan(B, G, V, dtype, mode, &p);
   if (st != SPEC_OK) return st;
+  if (!filter_args_ok(top_k, top_p)) return SPEC_ERR_ARG;
   const bool sample = mode == SPEC_MODE_SAMPLE;
   const bool draws = mode != SPEC_MODE_GREEDY;
+  const bool filt = filters(mode, V, top_k, top_p);
   if (!tgt || !gam || !out_tok || !out_n || !out_len) return SPEC_ERR_NULL;
   if (G > 0 && !tok) return SPEC_ERR_NULL;
   if ((sample && G > 0 && !dft) || (draws && !uni)) return SPEC_ERR_NULL;
@@ -1533,6 +1862,7 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.ctr = (unsigned*)(w + p.off_ctr);
   a.part = (uint64_t*)(w + p.off_part);
   a.wsum = (uint64_t*)(w + p.off_wsum);
+  a.thr = filt ? (const float*)(w + p.off_thr) : nullptr;
   a.B = B, a.G = G, a.V = V, a.NC = p.NC, a.CL = p.CL, a.NR = p.NR;
   a.k2 = draws ? (float)(1.4426950408889634 / (double)T) : 1.f;
   a.max_spin = 1u << 22;  // ~0.2 s of polling: far beyond any legitimate wait
@@ -1542,20 +1872,27 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   // of 16-byte vectors
   const bool al = aligned(tgt, 16) && (!sample || G == 0 || aligned(dft, 16)) &&
                   ((size_t)V * e) % 16 == 0;
+  if (filt) {  // the thresholds first, into the workspace, on the same stream
+    launch_filter(filter_args(tgt, dft, gam, (float*)(w + p.off_thr), B, G, V, T, mode, top_k,
+                              top_p),
+                  dtype, s);
+    const int hs = hip_status(hipGetLastError());
+    if (hs != SPEC_OK) return hs;
+  }
   if (dtype == SPEC_DTYPE_BF16) {
     if (sample)
-      launch<SPEC_DTYPE_BF16, SPEC_MODE_SAMPLE>(p.R, al, grid, s, a);
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_SAMPLE>(p.R, al, filt, grid, s, a);
     else if (draws)
-      launch<SPEC_DTYPE_BF16, SPEC_MODE_POINT>(p.R, al, grid, s, a);
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_POINT>(p.R, al, filt, grid, s, a);
     else
-      launch<SPEC_DTYPE_BF16, SPEC_MODE_GREEDY>(p.R, al, grid, s, a);
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_GREEDY>(p.R, al, false, grid, s, a);
   } else {
     if (sample)
-      launch<SPEC_DTYPE_F32, SPEC_MODE_SAMPLE>(p.R, al, grid, s, a);
+      launch<SPEC_DTYPE_F32, SPEC_MODE_SAMPLE>(p.R, al, filt, grid, s, a);
     else if (draws)
-      launch<SPEC_DTYPE_F32, SPEC_MODE_POINT>(p.R, al, grid, s, a);
+      launch<SPEC_DTYPE_F32, SPEC_MODE_POINT>(p.R, al, filt, grid, s, a);
     else
-      launch<SPEC_DTYPE_F32, SPEC_MODE_GREEDY>(p.R, al, grid, s, a);
+      launch<SPEC_DTYPE_F32, SPEC_MODE_GREEDY>(p.R, al, false, grid, s, a);
   }
   return hip_status(hipGetLastError());
 }
@@ -1592,8 +1929,9 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
                 int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_new_len,
                 void* workspace, size_t workspace_bytes, void* stream) {
   return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
-             gamma_max, V, dtype, temperature, mode, out_tokens, out_n_accepted, out_new_len,
-             workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, nullptr);
+             gamma_max, V, dtype, temperature, mode, 0, 1.f, out_tokens, out_n_accepted,
+             out_new_len, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr,
+             nullptr);
 }
 
 int spec_verify_probe(const void* target_logits, const void* draft_logits,
@@ -1605,8 +1943,67 @@ int spec_verify_probe(const void* target_logits, const void* draft_logits,
                       float* out_qx, float* out_z, float* out_m, float* out_s) {
   if ((out_px == nullptr) != (out_qx == nullptr)) return SPEC_ERR_NULL;
   return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
-             gamma_max, V, dtype, temperature, mode, out_tokens, out_n_accepted, out_new_len,
-             workspace, workspace_bytes, stream, out_px, out_qx, out_z, out_m, out_s);
+             gamma_max, V, dtype, temperature, mode, 0, 1.f, out_tokens, out_n_accepted,
+             out_new_len, workspace, workspace_bytes, stream, out_px, out_qx, out_z, out_m, out_s);
+}
+
+int spec_verify_filtered(const void* target_logits, const void* draft_logits,
+                         const int32_t* draft_tokens, const float* uniforms,
+                         const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
+                         int gamma_max, int V, int dtype, float temperature, int mode, int top_k,
+                         float top_p, int32_t* out_tokens, int32_t* out_n_accepted,
+                         int32_t* out_new_len, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
+             gamma_max, V, dtype, temperature, mode, top_k, top_p, out_tokens, out_n_accepted,
+             out_new_len, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr,
+             nullptr);
+}
+
+int spec_verify_filtered_probe(const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_tokens, const float* uniforms,
+                               const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
+                               int gamma_max, int V, int dtype, float temperature, int mode,
+                               int top_k, float top_p, int32_t* out_tokens,
+                               int32_t* out_n_accepted, int32_t* out_new_len, void* workspace,
+                               size_t workspace_bytes, void* stream, float* out_px, float* out_qx,
+                               float* out_z, float* out_m, float* out_s) {
+  if ((out_px == nullptr) != (out_qx == nullptr)) return SPEC_ERR_NULL;
+  return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
+             gamma_max, V, dtype, temperature, mode, top_k, top_p, out_tokens, out_n_accepted,
+             out_new_len, workspace, workspace_bytes, stream, out_px, out_qx, out_z, out_m, out_s);
+}
+
+int spec_filter_thresholds(const void* target_logits, const void* draft_logits,
+                           const int32_t* gamma_per_row, int B, int gamma_max, int V, int dtype,
+                           float temperature, int mode, int top_k, float top_p, float* out_thr,
+                           void* stream) {
+  if (B < 1 || V < 1 || V > kMaxVocab || gamma_max < 0 || gamma_max > SPEC_GAMMA_MAX_LIMIT)
+    return SPEC_ERR_SHAPE;
+  if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return SPEC_ERR_ARG;
+  if (mode != SPEC_MODE_SAMPLE && mode != SPEC_MODE_POINT) return SPEC_ERR_ARG;
+  if (!(temperature > 0.f && isfinite(temperature)) || !filter_args_ok(top_k, top_p))
+    return SPEC_ERR_ARG;
+  if (!target_logits || !gamma_per_row || !out_thr) return SPEC_ERR_NULL;
+  if (mode == SPEC_MODE_SAMPLE && gamma_max > 0 && !draft_logits) return SPEC_ERR_NULL;
+  if ((int64_t)B * (2 * gamma_max + 1) >= ((int64_t)1 << 31)) return SPEC_ERR_SHAPE;
+  const size_t e = dtype == SPEC_DTYPE_F32 ? 4 : 2;
+  if (mode != SPEC_MODE_SAMPLE) draft_logits = nullptr;
+  if (!aligned(target_logits, e) || (draft_logits && !aligned(draft_logits, e)) ||
+      !aligned(gamma_per_row, 4) || !aligned(out_thr, 4))
+    return SPEC_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (!filters(mode, V, top_k, top_p)) {
+    // nothing is cut: every threshold is -inf
+    const size_t n = (size_t)B * (2 * gamma_max + 1);
+    hipLaunchKernelGGL(fill_ninf_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, out_thr, n);
+    return hip_status(hipGetLastError());
+  }
+  launch_filter(filter_args(target_logits, draft_logits, gamma_per_row, out_thr, B, gamma_max, V,
+                            temperature, mode, top_k, top_p),
+                dtype, s);
+  return hip_status(hipGetLastError());
 }
 
 int spec_verify_plan(int B, int gamma_max, int V, int dtype, int mode, int64_t* out) {
@@ -1652,7 +2049,7 @@ const char* spec_verify_strerror(int status) {
   return "unknown status";
 }
 
-int spec_verify_version(void) { return 300; }
+int spec_verify_version(void) { return 400; }
 
 int spec_probe_read_blocks(size_t bytes) {
   return (int)((bytes + kProbeBytesPerBlock - 1) / kProbeBytesPerBlock);

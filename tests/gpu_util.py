@@ -35,11 +35,34 @@ def case_to_dev(case, torch, offset=0):
 def run(case, torch, probe=True, workspace=None, dev=None, offset=0):
     d = dev if dev is not None else case_to_dev(case, torch, offset)
     mode = MODES[case.mode]
-    # point-mass drafts have no draft logits: pass none, so a read would fault loudly
+    # point-mass drafts come without draft logits: none are passed
     draft = None if case.mode == "point" else d["draft"]
     res = sv.verify(d["target"], draft, d["tokens"], d["uniforms"], d["gamma"], d["kv"],
-                    temperature=case.T, mode=mode, workspace=workspace, probe=probe)
+                    temperature=case.T, mode=mode, workspace=workspace, probe=probe,
+                    top_k=case.extra.get("top_k", 0), top_p=case.extra.get("top_p", 1.0))
     torch.cuda.synchronize()
     out = [r.cpu().numpy() for r in res[:3]]
     pr = {k: v.cpu().numpy() for k, v in res[3].items()} if probe else None
     return out[0], out[1], out[2], pr
+
+
+def filtered_case(cfg, rnd, mode, top_k, top_p, **kw):
+    """A workload batch verified with top-k / top-p filtering.  When sampling,
+    the draft tokens are drawn from the filtered q (the drafter applies the
+    same filter; seed stream 7 of the batch)."""
+    import oracle
+    from speculative_decoding_verification_07_amd import inputs
+    case = inputs.make_case(cfg, rnd=rnd, mode=mode, **kw)
+    case.extra = dict(case.extra, top_k=top_k, top_p=float(np.float32(top_p)))
+    if mode == "sample":
+        rng = inputs.rng(case.config.cfg, rnd, 7)
+        x = case.tokens.copy()
+        for b in range(case.B):
+            for i in range(int(case.gamma[b])):
+                q, _ = oracle.filter_row(case.draft[b, i], temperature=case.T, top_k=top_k,
+                                         top_p=case.extra["top_p"])
+                c = np.cumsum(q)
+                j = int(np.searchsorted(c, rng.random() * c[-1], side="right"))
+                x[b, i] = min(j, case.V - 1)
+        case.tokens = x
+    return case

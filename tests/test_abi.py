@@ -75,6 +75,34 @@ def test_argument_errors(lib, kw, code):
     assert _call(lib, **kw) == code
 
 
+def _fcall(lib, **kw):
+    a = dict(tgt=A, dft=A, tok=A, uni=A, gam=A, kv=None, B=4, G=4, V=1000, dtype=sv.BF16,
+             T=1.0, mode=sv.SAMPLE, k=10, p=0.9, out_tok=A, out_n=A, out_len=A, ws=A2,
+             ws_bytes=1, stream=None)
+    a.update(kw)
+    return lib.spec_verify_filtered(a["tgt"], a["dft"], a["tok"], a["uni"], a["gam"], a["kv"],
+                                    a["B"], a["G"], a["V"], a["dtype"], a["T"], a["mode"],
+                                    a["k"], a["p"], a["out_tok"], a["out_n"], a["out_len"],
+                                    a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_filtered_argument_errors(lib):
+    # valid filter arguments get as far as the workspace check
+    assert _fcall(lib) == sv.ERR_WORKSPACE
+    assert _fcall(lib, k=0, p=1.0) == sv.ERR_WORKSPACE
+    assert _fcall(lib, mode=sv.GREEDY, dft=None, uni=None, k=-1 + 1, p=0.5) == sv.ERR_WORKSPACE
+    for bad in (dict(k=-1), dict(p=0.0), dict(p=1.5), dict(p=float("nan")), dict(p=-0.5)):
+        assert _fcall(lib, **bad) == sv.ERR_ARG, bad
+    th = lib.spec_filter_thresholds
+    assert th(A, A, A, 4, 4, 1000, sv.BF16, 1.0, sv.GREEDY, 5, 0.9, A, None) == sv.ERR_ARG
+    assert th(A, A, A, 4, 4, 1000, sv.BF16, 0.0, sv.SAMPLE, 5, 0.9, A, None) == sv.ERR_ARG
+    assert th(A, A, A, 4, 4, 1000, sv.BF16, 1.0, sv.SAMPLE, -2, 0.9, A, None) == sv.ERR_ARG
+    assert th(A, None, A, 4, 4, 1000, sv.BF16, 1.0, sv.SAMPLE, 5, 0.9, A, None) == sv.ERR_NULL
+    assert th(A, A, A, 4, 4, 1000, sv.BF16, 1.0, sv.SAMPLE, 5, 0.9, None, None) == sv.ERR_NULL
+    assert th(A, A, A, 0, 4, 1000, sv.BF16, 1.0, sv.SAMPLE, 5, 0.9, A, None) == sv.ERR_SHAPE
+    assert th(A + 1, A, A, 4, 4, 1000, sv.BF16, 1.0, sv.SAMPLE, 5, 0.9, A, None) == sv.ERR_ALIGN
+
+
 def test_null_tolerated_where_documented(lib):
     """Greedy may omit draft logits and uniforms, gamma_max = 0 may omit the
     draft tokens: validation must get past those (checked here with a
