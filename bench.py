@@ -11,6 +11,11 @@ the 256 MB Infinity Cache.
 Prints one JSON line.  `value` is verified rows per second; the roofline
 object gives the dominant (only) kernel's achieved HBM rate from the
 compulsory logit bytes and its event-timed average launch duration.
+
+With --top-k / --top-p a step is the filtered verify: the threshold kernel,
+then the verify on the filtered rows (two launches); the draft tokens are
+the workload's (drawn from the unfiltered q).  The threshold kernel is also
+timed alone, and the roofline names the longer of the two kernels.
 """
 from __future__ import annotations
 
@@ -41,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
     ap.add_argument("--mode", default="sample", choices=["sample", "greedy", "point"])
+    ap.add_argument("--top-k", type=int, default=0, help="top-k filter of p and q (0: off)")
+    ap.add_argument("--top-p", type=float, default=1.0, help="top-p filter of p and q (1: off)")
     ap.add_argument("--rotate", type=int, default=0, help="device copies (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -105,8 +112,10 @@ def main():
            torch.empty(B, dtype=torch.int32, device=dev),
            torch.empty(B, dtype=torch.int32, device=dev))
 
+    filt = mode != sv.GREEDY and ((0 < args.top_k < V) or args.top_p < 1.0)
     calls = [sv.Prepared(t, d, tok, uni, gam, kv, temperature=case.T, mode=mode, workspace=ws,
-                         out=out) for t, d in sets]
+                         out=out, top_k=args.top_k if filt else 0,
+                         top_p=args.top_p if filt else 1.0) for t, d in sets]
 
     for k in range(args.warmup):
         calls[k % rot]()
@@ -135,6 +144,33 @@ def main():
         ev1[k].record(stream)
     torch.cuda.synchronize()
     launch_ms = np.array([ev0[k].elapsed_time(ev1[k]) for k in range(K)])
+    filter_us = None
+    if filt:
+        # the threshold kernel alone, back to back, into a scratch array
+        import ctypes
+        thr = torch.empty((B, 2 * G + 1), dtype=torch.float32, device=dev)
+        sv.filter_thresholds(tgt0, dft0, gam, temperature=case.T, mode=mode, top_k=args.top_k,
+                             top_p=args.top_p, out=thr)  # argument checks, once
+        lib = sv.load()
+        hs = ctypes.c_void_p(stream.cuda_stream)
+        fargs = [(ctypes.c_void_p(t_.data_ptr()),
+                  ctypes.c_void_p(d_.data_ptr()) if d_ is not None else None) for t_, d_ in sets]
+        def thresholds(k):
+            t_, d_ = fargs[k % rot]
+            lib.spec_filter_thresholds(t_, d_, ctypes.c_void_p(gam.data_ptr()), B, G, V, dt,
+                                       ctypes.c_float(case.T), mode, args.top_k,
+                                       ctypes.c_float(args.top_p), ctypes.c_void_p(thr.data_ptr()),
+                                       hs)
+        for k in range(args.warmup):
+            thresholds(k)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for k in range(K):
+            thresholds(k)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        filter_us = f0.elapsed_time(f1) / K * 1e3
     diag = ws.diagnostics()
     n_acc = out[1].cpu().numpy()
 
@@ -143,6 +179,12 @@ def main():
     # is the back-to-back time per step (event pairs around single launches
     # add their own overhead and are reported separately)
     kern_s = ms_per_step * 1e-3
+    kernel_name = "verify_kernel"
+    if filter_us is not None:
+        # two launches per step: the longer one is the dominant kernel
+        verify_s = kern_s - filter_us * 1e-6
+        kern_s = max(verify_s, filter_us * 1e-6)
+        kernel_name = "verify_kernel" if verify_s >= filter_us * 1e-6 else "filter_kernel"
     achieved = step_bytes / kern_s / 1e9
     emitted = int((n_acc + 1).sum())
     tested = int(np.minimum(n_acc + 1, case.gamma).sum())
@@ -174,7 +216,7 @@ def main():
         with open(counters) as f:
             cnt = json.load(f)
         if cnt.get("source_sha256_16") == source_hash() and cnt.get("workload_config") == args.config \
-                and cnt.get("mode") == args.mode:
+                and cnt.get("mode") == args.mode and not filt:
             traffic = cnt.get("hbm_bytes_per_launch")
 
     cpu = None
@@ -188,19 +230,23 @@ def main():
                           case.kv_len, temperature=case.T,
                           mode={sv.SAMPLE: oracle.SAMPLE, sv.GREEDY: oracle.GREEDY,
                                 sv.POINT: oracle.POINT}[mode],
-                          threads=threads)
+                          threads=threads, top_k=args.top_k if filt else 0,
+                          top_p=args.top_p if filt else 1.0)
             t_cpu += time.perf_counter() - c0
             reps += 1
         cpu = {"value": B * reps / t_cpu, "unit": "rows/s", "cores": threads, "kind": "oracle",
                "sample": f"{reps} full batches of this workload ({B} rows each), "
                          f"{t_cpu:.1f} s of double-precision oracle work"}
 
+    ftxt = f" top_k={args.top_k} top_p={args.top_p}" if filt else ""
     cfgd = {"workload": f"verify B={B} gamma={G} V={V} "
                         f"{'bf16' if dt == sv.BF16 else 'fp32'} logits T={case.T} {args.mode}"
-                        f" (config {args.config})",
+                        f"{ftxt} (config {args.config})",
             "B": B, "gamma": G, "V": V, "logits_dtype": "bf16" if dt == sv.BF16 else "fp32",
             "mode": args.mode, "temperature": case.T, "rotated_copies": rot,
             "compulsory_bytes_per_step": step_bytes}
+    if filt:
+        cfgd.update(top_k=args.top_k, top_p=args.top_p)
     line = {
         "metric": "verified rows/s (batched speculative-decoding verify step)",
         "value": B * K / (total_ms * 1e-3),
@@ -219,6 +265,7 @@ def main():
         "step_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernel_us": kern_s * 1e6,
+        "filter_kernel_us": filter_us,
         "kernel_us_event_pair_mean": float(launch_ms.mean()) * 1e3,
         "kernel_us_event_pair_p50": float(np.median(launch_ms)) * 1e3,
         "acceptance_rate": (emitted - B) / max(tested, 1),
@@ -229,7 +276,7 @@ def main():
         "diagnostics": diag,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "verify_kernel", "bytes_per_launch": step_bytes},
+                     "kernel": kernel_name, "bytes_per_launch": step_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

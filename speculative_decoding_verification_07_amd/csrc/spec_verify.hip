@@ -39,6 +39,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <type_traits>
 #include <string.h>
 
 #include "spec_verify.h"
@@ -1525,14 +1526,16 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
 //          under softmax(l / T) (all copies of a value together).
 // Values are ordered through sortable keys (the float's bits with the sign
 // bit flipped, all bits flipped when negative; larger value, larger key) and
-// selected by most significant digits, one histogram per level over the
-// entries that match the digits chosen so far: 12 bits, then 4 for bf16
-// (whose keys carry nothing below bit 16) or 12 and 8 for fp32.  Masses are
+// selected by most significant digits, 8 bits per level (two levels for bf16,
+// whose keys carry nothing below bit 16; four for fp32), one histogram per
+// level over the entries that match the digits chosen so far.  The levels run
+// over a candidate list in LDS (the entries above a floor that provably lies
+// under the threshold), or over the whole row when the list would overflow.  Masses are
 // 2^fma(l, k2, -R(max)) (the weights of the verify) in fixed point, units of
 // 2^-42, so their sums are exact integers whatever the order of the additions.
 constexpr int kFThreads = 256;
 constexpr int kFWaves = kFThreads / 64;
-constexpr int kFBins = 4096;
+constexpr int kFBins = 256;
 constexpr double kMassUnit = 4398046511104.0;  // 2^42
 
 struct FArgs {
@@ -1545,8 +1548,14 @@ struct FArgs {
   float k2, top_p;
 };
 
+constexpr int kFSlots = 32;  // candidate keys each thread can keep in LDS
+constexpr int kFCand = kFThreads * kFSlots;
+
 struct FLds {
   unsigned long long h[kFBins];
+  uint32_t cand[kFCand];
+  float tmax[kFThreads];
+  unsigned ccount[kFThreads];  // candidates each thread found
   unsigned long long red[kFWaves];
   unsigned long long mask[kFWaves];
   float fmax[kFWaves];
@@ -1565,13 +1574,9 @@ __device__ __forceinline__ float funkey(uint32_t k) {
 // Digit levels: shift and width of level lv.
 template <int DT>
 struct FLevels {
-  static constexpr int N = DT == SPEC_DTYPE_BF16 ? 2 : 3;
-  __device__ static int shift(int lv) {
-    return DT == SPEC_DTYPE_BF16 ? (lv == 0 ? 20 : 16) : (lv == 0 ? 20 : lv == 1 ? 8 : 0);
-  }
-  __device__ static int bits(int lv) {
-    return DT == SPEC_DTYPE_BF16 ? (lv == 0 ? 12 : 4) : (lv == 2 ? 8 : 12);
-  }
+  static constexpr int N = DT == SPEC_DTYPE_BF16 ? 2 : 4;
+  __device__ static int shift(int lv) { return 24 - 8 * lv; }
+  __device__ static int bits(int) { return 8; }
 };
 
 __device__ float fblock_max(float v, FLds& L) {
@@ -1654,12 +1659,65 @@ __device__ int find_cross(FLds& L, int nb, uint64_t need, uint64_t& above, uint6
   return d;
 }
 
+// Calls f(value) for every element of a row of V entries: 16-byte vector
+// loads for the aligned body (sixteen per thread in flight: with about two
+// such workgroups per CU the passes are otherwise bound by the latency of
+// too few loads), the unaligned head
+// and tail element by element.
+// VEC (optional): g(fe) is called on each vector's unpacked elements
+// instead, so the caller can act on a vector at once.  part > 1: only the
+// head and the first 1/part of the vectors.
+template <int DT, class F, class VF>
+__device__ __forceinline__ void row_for_each_v(const char* row, int V, int part, F f, VF g) {
+  using E = Elt<DT>;
+  const int t = threadIdx.x;
+  int head = (int)(((16u - ((unsigned)(uintptr_t)row & 15u)) & 15u) / E::kBytes);
+  if (head > V) head = V;
+  const int nv_all = (V - head) / E::kVec;
+  const int jb = head + nv_all * E::kVec;
+  const int nv = part > 1 ? (nv_all + part - 1) / part : nv_all;
+  if (t < head) f(E::one(row, t));
+  if (part <= 1 && t < V - jb) f(E::one(row, jb + t));
+  const uint4* vp = (const uint4*)(row + head * E::kBytes);
+  constexpr int U = 16;
+  // the same number of rounds in every lane (g may use cross-lane
+  // operations); vectors past the end read as -inf
+  for (int q0 = 0; q0 < nv; q0 += kFThreads * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u * kFThreads + t;
+      v[u] = q < nv ? vp[q] : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord,
+                                           E::kNegInfWord);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q0 + u * kFThreads >= nv) break;  // uniform
+      float fe[E::kVec];
+      E::unpack(v[u], fe);
+      g(fe);
+    }
+  }
+}
+
+template <int DT, class F>
+__device__ __forceinline__ void row_for_each(const char* row, int V, F f) {
+  row_for_each_v<DT>(row, V, 1, f, [&](const float* fe) {
+#pragma unroll
+    for (int e = 0; e < Elt<DT>::kVec; ++e) f(fe[e]);
+  });
+}
+
+__device__ __forceinline__ unsigned long long fixed_mass(float l, float k2, float R) {
+  return (unsigned long long)((double)ex2(fmaf(l, k2, -R)) * kMassUnit);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
   using E = Elt<DT>;
   using Lv = FLevels<DT>;
   __shared__ FLds L;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
   const int b = (int)(blockIdx.x / (unsigned)a.NR2), slot = (int)(blockIdx.x % (unsigned)a.NR2);
   const int g = a.gam[b];
   float* out = a.thr + (int64_t)b * (2 * a.G + 1) + slot;
@@ -1672,43 +1730,125 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
   }
   const char* row = is_t ? (const char*)a.tgt + ((int64_t)b * (a.G + 1) + slot) * a.V * E::kBytes
                          : (const char*)a.dft + ((int64_t)b * a.G + (slot - a.G - 1)) * a.V * E::kBytes;
-  float mx = NEG_INF;
-  for (int j = t; j < a.V; j += kFThreads) mx = fmaxf(mx, E::one(row, j));
-  mx = fblock_max(mx, L);
+  const bool use_k = a.top_k > 0 && a.top_k < a.V;
+  const bool use_p = a.top_p < 1.f;
+
+  // A floor under the threshold, so that the selection can work on the
+  // entries above it only.  top-k (k <= threads): the k-th largest of the
+  // threads' maxima over the first quarter of the row, since k distinct
+  // entries reach it.  top-p alone: every entry below mx - D weighs under
+  // 2^(-D k2) of the largest, so all of them together weigh under
+  // V 2^(-D k2) <= (1 - top_p) of the row's mass (at least the largest
+  // entry's); the top-p set therefore lies above mx - D.
+  float floor_v = NEG_INF, mx = NEG_INF;
+  if (use_k && a.top_k <= kFThreads) {
+    float tm = NEG_INF;
+    row_for_each_v<DT>(row, a.V, 4, [&](float l) { tm = fmaxf(tm, l); }, [&](const float* fe) {
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) tm = fmaxf(tm, fe[e]);
+    });
+    L.tmax[t] = tm;
+    __syncthreads();
+    int above = 0;  // rank of this thread's maximum, ties by thread index
+    for (int s2 = 0; s2 < kFThreads; ++s2) {
+      const float o = L.tmax[s2];
+      above += (o > tm) | ((o == tm) & (s2 < t));
+    }
+    if (above == a.top_k - 1) L.fmax[0] = tm;
+    __syncthreads();
+    floor_v = L.fmax[0];
+    __syncthreads();
+  } else if (use_p && !use_k) {
+    float tm = NEG_INF;
+    row_for_each<DT>(row, a.V, [&](float l) { tm = fmaxf(tm, l); });
+    mx = fblock_max(tm, L);
+    const double D = (log2((double)a.V) - log2(1.0 - (double)a.top_p)) / (double)a.k2 + 2.0;
+    if (mx != NEG_INF) floor_v = (float)((double)mx - D);
+  }
+  // (the key floor: float comparisons tie -0 with +0, keys put -0 first)
+  const uint32_t floor_key =
+      floor_v == NEG_INF ? 0u : fkey(floor_v == 0.f ? -0.f : floor_v);
+
+  // the candidates: every entry at or above the floor, each thread into its
+  // own kFSlots slots of LDS (no cross-lane work per entry; a thread that
+  // finds more sends the row to the whole-row selection); the row's largest
+  // value; the total mass when top-p runs alone (its largest value is known
+  // by now).  A float compare selects them (it also takes -0 against a +0
+  // floor: a harmless extra candidate).
+  const bool need_w = use_p && !use_k;
+  const float Rw = need_w && mx != NEG_INF ? ref_of(mx, a.k2) : 0.f;
+  unsigned long long wsum = 0;
+  float tm2 = NEG_INF;
+  unsigned mine = 0;
+  uint32_t* slots = L.cand + t * kFSlots;
+  // (two instantiations: the total mass only when top-p runs alone; a
+  // uniform test inside the loop would cost its conversions on every entry)
+  auto candidates = [&](auto with_w) {
+    constexpr bool kW = decltype(with_w)::value;
+    auto one = [&](float l) {
+      tm2 = fmaxf(tm2, l);
+      if (kW) wsum += fixed_mass(l, a.k2, Rw);
+      if (l >= floor_v) {
+        if (mine < (unsigned)kFSlots) slots[mine] = fkey(l);
+        ++mine;
+      }
+    };
+    row_for_each_v<DT>(row, a.V, 1, one, [&](const float* fe) {
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) one(fe[e]);
+    });
+  };
+  if (need_w)
+    candidates(std::integral_constant<bool, true>{});
+  else
+    candidates(std::integral_constant<bool, false>{});
+  L.ccount[t] = mine;
+  mx = fblock_max(tm2, L);
   if (mx == NEG_INF) {  // a dead row: the walk reports it
     if (t == 0) *out = NEG_INF;
     return;
   }
-  const bool use_k = a.top_k > 0 && a.top_k < a.V;
-  const bool use_p = a.top_p < 1.f;
-  // radix selection: `mass` weighs each entry by its fixed-point mass, else 1;
-  // only entries with key >= floor_key take part
-  auto select = [&](bool mass, uint64_t need, uint32_t floor_key) -> uint32_t {
-    const float R = ref_of(mx, a.k2);
+  const float R = ref_of(mx, a.k2);
+  uint64_t w_all = 0;
+  if (use_p && !use_k) {
+    uint64_t incl, excl;
+    fblock_scan(wsum, L, incl, excl, w_all);
+  }
+  __syncthreads();
+  const bool listed = __syncthreads_and(mine <= (unsigned)kFSlots) != 0;  // else: whole-row passes
+
+  // radix selection over the candidates (or the row): `mass` weighs each
+  // entry by its fixed-point mass, else 1; only keys >= floor_key2 count.
+  // W: the mass the top-p target is a fraction of (0: the histogram's total)
+  auto select = [&](bool mass, uint64_t need, uint32_t floor_key2, uint64_t W) -> uint32_t {
     uint32_t prefix = 0, pmask = 0;
     for (int lv = 0; lv < Lv::N; ++lv) {
       const int sh = Lv::shift(lv), nb = 1 << Lv::bits(lv);
       for (int i = t; i < nb; i += kFThreads) L.h[i] = 0;
       __syncthreads();
-      for (int j = t; j < a.V; j += kFThreads) {
-        const float l = E::one(row, j);
-        const uint32_t k = fkey(l);
-        if (k >= floor_key && (k & pmask) == prefix) {
-          const unsigned long long w =
-              mass ? (unsigned long long)((double)ex2(fmaf(l, a.k2, -R)) * kMassUnit) : 1ull;
+      auto add = [&](uint32_t k) {
+        if (k >= floor_key2 && (k & pmask) == prefix) {
+          const unsigned long long w = mass ? fixed_mass(funkey(k), a.k2, R) : 1ull;
           if (w) atomicAdd(&L.h[(k >> sh) & (nb - 1)], w);
         }
+      };
+      if (listed) {
+        for (int i = t; i < kFCand; i += kFThreads)
+          if ((unsigned)(i % kFSlots) < L.ccount[i / kFSlots]) add(L.cand[i]);
+      } else {
+        row_for_each<DT>(row, a.V, [&](float l) { add(fkey(l)); });
       }
       __syncthreads();
       uint64_t above, total;
       if (mass && lv == 0) {
         // the target: top_p of the mass kept so far, rounded up to a unit
-        uint64_t sum = 0, incl, excl;
-        for (int i = t; i < nb; i += kFThreads) sum += L.h[i];
-        fblock_scan(sum, L, incl, excl, total);
-        need = (uint64_t)ceil((double)a.top_p * (double)total);
+        if (W == 0) {
+          uint64_t sum = 0, incl, excl;
+          for (int i = t; i < nb; i += kFThreads) sum += L.h[i];
+          fblock_scan(sum, L, incl, excl, W);
+        }
+        need = (uint64_t)ceil((double)a.top_p * (double)W);
         if (need < 1) need = 1;
-        if (need > total) need = total;
       }
       const int d = find_cross(L, nb, need, above, total);
       need -= above;
@@ -1718,9 +1858,11 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
     return prefix;
   };
   uint32_t key = 0;
-  if (use_k) key = select(false, (uint64_t)a.top_k, 0u);
+  if (use_k) key = select(false, (uint64_t)a.top_k, floor_key, 0);
   if (use_p) {
-    const uint32_t kp = select(true, 0, key);
+    // top-k kept: its own mass (all of it is among the candidates); top-p
+    // alone: the whole row's
+    const uint32_t kp = select(true, 0, use_k ? key : floor_key, use_k ? 0 : w_all);
     key = kp > key ? kp : key;
   }
   // a bf16 key's low 16 bits: zero for positive values, all ones for negative
