@@ -34,7 +34,7 @@ ROTATE_BYTES = 1 << 30  # at least this much distinct logit memory in rotation
 # HBM byte counters of the kernel per workload and mode (committed summaries of
 # rocprofv3 FETCH_SIZE / WRITE_SIZE runs); used only while the kernel source
 # still has the hash they were taken on
-COUNTERS = os.path.join(ROOT, "profiles", "verify_kernel_c{config}_{mode}_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "{kernel}_c{config}_{mode}{filt}_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_07_amd", "csrc",
                           "spec_verify.hip")
 
@@ -211,12 +211,13 @@ def main():
     del probe
 
     traffic = None
-    counters = COUNTERS.format(config=args.config, mode=args.mode)
+    counters = COUNTERS.format(kernel=kernel_name, config=args.config, mode=args.mode,
+                               filt=f"_k{args.top_k}_p{args.top_p:g}" if filt else "")
     if os.path.exists(counters):
         with open(counters) as f:
             cnt = json.load(f)
         if cnt.get("source_sha256_16") == source_hash() and cnt.get("workload_config") == args.config \
-                and cnt.get("mode") == args.mode and not filt:
+                and cnt.get("mode") == args.mode:
             traffic = cnt.get("hbm_bytes_per_launch")
 
     cpu = None
