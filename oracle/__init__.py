@@ -56,6 +56,8 @@ def _load():
         lib.oracle_draw_cdf.restype = i32
         lib.oracle_filter_row.argtypes = [P, i32, i32, D, i32, D, P, P, P]
         lib.oracle_filter_row.restype = i32
+        lib.oracle_ngram_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P]
+        lib.oracle_ngram_draft.restype = i32
         _lib = lib
     return _lib
 
@@ -175,3 +177,29 @@ def filter_row(logits, *, temperature=1.0, top_k=0, top_p=1.0, margin=False):
     if rc != 0:
         raise ValueError("oracle refused the row or its arguments")
     return (prob, tau.value, mg.value) if margin else (prob, tau.value)
+
+
+@dataclass
+class DraftResult:
+    draft: np.ndarray    # int32 [B, gamma], -1 after the draft
+    length: np.ndarray   # int32 [B]
+    n: np.ndarray        # int32 [B]; the n-gram length that matched, -1 if none
+    pos: np.ndarray      # int32 [B]; where the copied continuation starts, -1 if none
+
+
+def ngram_draft(context, ctx_len, *, n_min=1, n_max=4, gamma=4) -> DraftResult:
+    """Prompt-lookup drafting over int32 contexts [B, stride] with lengths
+    ctx_len [B] (see oracle_ngram_draft in spec_oracle.c)."""
+    lib = _load()
+    context = np.ascontiguousarray(context, dtype=np.int32)
+    B, stride = context.shape
+    ctx_len = np.ascontiguousarray(ctx_len, dtype=np.int32).reshape(B)
+    draft = np.empty((B, gamma), np.int32)
+    length = np.empty(B, np.int32)
+    n = np.empty(B, np.int32)
+    pos = np.empty(B, np.int32)
+    rc = lib.oracle_ngram_draft(_ptr(context), _ptr(ctx_len), B, stride, int(n_min), int(n_max),
+                                int(gamma), _ptr(draft), _ptr(length), _ptr(n), _ptr(pos))
+    if rc != 0:
+        raise ValueError("oracle refused the drafting arguments")
+    return DraftResult(draft, length, n, pos)

@@ -500,3 +500,58 @@ int oracle_filter_row(const void* logits, int dtype, int V, double T, int top_k,
   if (tau_out) *tau_out = filter_threshold(&c, logits, 0, m, NULL);
   return 0;
 }
+
+/* ---------------------------------------------------------------- drafting
+ * Prompt-lookup (n-gram) drafting ("Speculative decoding", mhtirogla.ai,
+ * "Implementation notes": copy the continuation of the last matching n-gram
+ * from the prompt; tusharamrit, "Self-speculation": search the existing
+ * context for the current suffix and propose what followed it last time).
+ * Reading: for n = n_max down to n_min, the suffix is the last n tokens of
+ * the context c[0..L); its most recent earlier occurrence is the largest j
+ * with j + n <= L - 1 (so that a token follows it) and c[j..j+n) equal to
+ * the suffix; the first n with an occurrence wins (the longest match), and
+ * the draft is c[j+n .. min(j+n+gamma, L)).  No occurrence for any n: no
+ * draft.
+ * context: int32 [B, stride]; ctx_len[b] in [0, stride] tokens of row b.
+ * out_draft: int32 [B, gamma] (-1 after the draft); out_len: [B] draft
+ * lengths; out_n, out_pos (optional): the n that matched and the draft's
+ * start j + n (-1 when none).  A row whose length lies outside [0, stride]
+ * gets no draft and out_n = -2.  Returns 0, or -1 for refused arguments. */
+int oracle_ngram_draft(const int32_t* context, const int32_t* ctx_len, int B, int stride,
+                       int n_min, int n_max, int gamma, int32_t* out_draft, int32_t* out_len,
+                       int32_t* out_n, int32_t* out_pos) {
+  if (!context || !ctx_len || !out_draft || !out_len) return -1;
+  if (B < 0 || stride < 0 || n_min < 1 || n_max < n_min || gamma < 0) return -1;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* c = context + (size_t)b * stride;
+    const int L = ctx_len[b];
+    int32_t* d = out_draft + (size_t)b * gamma;
+    for (int i = 0; i < gamma; ++i) d[i] = -1;
+    out_len[b] = 0;
+    if (out_n) out_n[b] = -1;
+    if (out_pos) out_pos[b] = -1;
+    if (L < 0 || L > stride) {
+      if (out_n) out_n[b] = -2;
+      continue;
+    }
+    for (int n = n_max; n >= n_min; --n) {
+      if (L < n + 1) continue;
+      int found = -1;
+      for (int j = L - n - 1; j >= 0 && found < 0; --j) {
+        int same = 1;
+        for (int i = 0; i < n && same; ++i) same = c[j + i] == c[L - n + i];
+        if (same) found = j;
+      }
+      if (found >= 0) {
+        const int start = found + n;
+        int k = 0;
+        for (; k < gamma && start + k < L; ++k) d[k] = c[start + k];
+        out_len[b] = k;
+        if (out_n) out_n[b] = n;
+        if (out_pos) out_pos[b] = start;
+        break;
+      }
+    }
+  }
+  return 0;
+}
