@@ -16,6 +16,12 @@ With --top-k / --top-p a step is the filtered verify: the threshold kernel,
 then the verify on the filtered rows (two launches); the draft tokens are
 the workload's (drawn from the unfiltered q).  The threshold kernel is also
 timed alone, and the roofline names the longer of the two kernels.
+
+--mode ngram times prompt-lookup drafting alone (spec_ngram_draft over 64
+contexts of 16k..32k tokens, n = 4..1, gamma = 4; context copies rotated like
+the logits).  --mode round times a whole model-free speculative round: the
+drafter, then the point-mode verify of its drafts against the B=64,
+V=128256 target logits, both launches on one stream.
 """
 from __future__ import annotations
 
@@ -37,6 +43,9 @@ ROTATE_BYTES = 1 << 30  # at least this much distinct logit memory in rotation
 COUNTERS = os.path.join(ROOT, "profiles", "{kernel}_c{config}_{mode}{filt}_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_07_amd", "csrc",
                           "spec_verify.hip")
+NGRAM_SRC = os.path.join(ROOT, "speculative_decoding_verification_07_amd", "csrc",
+                         "spec_ngram.hip")
+NGRAM_COUNTERS = os.path.join(ROOT, "profiles", "ngram_kernel_{contexts}_counters.json")
 
 
 def parse():
@@ -45,7 +54,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
-    ap.add_argument("--mode", default="sample", choices=["sample", "greedy", "point"])
+    ap.add_argument("--mode", default="sample",
+                    choices=["sample", "greedy", "point", "ngram", "round"])
+    ap.add_argument("--contexts", default="ctx32k", help="drafting workload (ngram, round)")
     ap.add_argument("--top-k", type=int, default=0, help="top-k filter of p and q (0: off)")
     ap.add_argument("--top-p", type=float, default=1.0, help="top-p filter of p and q (1: off)")
     ap.add_argument("--rotate", type=int, default=0, help="device copies (0: enough for 1 GiB)")
@@ -57,9 +68,208 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def source_hash(path=KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_ceiling(sv, torch, dev, stream, with_copy=False) -> float:
+    """HBM read ceiling of this machine: plain streaming read of 4 GiB (GB/s)."""
+    probe = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    pout = None
+    for _ in range(3):
+        pout = sv.probe_read(probe, pout)
+    torch.cuda.synchronize()
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe0.record(stream)
+    for _ in range(10):
+        sv.probe_read(probe, pout)
+    pe1.record(stream)
+    torch.cuda.synchronize()
+    ceiling = probe.numel() * 10 / (pe0.elapsed_time(pe1) * 1e-3) / 1e9
+    if with_copy:
+        dst = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            sv.probe_copy(probe[: 1 << 28], dst)
+        torch.cuda.synchronize()
+        del dst
+    del probe
+    return ceiling
+
+
+def timed(run, K, warmup, stream, torch):
+    """K back-to-back calls of run(k) between two events on the launch
+    stream, after `warmup` untimed ones; returns (total ms, wall s)."""
+    for k in range(warmup):
+        run(k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(K):
+        run(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), time.perf_counter() - wall0
+
+
+def bench_drafting(args):
+    """--mode ngram (drafting alone) and --mode round (drafting + point verify)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_07_amd as sv
+    from speculative_decoding_verification_07_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib = sv.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    hs = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+
+    t0 = time.time()
+    cc = inputs.CONTEXT_CONFIGS[args.contexts]
+    ctx, lens = inputs.make_contexts(cc, rnd=0)
+    B, G = cc.B, cc.gamma
+    draft_bytes = inputs.context_bytes(lens, G)
+    ctx0 = torch.from_numpy(ctx).to(dev)
+    ln = torch.from_numpy(lens).to(dev)
+    rot_c = args.rotate or max(1, -(-ROTATE_BYTES // ctx.nbytes))
+    ctxs = [ctx0] + [ctx0.clone() for _ in range(rot_c - 1)]
+    nws = sv.Workspace(sv.ngram_workspace_bytes(B))
+    d_tok = torch.empty((B, G), dtype=torch.int32, device=dev)
+    d_len, d_n, d_pos = (torch.empty(B, dtype=torch.int32, device=dev) for _ in range(3))
+    sv.ngram_draft(ctx0, ln, n_min=cc.n_min, n_max=cc.n_max, gamma=G, workspace=nws,
+                   out=(d_tok, d_len, d_n, d_pos))  # argument checks, once
+    dargs = [(P(c.data_ptr()), P(ln.data_ptr()), B, cc.stride, cc.n_min, cc.n_max, G,
+              P(d_tok.data_ptr()), P(d_len.data_ptr()), P(d_n.data_ptr()), P(d_pos.data_ptr()),
+              P(nws.ptr), nws.nbytes, hs) for c in ctxs]
+
+    def draft(k):
+        lib.spec_ngram_draft(*dargs[k % rot_c])
+
+    K = args.steps
+    calls, case, step_bytes, rot_v = [draft], None, draft_bytes, 0
+    if args.mode == "round":
+        case = inputs.make_case(args.config, rnd=0, mode="point")
+        if case.G < G or case.B != B:
+            raise SystemExit("round: the verify workload must have the drafter's batch and "
+                             "at least its gamma")
+        V = case.V
+        dt = sv.BF16 if case.target.dtype == np.uint16 else sv.F32
+
+        def logits(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        tgt0 = logits(np.ascontiguousarray(case.target[:, :G + 1]))
+        rot_v = args.rotate or max(1, -(-ROTATE_BYTES // (tgt0.numel() * tgt0.element_size())))
+        tgts = [tgt0] + [tgt0.clone() for _ in range(rot_v - 1)]
+        uni = torch.from_numpy(np.ascontiguousarray(case.uniforms[:, :G + 1])).to(dev)
+        kv = torch.from_numpy(case.kv_len).to(dev)
+        vws = sv.Workspace(sv.workspace_bytes(B, G, V, dt, sv.POINT))
+        vout = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+        verifies = [sv.Prepared(t, None, d_tok, uni, d_len, kv, temperature=case.T,
+                                mode=sv.POINT, workspace=vws, out=vout) for t in tgts]
+        def verify(k):
+            verifies[k % rot_v]()
+
+        calls.append(verify)
+        # compulsory verify bytes: g_b + 1 target rows per row, g_b the draft length
+        e = tgt0.element_size()
+
+    gen_s = time.time() - t0
+
+    def step(k):
+        for c in calls:
+            c(k)
+
+    total_ms, wall = timed(step, K, args.warmup, stream, torch)
+    draft_ms, _ = timed(draft, K, args.warmup, stream, torch)
+    ms_per_step = total_ms / K
+    draft_us = draft_ms / K * 1e3
+    if case is not None:
+        # the verify alone, on the drafts the last step left
+        verify_ms, _ = timed(verify, K, args.warmup, stream, torch)
+    g_b = d_len.cpu().numpy()
+    n_b = d_n.cpu().numpy()
+    line_extra = {}
+    if args.mode == "round":
+        step_bytes = draft_bytes + int((g_b.astype(np.int64) + 1).sum()) * V * e
+        verify_us = verify_ms / K * 1e3
+        n_acc = vout[1].cpu().numpy()
+        emitted = int((n_acc + 1).sum())
+        kern_name, kern_us = (("verify_kernel", verify_us) if verify_us >= draft_us
+                              else ("ngram_kernel", draft_us))
+        kern_bytes = step_bytes - draft_bytes if kern_name == "verify_kernel" else draft_bytes
+        line_extra = {"verify_kernel_us": verify_us, "emitted_tokens_per_s":
+                      emitted * K / (total_ms * 1e-3), "mean_emitted_per_row": emitted / B,
+                      "diagnostics": vws.diagnostics()}
+    else:
+        kern_name, kern_us, kern_bytes = "ngram_kernel", draft_us, draft_bytes
+    achieved = kern_bytes / (kern_us * 1e-6) / 1e9
+    ceiling = read_ceiling(sv, torch, dev, stream, args.with_copy)
+
+    traffic = None
+    if kern_name == "ngram_kernel" and os.path.exists(NGRAM_COUNTERS.format(contexts=args.contexts)):
+        with open(NGRAM_COUNTERS.format(contexts=args.contexts)) as f:
+            cnt = json.load(f)
+        if cnt.get("source_sha256_16") == source_hash(NGRAM_SRC):
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and reps < 100000:
+            c0 = time.perf_counter()
+            oracle.ngram_draft(ctx, lens, n_min=cc.n_min, n_max=cc.n_max, gamma=G)
+            if case is not None:
+                w = oracle.ngram_draft(ctx, lens, n_min=cc.n_min, n_max=cc.n_max, gamma=G)
+                oracle.verify(case.target[:, :G + 1], None, np.maximum(w.draft, 0),
+                              case.uniforms[:, :G + 1], w.length, case.kv_len,
+                              temperature=case.T, mode=oracle.POINT, threads=1)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        what = "drafting" if case is None else "drafting + point verify (one core)"
+        cpu = {"value": B * reps / t_cpu, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} full batches of this workload ({B} rows each), "
+                         f"{t_cpu:.1f} s of oracle {what}"}
+
+    wl = (f"prompt-lookup drafting B={B} contexts {cc.L_lo}..{cc.stride} tokens "
+          f"n={cc.n_max}..{cc.n_min} gamma={G} ({args.contexts})")
+    if case is not None:
+        wl += f" + point verify V={V} bf16 T={case.T} (config {args.config})"
+    line = {
+        "metric": ("drafted rows/s (prompt-lookup drafting)" if case is None else
+                   "verified rows/s (model-free round: prompt-lookup draft + point verify)"),
+        "value": B * K / (total_ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32" if case is None else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl, "B": B, "stride": cc.stride, "gamma": G,
+                   "n_max": cc.n_max, "n_min": cc.n_min, "rotated_context_copies": rot_c,
+                   "rotated_logit_copies": rot_v, "compulsory_bytes_per_step": step_bytes},
+        "ngram_kernel_us": draft_us,
+        "draft_rows_matched": int((n_b > 0).sum()),
+        "mean_draft_len": float(g_b.mean()),
+        "step_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "read_ceiling_gbps": ceiling, "wall_s_timed": wall, "input_gen_s": gen_s,
+        **line_extra,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": kern_name, "bytes_per_launch": kern_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
 
 
 def main():
@@ -69,6 +279,9 @@ def main():
               "independent per batch row, so N GPUs would each run this same benchmark on "
               "their own rows", file=sys.stderr)
         sys.exit(2)
+    if args.mode in ("ngram", "round"):
+        bench_drafting(args)
+        return
 
     import numpy as np
     import torch
@@ -189,26 +402,7 @@ def main():
     emitted = int((n_acc + 1).sum())
     tested = int(np.minimum(n_acc + 1, case.gamma).sum())
 
-    # HBM read ceiling of this machine: plain streaming read of 4 GiB
-    probe = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
-    pout = None
-    for _ in range(3):
-        pout = sv.probe_read(probe, pout)
-    torch.cuda.synchronize()
-    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    pe0.record(stream)
-    for _ in range(10):
-        sv.probe_read(probe, pout)
-    pe1.record(stream)
-    torch.cuda.synchronize()
-    ceiling = probe.numel() * 10 / (pe0.elapsed_time(pe1) * 1e-3) / 1e9
-    if args.with_copy:
-        dst = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
-        for _ in range(5):
-            sv.probe_copy(probe[: 1 << 28], dst)
-        torch.cuda.synchronize()
-        del dst
-    del probe
+    ceiling = read_ceiling(sv, torch, dev, stream, args.with_copy)
 
     traffic = None
     counters = COUNTERS.format(kernel=kernel_name, config=args.config, mode=args.mode,

@@ -1,6 +1,7 @@
 """MI355X (gfx950) batched verify step of speculative decoding.
 
-Thin ctypes binding over the C ABI declared in include/spec_verify.h.  Every
+Thin ctypes binding over the C ABI declared in include/spec_verify.h and
+include/spec_ngram.h (prompt-lookup drafting).  Every
 step of the verify runs in the HIP kernels of libspecverify.so; this module
 only checks tensor shapes, allocates outputs with torch, and passes raw device
 pointers and the current HIP stream.  There is no CPU fallback: importing the
@@ -25,7 +26,9 @@ EXPORTS = (
     "spec_verify_workspace_reset", "spec_verify_plan", "spec_verify_tune",
     "spec_verify_diagnostics", "spec_verify_strerror", "spec_verify_version",
     "spec_probe_read", "spec_probe_read_blocks", "spec_probe_copy",
+    "spec_ngram_draft", "spec_ngram_workspace_bytes",
 )
+NGRAM_MAX_N, NGRAM_MAX_GAMMA, NGRAM_MAX_STRIDE = 64, 256, 1 << 25
 
 _lib = None
 
@@ -77,6 +80,10 @@ def load():
     lib.spec_probe_read_blocks.restype = i32
     lib.spec_probe_copy.argtypes = [P, P, sz, P]
     lib.spec_probe_copy.restype = i32
+    lib.spec_ngram_workspace_bytes.argtypes = [i32]
+    lib.spec_ngram_workspace_bytes.restype = sz
+    lib.spec_ngram_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    lib.spec_ngram_draft.restype = i32
     _lib = lib
     return lib
 
@@ -285,6 +292,42 @@ class Prepared:
         rc = self._fn(*self._args)
         if rc != OK:
             raise SpecVerifyError(rc, "spec_verify")
+
+
+def ngram_workspace_bytes(B: int) -> int:
+    return int(load().spec_ngram_workspace_bytes(B))
+
+
+def ngram_draft(context, ctx_len, *, n_min: int = 1, n_max: int = 4, gamma: int = 4,
+                workspace: Workspace | None = None, out=None, stream=None):
+    """spec_ngram_draft (prompt-lookup drafting) on torch device tensors:
+    context int32 [B, stride], ctx_len int32 [B].
+
+    Returns (draft [B, gamma], length [B], n [B], pos [B]), all int32; draft
+    and length are ready to pass to verify(mode=POINT) as draft_tokens and
+    gamma_per_row.  `out` may pass preallocated tensors in that order.  The
+    call is asynchronous on `stream` (default: torch's current stream)."""
+    torch = _torch()
+    if context.dim() != 2 or tuple(ctx_len.shape) != (context.shape[0],):
+        raise ValueError("context must be int32 [B, stride] and ctx_len int32 [B]")
+    for name, t in (("context", context), ("ctx_len", ctx_len)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be torch.int32")
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B, stride = context.shape
+    dev = context.device
+    if workspace is None:
+        workspace = Workspace(ngram_workspace_bytes(B), device=dev, stream=stream)
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               *(torch.empty(B, dtype=torch.int32, device=dev) for _ in range(3)))
+    draft, length, n, pos = out
+    _check(load().spec_ngram_draft(_ptr(context), _ptr(ctx_len), B, stride, int(n_min),
+                                   int(n_max), int(gamma), _ptr(draft), _ptr(length), _ptr(n),
+                                   _ptr(pos), ctypes.c_void_p(workspace.ptr), workspace.nbytes,
+                                   _stream_handle(stream)), "spec_ngram_draft")
+    return draft, length, n, pos
 
 
 def probe_read(src, out=None, stream=None):

@@ -1,4 +1,4 @@
-"""Build libspecverify.so in-tree with hipcc for gfx950."""
+"""Build libspecverify.so (verify and n-gram drafting) in-tree with hipcc for gfx950."""
 from __future__ import annotations
 
 import os
@@ -7,7 +7,7 @@ import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
-SRC = os.path.join(_HERE, "csrc", "spec_verify.hip")
+SRCS = [os.path.join(_HERE, "csrc", f) for f in ("spec_verify.hip", "spec_ngram.hip")]
 OUT = os.path.join(_HERE, "libspecverify.so")
 
 HIPCC_FLAGS = [
@@ -23,7 +23,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)

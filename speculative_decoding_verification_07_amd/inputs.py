@@ -270,3 +270,87 @@ def algorithmic_bytes(case: Case) -> int:
     g = np.clip(g, 0, case.G)
     rows = (g + 1) if case.mode in ("greedy", "point") else (2 * g + 1)
     return int(rows.sum()) * case.V * e
+
+
+# ------------------------------------------------------------ drafting contexts
+@dataclass(frozen=True)
+class ContextConfig:
+    """Token contexts for prompt-lookup drafting: B rows of up to `stride`
+    tokens, lengths ~ U{L_lo..stride}, vocabulary V."""
+    name: str
+    B: int
+    stride: int
+    L_lo: int
+    V: int
+    gamma: int
+    n_min: int
+    n_max: int
+    copy_prob: float = 0.5       # share of segments copied from earlier in the row
+    span: tuple = (4, 64)        # segment lengths ~ U{span}
+    zipf_s: float = 1.1          # token frequencies ~ 1 / rank^s
+
+
+CONTEXT_CONFIGS = {
+    # the measured workload: the verify workload's batch and draft length,
+    # long copy-heavy contexts (edit / summarisation / retrieval outputs)
+    "ctx32k": ContextConfig("ctx32k", B=64, stride=32768, L_lo=16384, V=128256, gamma=4,
+                            n_min=1, n_max=4),
+    # small: a few chunks per row, for element-by-element parity
+    "ctx5k": ContextConfig("ctx5k", B=32, stride=5000, L_lo=0, V=1000, gamma=6, n_min=1,
+                           n_max=5),
+}
+
+
+def make_contexts(cc: ContextConfig | str, rnd: int = 0, pad: str = "random", **overrides):
+    """Seeded token contexts (numpy Philox, SeedSequence([1000, round, 8])).
+
+    Each row is built segment by segment: with probability copy_prob a
+    segment repeats a span of the row's earlier tokens (the copying that
+    makes prompt lookup pay off), otherwise it draws fresh tokens with
+    Zipf(zipf_s) frequencies over a fixed random ranking of the vocabulary.
+    Tokens after a row's length are filler: random tokens (pad="random") or
+    repeats of the row's last tokens (pad="suffix", which would produce
+    matches if anything past the length were read).
+    Returns (context int32 [B, stride], lengths int32 [B])."""
+    if isinstance(cc, str):
+        cc = CONTEXT_CONFIGS[cc]
+    if overrides:
+        cc = replace(cc, **overrides)
+    g = np.random.Generator(np.random.Philox(np.random.SeedSequence([1000, rnd, 8])))
+    ranks = np.arange(1, cc.V + 1, dtype=np.float64)
+    cdf = np.cumsum(ranks ** -cc.zipf_s)
+    cdf /= cdf[-1]
+    perm = g.permutation(cc.V).astype(np.int32)
+    lens = g.integers(cc.L_lo, cc.stride + 1, size=cc.B).astype(np.int32)
+    ctx = np.empty((cc.B, cc.stride), np.int32)
+    lo, hi = cc.span
+    for b in range(cc.B):
+        row = ctx[b]
+        L = int(lens[b])
+        t = 0
+        while t < L:
+            n = min(int(g.integers(lo, hi + 1)), L - t)
+            if t > 0 and g.random() < cc.copy_prob:
+                s = int(g.integers(0, t))
+                for i in range(n):          # may overlap what it writes
+                    row[t + i] = row[s + i]
+            else:
+                u = g.random(n)
+                row[t:t + n] = perm[np.minimum(np.searchsorted(cdf, u), cc.V - 1)]
+            t += n
+        rest = cc.stride - L
+        if rest > 0:
+            if pad == "suffix" and L > 0:
+                tail = row[max(0, L - 8):L]
+                row[L:] = np.resize(tail, rest)
+            else:
+                row[L:] = g.integers(0, cc.V, size=rest)
+    return ctx, lens
+
+
+def context_bytes(lens: np.ndarray, gamma: int) -> int:
+    """Compulsory bytes of one drafting call: every token that can end an
+    occurrence (L - 1 per row, 4 bytes each), the length, and the outputs
+    (gamma + 3 int32 per row: draft, length, n, position)."""
+    L = np.clip(lens.astype(np.int64), 0, None)
+    return int((np.maximum(L - 1, 0) * 4).sum()) + len(L) * 4 * (1 + gamma + 3)
