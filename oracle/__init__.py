@@ -58,6 +58,8 @@ def _load():
         lib.oracle_filter_row.restype = i32
         lib.oracle_ngram_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P]
         lib.oracle_ngram_draft.restype = i32
+        lib.oracle_gamma_control.argtypes = [P, P, P, P, P, i32, i32, D, D, D, D, i32, P, P]
+        lib.oracle_gamma_control.restype = i32
         _lib = lib
     return _lib
 
@@ -203,3 +205,30 @@ def ngram_draft(context, ctx_len, *, n_min=1, n_max=4, gamma=4) -> DraftResult:
     if rc != 0:
         raise ValueError("oracle refused the drafting arguments")
     return DraftResult(draft, length, n, pos)
+
+
+def gamma_control(state, n_accepted=None, gamma_used=None, *, active=None, gamma_limit=None,
+                  gamma_max=4, decay=0.9, prior_alpha=0.6, prior_weight=2.0, draft_cost=0.05,
+                  batch_off=0):
+    """Adaptive draft length (see oracle_gamma_control in spec_oracle.c).
+
+    state: float64 [B, 2] {A, T}, updated in place.  n_accepted, gamma_used:
+    int32 [B] of the previous round (both None: no previous round).  Returns
+    (gamma int32 [B], alpha float64 [B])."""
+    lib = _load()
+    if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+            and state.flags.c_contiguous and state.ndim == 2 and state.shape[1] == 2):
+        raise ValueError("state must be a C-contiguous float64 [B, 2] array")
+    B = state.shape[0]
+    opt = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.int32).reshape(B)
+    n_accepted, gamma_used, active, gamma_limit = map(opt, (n_accepted, gamma_used, active,
+                                                            gamma_limit))
+    gamma = np.empty(B, np.int32)
+    alpha = np.empty(B, np.float64)
+    rc = lib.oracle_gamma_control(_ptr(n_accepted), _ptr(gamma_used), _ptr(active),
+                                  _ptr(gamma_limit), _ptr(state), B, int(gamma_max), float(decay),
+                                  float(prior_alpha), float(prior_weight), float(draft_cost),
+                                  int(batch_off), _ptr(gamma), _ptr(alpha))
+    if rc != 0:
+        raise ValueError("oracle refused the controller arguments")
+    return gamma, alpha

@@ -555,3 +555,84 @@ int oracle_ngram_draft(const int32_t* context, const int32_t* ctx_len, int B, in
   }
   return 0;
 }
+
+/* --------------------------------------------------------------- adaptive gamma
+ * Per-request draft length from running acceptance, speculation off at large
+ * batch ("Speculative decoding", mhtirogla.ai, "Efficiency" and
+ * "Implementation notes": expected tokens per pass, wall-clock speedup
+ * E / (1 + gamma c), gamma adaptive per request from running acceptance and
+ * off once the batch is compute-bound; blog.lo0.es "When speculative does
+ * NOT help": the large-batch crossover; tusharamrit "Speculative decoding":
+ * adapt gamma from recent acceptance, speedup table; dantp-ai "How much
+ * speedup, really?": an optimal lookahead for every acceptance rate).
+ * Reading:
+ *   state per row: discounted accepted count A and tested count T.
+ *   observation of a round with g = gamma_used[b] >= 1 and n = n_acc[b] >= 0:
+ *     the walk tested min(n + 1, g) drafts and accepted n of them;
+ *     A <- d A + n,  T <- d T + min(n + 1, g).
+ *   a row without an observation (g = 0, n < 0, or no previous round) only
+ *   ages its evidence: A <- d A, T <- d T.  Inactive rows are left alone.
+ *   running acceptance  alpha = (A + w0 alpha0) / (T + w0)  (alpha0 when
+ *   T + w0 = 0).
+ *   E(gamma) = sum_{i=0..gamma} alpha^i   (tokens per pass, page formula)
+ *   gamma_b = the smallest gamma in [0, min(gamma_max, limit_b)] maximising
+ *     E(gamma) / (1 + gamma c), compared without division:
+ *     E(g1) (1 + g2 c) > E(g2) (1 + g1 c).
+ *   If the number of active rows is >= batch_off (batch_off >= 1), every
+ *   row gets gamma 0 (its state is still updated).
+ * Inactive rows (active[b] == 0) get gamma 0 and keep their state.
+ * state: double [B][2] {A, T}, updated in place.  out_alpha (optional): the
+ * alpha each active row's choice used.  Returns 0, or -1 for refused
+ * arguments. */
+int oracle_gamma_control(const int32_t* n_acc, const int32_t* gamma_used, const int32_t* active,
+                         const int32_t* gamma_limit, double* state, int B, int gamma_max,
+                         double decay, double prior_alpha, double prior_weight, double draft_cost,
+                         int batch_off, int32_t* out_gamma, double* out_alpha) {
+  if (!state || !out_gamma || B < 0 || gamma_max < 0) return -1;
+  if ((n_acc == NULL) != (gamma_used == NULL)) return -1;
+  if (!(decay >= 0.0 && decay <= 1.0) || !(prior_alpha >= 0.0 && prior_alpha <= 1.0)) return -1;
+  if (!(prior_weight >= 0.0) || !(draft_cost >= 0.0) || isinf(prior_weight) || isinf(draft_cost))
+    return -1;
+  if (batch_off < 0) return -1;
+  int n_active = 0;
+  for (int b = 0; b < B; ++b) n_active += !active || active[b] != 0;
+  const int off = batch_off >= 1 && n_active >= batch_off;
+  for (int b = 0; b < B; ++b) {
+    out_gamma[b] = 0;
+    if (out_alpha) out_alpha[b] = 0.0;
+    if (active && active[b] == 0) continue;
+    double A = state[2 * b], T = state[2 * b + 1];
+    const int g = gamma_used ? gamma_used[b] : 0;
+    const int n = n_acc ? n_acc[b] : -1;
+    if (g >= 1 && n >= 0 && n <= g) {
+      const int tested = n + 1 < g ? n + 1 : g;
+      A = decay * A + (double)n;
+      T = decay * T + (double)tested;
+    } else {
+      A = decay * A;
+      T = decay * T;
+    }
+    state[2 * b] = A;
+    state[2 * b + 1] = T;
+    const double den = T + prior_weight;
+    const double alpha = den > 0.0 ? (A + prior_weight * prior_alpha) / den : prior_alpha;
+    if (out_alpha) out_alpha[b] = alpha;
+    if (off) continue;
+    int cap = gamma_max;
+    if (gamma_limit && gamma_limit[b] < cap) cap = gamma_limit[b] < 0 ? 0 : gamma_limit[b];
+    /* E(0) = 1; E(k) = E(k-1) + alpha^k */
+    double best_e = 1.0, pw = 1.0, e = 1.0;
+    int best = 0;
+    for (int k = 1; k <= cap; ++k) {
+      pw = pw * alpha;
+      e = e + pw;
+      /* e / (1 + k c) > best_e / (1 + best c) */
+      if (e * (1.0 + (double)best * draft_cost) > best_e * (1.0 + (double)k * draft_cost)) {
+        best = k;
+        best_e = e;
+      }
+    }
+    out_gamma[b] = best;
+  }
+  return 0;
+}
