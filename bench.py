@@ -21,7 +21,10 @@ timed alone, and the roofline names the longer of the two kernels.
 contexts of 16k..32k tokens, n = 4..1, gamma = 4; context copies rotated like
 the logits).  --mode round times a whole model-free speculative round: the
 drafter, then the point-mode verify of its drafts against the B=64,
-V=128256 target logits, both launches on one stream.
+V=128256 target logits, both launches on one stream; with --adapt the
+draft-length controller runs between them (capped by the draft lengths, fed
+the previous round's accepted counts).  --mode adapt times the controller
+alone over the same 64 rows.
 """
 from __future__ import annotations
 
@@ -46,6 +49,9 @@ KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_07_amd", "csr
 NGRAM_SRC = os.path.join(ROOT, "speculative_decoding_verification_07_amd", "csrc",
                          "spec_ngram.hip")
 NGRAM_COUNTERS = os.path.join(ROOT, "profiles", "ngram_kernel_{contexts}_counters.json")
+# controller bytes per row: accepted count, previous length, length limit
+# and state {A, T} read; length and state written
+CONTROL_BYTES_PER_ROW = 4 + 4 + 4 + 16 + 4 + 16
 
 
 def parse():
@@ -55,7 +61,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3)")
     ap.add_argument("--mode", default="sample",
-                    choices=["sample", "greedy", "point", "ngram", "round"])
+                    choices=["sample", "greedy", "point", "ngram", "round", "adapt"])
+    ap.add_argument("--adapt", action="store_true",
+                    help="round: insert the adaptive draft-length controller")
+    ap.add_argument("--draft-cost", type=float, default=0.05,
+                    help="controller: cost of one draft token, in target passes")
     ap.add_argument("--contexts", default="ctx32k", help="drafting workload (ngram, round)")
     ap.add_argument("--top-k", type=int, default=0, help="top-k filter of p and q (0: off)")
     ap.add_argument("--top-p", type=float, default=1.0, help="top-p filter of p and q (1: off)")
@@ -151,8 +161,24 @@ def bench_drafting(args):
     def draft(k):
         lib.spec_ngram_draft(*dargs[k % rot_c])
 
+    # the controller: previous round's counts in, this round's lengths out
+    # (in place), capped by the draft lengths
+    ctl = sv.GammaControl(B, gamma_max=G, draft_cost=args.draft_cost)
+    c_nacc = torch.full((B,), -1, dtype=torch.int32, device=dev)
+    c_gam = torch.zeros(B, dtype=torch.int32, device=dev)
+    ctl(c_nacc, c_gam, gamma_limit=d_len, out=c_gam)  # argument checks, once
+    cargs = (P(c_nacc.data_ptr()), P(c_gam.data_ptr()), None, P(d_len.data_ptr()),
+             P(ctl.state.data_ptr()), B, *ctl.params,
+             P(c_gam.data_ptr()), None, hs)
+
+    def control(k):
+        lib.spec_gamma_control(*cargs)
+
     K = args.steps
+    adapt = args.mode == "adapt" or (args.mode == "round" and args.adapt)
     calls, case, step_bytes, rot_v = [draft], None, draft_bytes, 0
+    if args.mode == "adapt":
+        calls, step_bytes = [control], B * CONTROL_BYTES_PER_ROW
     if args.mode == "round":
         case = inputs.make_case(args.config, rnd=0, mode="point")
         if case.G < G or case.B != B:
@@ -175,11 +201,15 @@ def bench_drafting(args):
         vout = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
                 torch.empty(B, dtype=torch.int32, device=dev),
                 torch.empty(B, dtype=torch.int32, device=dev))
-        verifies = [sv.Prepared(t, None, d_tok, uni, d_len, kv, temperature=case.T,
-                                mode=sv.POINT, workspace=vws, out=vout) for t in tgts]
+        vout = (vout[0], c_nacc, vout[2]) if adapt else vout
+        verifies = [sv.Prepared(t, None, d_tok, uni, c_gam if adapt else d_len, kv,
+                                temperature=case.T, mode=sv.POINT, workspace=vws, out=vout)
+                    for t in tgts]
         def verify(k):
             verifies[k % rot_v]()
 
+        if adapt:
+            calls.append(control)
         calls.append(verify)
         # compulsory verify bytes: g_b + 1 target rows per row, g_b the draft length
         e = tgt0.element_size()
@@ -192,6 +222,10 @@ def bench_drafting(args):
 
     total_ms, wall = timed(step, K, args.warmup, stream, torch)
     draft_ms, _ = timed(draft, K, args.warmup, stream, torch)
+    control_us = None
+    if adapt:
+        control_ms, _ = timed(control, K, args.warmup, stream, torch)
+        control_us = control_ms / K * 1e3
     ms_per_step = total_ms / K
     draft_us = draft_ms / K * 1e3
     if case is not None:
@@ -199,18 +233,24 @@ def bench_drafting(args):
         verify_ms, _ = timed(verify, K, args.warmup, stream, torch)
     g_b = d_len.cpu().numpy()
     n_b = d_n.cpu().numpy()
-    line_extra = {}
+    line_extra = {"control_kernel_us": control_us} if adapt else {}
+    if adapt:
+        line_extra["mean_controlled_gamma"] = float(c_gam.float().mean())
     if args.mode == "round":
-        step_bytes = draft_bytes + int((g_b.astype(np.int64) + 1).sum()) * V * e
+        g_v = (c_gam if adapt else d_len).cpu().numpy().astype(np.int64)
+        step_bytes = (draft_bytes + int((g_v + 1).sum()) * V * e
+                      + (B * CONTROL_BYTES_PER_ROW if adapt else 0))
         verify_us = verify_ms / K * 1e3
         n_acc = vout[1].cpu().numpy()
         emitted = int((n_acc + 1).sum())
         kern_name, kern_us = (("verify_kernel", verify_us) if verify_us >= draft_us
                               else ("ngram_kernel", draft_us))
-        kern_bytes = step_bytes - draft_bytes if kern_name == "verify_kernel" else draft_bytes
-        line_extra = {"verify_kernel_us": verify_us, "emitted_tokens_per_s":
-                      emitted * K / (total_ms * 1e-3), "mean_emitted_per_row": emitted / B,
-                      "diagnostics": vws.diagnostics()}
+        kern_bytes = int((g_v + 1).sum()) * V * e if kern_name == "verify_kernel" else draft_bytes
+        line_extra.update({"verify_kernel_us": verify_us, "emitted_tokens_per_s":
+                           emitted * K / (total_ms * 1e-3), "mean_emitted_per_row": emitted / B,
+                           "diagnostics": vws.diagnostics()})
+    elif args.mode == "adapt":
+        kern_name, kern_us, kern_bytes = "gamma_kernel", control_us, step_bytes
     else:
         kern_name, kern_us, kern_bytes = "ngram_kernel", draft_us, draft_bytes
     achieved = kern_bytes / (kern_us * 1e-6) / 1e9
@@ -227,33 +267,53 @@ def bench_drafting(args):
     if not args.no_cpu:
         import oracle
         reps, t_cpu = 0, 0.0
+        ost = np.zeros((B, 2))
+        o_n = np.full(B, -1, np.int32)
+        o_g = np.zeros(B, np.int32)
         while t_cpu < args.cpu_seconds and reps < 100000:
             c0 = time.perf_counter()
-            oracle.ngram_draft(ctx, lens, n_min=cc.n_min, n_max=cc.n_max, gamma=G)
-            if case is not None:
+            if args.mode == "adapt":
+                oracle.gamma_control(ost, o_n, o_g, gamma_limit=g_b, gamma_max=G,
+                                     draft_cost=args.draft_cost)
+            else:
                 w = oracle.ngram_draft(ctx, lens, n_min=cc.n_min, n_max=cc.n_max, gamma=G)
-                oracle.verify(case.target[:, :G + 1], None, np.maximum(w.draft, 0),
-                              case.uniforms[:, :G + 1], w.length, case.kv_len,
-                              temperature=case.T, mode=oracle.POINT, threads=1)
+            if case is not None:
+                gv = w.length
+                if adapt:
+                    gv, _ = oracle.gamma_control(ost, o_n, o_g, gamma_limit=w.length,
+                                                 gamma_max=G, draft_cost=args.draft_cost)
+                r = oracle.verify(case.target[:, :G + 1], None, np.maximum(w.draft, 0),
+                                  case.uniforms[:, :G + 1], gv, case.kv_len,
+                                  temperature=case.T, mode=oracle.POINT, threads=1)
+                o_n, o_g = r.n_accepted, gv
             t_cpu += time.perf_counter() - c0
             reps += 1
-        what = "drafting" if case is None else "drafting + point verify (one core)"
+        what = {"ngram": "drafting", "adapt": "draft-length control",
+                "round": "drafting + " + ("control + " if adapt else "") + "point verify"}[args.mode]
         cpu = {"value": B * reps / t_cpu, "unit": "rows/s", "cores": 1, "kind": "oracle",
                "sample": f"{reps} full batches of this workload ({B} rows each), "
                          f"{t_cpu:.1f} s of oracle {what}"}
 
     wl = (f"prompt-lookup drafting B={B} contexts {cc.L_lo}..{cc.stride} tokens "
           f"n={cc.n_max}..{cc.n_min} gamma={G} ({args.contexts})")
+    if adapt:
+        wl += f" + adaptive gamma (draft cost {args.draft_cost})"
+    if args.mode == "adapt":
+        wl = (f"adaptive draft length B={B} gamma_max={G} draft cost {args.draft_cost}, "
+              f"capped by the {args.contexts} draft lengths")
     if case is not None:
         wl += f" + point verify V={V} bf16 T={case.T} (config {args.config})"
+    metric = {"ngram": "drafted rows/s (prompt-lookup drafting)",
+              "adapt": "controlled rows/s (adaptive draft length)",
+              "round": "verified rows/s (model-free round: prompt-lookup draft + "
+                       + ("adaptive gamma + " if adapt else "") + "point verify)"}[args.mode]
     line = {
-        "metric": ("drafted rows/s (prompt-lookup drafting)" if case is None else
-                   "verified rows/s (model-free round: prompt-lookup draft + point verify)"),
+        "metric": metric,
         "value": B * K / (total_ms * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int32" if case is None else "f32",
+        "dtype": {"ngram": "int32", "adapt": "f64", "round": "f32"}[args.mode],
         "data": "synthetic",
         "config": {"workload": wl, "B": B, "stride": cc.stride, "gamma": G,
                    "n_max": cc.n_max, "n_min": cc.n_min, "rotated_context_copies": rot_c,
@@ -279,7 +339,7 @@ def main():
               "independent per batch row, so N GPUs would each run this same benchmark on "
               "their own rows", file=sys.stderr)
         sys.exit(2)
-    if args.mode in ("ngram", "round"):
+    if args.mode in ("ngram", "round", "adapt"):
         bench_drafting(args)
         return
 

@@ -1,7 +1,8 @@
 """MI355X (gfx950) batched verify step of speculative decoding.
 
-Thin ctypes binding over the C ABI declared in include/spec_verify.h and
-include/spec_ngram.h (prompt-lookup drafting).  Every
+Thin ctypes binding over the C ABI declared in include/spec_verify.h,
+include/spec_ngram.h (prompt-lookup drafting) and include/spec_adapt.h
+(adaptive draft length).  Every
 step of the verify runs in the HIP kernels of libspecverify.so; this module
 only checks tensor shapes, allocates outputs with torch, and passes raw device
 pointers and the current HIP stream.  There is no CPU fallback: importing the
@@ -26,7 +27,7 @@ EXPORTS = (
     "spec_verify_workspace_reset", "spec_verify_plan", "spec_verify_tune",
     "spec_verify_diagnostics", "spec_verify_strerror", "spec_verify_version",
     "spec_probe_read", "spec_probe_read_blocks", "spec_probe_copy",
-    "spec_ngram_draft", "spec_ngram_workspace_bytes",
+    "spec_ngram_draft", "spec_ngram_workspace_bytes", "spec_gamma_control",
 )
 NGRAM_MAX_N, NGRAM_MAX_GAMMA, NGRAM_MAX_STRIDE = 64, 256, 1 << 25
 
@@ -84,6 +85,9 @@ def load():
     lib.spec_ngram_workspace_bytes.restype = sz
     lib.spec_ngram_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     lib.spec_ngram_draft.restype = i32
+    d = ctypes.c_double
+    lib.spec_gamma_control.argtypes = [P, P, P, P, P, i32, i32, d, d, d, d, i32, P, P, P]
+    lib.spec_gamma_control.restype = i32
     _lib = lib
     return lib
 
@@ -328,6 +332,43 @@ def ngram_draft(context, ctx_len, *, n_min: int = 1, n_max: int = 4, gamma: int 
                                    _ptr(pos), ctypes.c_void_p(workspace.ptr), workspace.nbytes,
                                    _stream_handle(stream)), "spec_ngram_draft")
     return draft, length, n, pos
+
+
+class GammaControl:
+    """spec_gamma_control with its parameters fixed: the running-acceptance
+    state of B request slots (float64 [B, 2] on the device, zero-filled) and
+    one call per round.  Zero a slot's row of `state` when it takes a new
+    request."""
+
+    def __init__(self, B: int, *, gamma_max: int = 4, decay: float = 0.9,
+                 prior_alpha: float = 0.6, prior_weight: float = 2.0, draft_cost: float = 0.05,
+                 batch_off: int = 0, device="cuda"):
+        torch = _torch()
+        self.B = int(B)
+        self.params = (int(gamma_max), float(decay), float(prior_alpha), float(prior_weight),
+                       float(draft_cost), int(batch_off))
+        self.state = torch.zeros((self.B, 2), dtype=torch.float64, device=device)
+
+    def __call__(self, n_accepted=None, gamma_used=None, *, active=None, gamma_limit=None,
+                 out=None, alpha=None, stream=None):
+        """Returns out_gamma (int32 [B]); `alpha`, if given, receives the
+        running acceptance (float64 [B])."""
+        torch = _torch()
+        for name, t in (("n_accepted", n_accepted), ("gamma_used", gamma_used),
+                        ("active", active), ("gamma_limit", gamma_limit)):
+            if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (self.B,)
+                                  or not t.is_contiguous() or not t.is_cuda):
+                raise ValueError(f"{name} must be a contiguous int32 [B] device tensor")
+        if alpha is not None and (alpha.dtype != torch.float64 or tuple(alpha.shape) != (self.B,)):
+            raise ValueError("alpha must be float64 [B]")
+        if out is None:
+            out = torch.empty(self.B, dtype=torch.int32, device=self.state.device)
+        g, decay, pa, pw, c, off = self.params
+        _check(load().spec_gamma_control(_ptr(n_accepted), _ptr(gamma_used), _ptr(active),
+                                         _ptr(gamma_limit), _ptr(self.state), self.B, g, decay,
+                                         pa, pw, c, off, _ptr(out), _ptr(alpha),
+                                         _stream_handle(stream)), "spec_gamma_control")
+        return out
 
 
 def probe_read(src, out=None, stream=None):

@@ -1,4 +1,5 @@
-"""Build libspecverify.so (verify and n-gram drafting) in-tree with hipcc for gfx950."""
+"""Build libspecverify.so (verify, n-gram drafting, adaptive draft length)
+in-tree with hipcc for gfx950."""
 from __future__ import annotations
 
 import os
@@ -7,7 +8,8 @@ import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
-SRCS = [os.path.join(_HERE, "csrc", f) for f in ("spec_verify.hip", "spec_ngram.hip")]
+SRCS = [os.path.join(_HERE, "csrc", f)
+        for f in ("spec_verify.hip", "spec_ngram.hip", "spec_adapt.hip")]
 OUT = os.path.join(_HERE, "libspecverify.so")
 
 HIPCC_FLAGS = [
