@@ -1708,8 +1708,22 @@ __device__ __forceinline__ void row_for_each(const char* row, int V, F f) {
   });
 }
 
+// Histogram bin of a weight 2^e (e <= about 0): bins 1/8 of a unit of e
+// wide, the largest weights in the top bin, everything 2^-32 and below in
+// bin 0.  Monotone in e, so a bin is a range of values and equal values share
+// one.
+__device__ __forceinline__ int pmass_bin(float e) {
+  const float d = fminf(fmaxf(-e * 8.f, 0.f), (float)(kFBins - 1));
+  return kFBins - 1 - (int)d;
+}
+
+// The weight 2^e in fixed point: trunc(ex2(e) * 2^42).
+__device__ __forceinline__ unsigned long long fixed_mass_e(float e) {
+  return (unsigned long long)((double)ex2(e) * kMassUnit);
+}
+
 __device__ __forceinline__ unsigned long long fixed_mass(float l, float k2, float R) {
-  return (unsigned long long)((double)ex2(fmaf(l, k2, -R)) * kMassUnit);
+  return fixed_mass_e(fmaf(l, k2, -R));
 }
 
 template <int DT>
@@ -1736,11 +1750,13 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
   // A floor under the threshold, so that the selection can work on the
   // entries above it only.  top-k (k <= threads): the k-th largest of the
   // threads' maxima over the first quarter of the row, since k distinct
-  // entries reach it.  top-p alone: every entry below mx - D weighs under
-  // 2^(-D k2) of the largest, so all of them together weigh under
-  // V 2^(-D k2) <= (1 - top_p) of the row's mass (at least the largest
-  // entry's); the top-p set therefore lies above mx - D.
+  // entries reach it.  top-p alone: a histogram of the row's masses over
+  // bins of the weight's exponent (1/8 of a unit wide) finds the bin the
+  // threshold lies in and the exact mass above it; only that bin's entries
+  // become candidates.
   float floor_v = NEG_INF, mx = NEG_INF;
+  int p_bin = -1;          // top-p alone: the bin holding the threshold
+  uint64_t p_need = 0;     // and the mass still needed within it
   if (use_k && a.top_k <= kFThreads) {
     float tm = NEG_INF;
     row_for_each_v<DT>(row, a.V, 4, [&](float l) { tm = fmaxf(tm, l); }, [&](const float* fe) {
@@ -1762,8 +1778,32 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
     float tm = NEG_INF;
     row_for_each<DT>(row, a.V, [&](float l) { tm = fmaxf(tm, l); });
     mx = fblock_max(tm, L);
-    const double D = (log2((double)a.V) - log2(1.0 - (double)a.top_p)) / (double)a.k2 + 2.0;
-    if (mx != NEG_INF) floor_v = (float)((double)mx - D);
+    if (mx == NEG_INF) {  // a dead row: the walk reports it
+      if (t == 0) *out = NEG_INF;
+      return;
+    }
+    const float Rp = ref_of(mx, a.k2);
+    for (int i = t; i < kFBins; i += kFThreads) L.h[i] = 0;
+    __syncthreads();
+    unsigned long long ws = 0;
+    // every entry is added (a zero mass adds nothing): no branch per entry
+    auto hist = [&](float l) {
+      const float e = fmaf(l, a.k2, -Rp);
+      const unsigned long long w = fixed_mass_e(e);
+      ws += w;
+      atomicAdd(&L.h[pmass_bin(e)], w);
+    };
+    row_for_each_v<DT>(row, a.V, 1, hist, [&](const float* fe) {
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) hist(fe[e]);
+    });
+    __syncthreads();
+    uint64_t incl, excl, W;
+    fblock_scan(ws, L, incl, excl, W);
+    uint64_t need = (uint64_t)ceil((double)a.top_p * (double)W), above, total;
+    if (need < 1) need = 1;
+    p_bin = find_cross(L, kFBins, need, above, total);
+    p_need = need - above;
   }
   // (the key floor: float comparisons tie -0 with +0, keys put -0 first)
   const uint32_t floor_key =
@@ -1775,52 +1815,73 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
   // value; the total mass when top-p runs alone (its largest value is known
   // by now).  A float compare selects them (it also takes -0 against a +0
   // floor: a harmless extra candidate).
-  const bool need_w = use_p && !use_k;
-  const float Rw = need_w && mx != NEG_INF ? ref_of(mx, a.k2) : 0.f;
-  unsigned long long wsum = 0;
+  const bool p_alone = use_p && !use_k;
   float tm2 = NEG_INF;
   unsigned mine = 0;
   uint32_t* slots = L.cand + t * kFSlots;
-  // (two instantiations: the total mass only when top-p runs alone; a
-  // uniform test inside the loop would cost its conversions on every entry)
-  auto candidates = [&](auto with_w) {
-    constexpr bool kW = decltype(with_w)::value;
-    auto one = [&](float l) {
-      tm2 = fmaxf(tm2, l);
-      if (kW) wsum += fixed_mass(l, a.k2, Rw);
-      if (l >= floor_v) {
-        if (mine < (unsigned)kFSlots) slots[mine] = fkey(l);
-        ++mine;
-      }
+  // (two instantiations: the threshold's bin when top-p runs alone, the
+  // floor otherwise; a uniform test inside the loop would cost on every entry)
+  auto candidates = [&](auto in_bin) {
+    constexpr bool kBin = decltype(in_bin)::value;
+    const float Rp = kBin ? ref_of(mx, a.k2) : 0.f;
+    // the bin's value range, widened: only entries inside it take the
+    // exact bin test
+    float lo = NEG_INF, hi = INFINITY;
+    if (kBin) {
+      const float e_lo = -(float)(kFBins - p_bin) * 0.125f, e_hi = e_lo + 0.125f;
+      if (p_bin > 0) lo = (Rp + e_lo) / a.k2;
+      if (p_bin < kFBins - 1) hi = (Rp + e_hi) / a.k2;
+      lo -= 1e-3f * (1.f + fabsf(lo));
+      hi += 1e-3f * (1.f + fabsf(hi));
+    }
+    // bins as the histogram made them; an extra entry of zero mass at the
+    // bottom is harmless (it weighs nothing in the selection)
+    auto keep = [&](float l) {
+      if (kBin && pmass_bin(fmaf(l, a.k2, -Rp)) != p_bin) return;
+      if (mine < (unsigned)kFSlots) slots[mine] = fkey(l);
+      ++mine;
     };
+    auto one = [&](float l) {
+      if (!kBin) tm2 = fmaxf(tm2, l);
+      if (kBin ? (l >= lo) & (l <= hi) : l >= floor_v) keep(l);
+    };
+    // top-p alone, per vector: a mask of the entries in the bin's range,
+    // and one (rarely taken) branch for the vector
     row_for_each_v<DT>(row, a.V, 1, one, [&](const float* fe) {
+      if (kBin) {
+        unsigned in = 0;
 #pragma unroll
-      for (int e = 0; e < E::kVec; ++e) one(fe[e]);
+        for (int e = 0; e < E::kVec; ++e) in |= (unsigned)((fe[e] >= lo) & (fe[e] <= hi)) << e;
+        if (in) {
+#pragma unroll
+          for (int e = 0; e < E::kVec; ++e)
+            if ((in >> e) & 1u) keep(fe[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E::kVec; ++e) one(fe[e]);
+      }
     });
   };
-  if (need_w)
+  if (p_alone)
     candidates(std::integral_constant<bool, true>{});
   else
     candidates(std::integral_constant<bool, false>{});
   L.ccount[t] = mine;
-  mx = fblock_max(tm2, L);
+  if (!p_alone) mx = fblock_max(tm2, L);  // (top-p alone: known from its first pass)
   if (mx == NEG_INF) {  // a dead row: the walk reports it
     if (t == 0) *out = NEG_INF;
     return;
   }
   const float R = ref_of(mx, a.k2);
-  uint64_t w_all = 0;
-  if (use_p && !use_k) {
-    uint64_t incl, excl;
-    fblock_scan(wsum, L, incl, excl, w_all);
-  }
   __syncthreads();
   const bool listed = __syncthreads_and(mine <= (unsigned)kFSlots) != 0;  // else: whole-row passes
 
   // radix selection over the candidates (or the row): `mass` weighs each
   // entry by its fixed-point mass, else 1; only keys >= floor_key2 count.
   // W: the mass the top-p target is a fraction of (0: the histogram's total)
-  auto select = [&](bool mass, uint64_t need, uint32_t floor_key2, uint64_t W) -> uint32_t {
+  auto select = [&](bool mass, uint64_t need, uint32_t floor_key2, uint64_t W,
+                    bool given) -> uint32_t {
     uint32_t prefix = 0, pmask = 0;
     for (int lv = 0; lv < Lv::N; ++lv) {
       const int sh = Lv::shift(lv), nb = 1 << Lv::bits(lv);
@@ -1840,7 +1901,7 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
       }
       __syncthreads();
       uint64_t above, total;
-      if (mass && lv == 0) {
+      if (mass && lv == 0 && !given) {
         // the target: top_p of the mass kept so far, rounded up to a unit
         if (W == 0) {
           uint64_t sum = 0, incl, excl;
@@ -1858,11 +1919,15 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
     return prefix;
   };
   uint32_t key = 0;
-  if (use_k) key = select(false, (uint64_t)a.top_k, floor_key, 0);
+  if (use_k) key = select(false, (uint64_t)a.top_k, floor_key, 0, false);
   if (use_p) {
-    // top-k kept: its own mass (all of it is among the candidates); top-p
-    // alone: the whole row's
-    const uint32_t kp = select(true, 0, use_k ? key : floor_key, use_k ? 0 : w_all);
+    // top-k kept: top_p of its own mass (all of it is among the
+    // candidates); top-p alone: the mass still needed within the
+    // threshold's bin (its candidates; the whole row, with the row's
+    // target, when they overflow)
+    const uint32_t kp = p_alone ? (listed ? select(true, p_need, 0, 0, true)
+                                          : select(true, 0, 0, 0, false))
+                                : select(true, 0, key, 0, false);
     key = kp > key ? kp : key;
   }
   // a bf16 key's low 16 bits: zero for positive values, all ones for negative

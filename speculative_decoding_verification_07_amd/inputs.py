@@ -295,6 +295,10 @@ CONTEXT_CONFIGS = {
     # long copy-heavy contexts (edit / summarisation / retrieval outputs)
     "ctx32k": ContextConfig("ctx32k", B=64, stride=32768, L_lo=16384, V=128256, gamma=4,
                             n_min=1, n_max=4),
+    # long contexts (retrieval-sized inputs): where the bytes, not the
+    # launch, set the time
+    "ctx128k": ContextConfig("ctx128k", B=64, stride=131072, L_lo=65536, V=128256, gamma=4,
+                             n_min=1, n_max=4),
     # small: a few chunks per row, for element-by-element parity
     "ctx5k": ContextConfig("ctx5k", B=32, stride=5000, L_lo=0, V=1000, gamma=6, n_min=1,
                            n_max=5),

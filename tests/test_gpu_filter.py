@@ -101,17 +101,30 @@ def test_filtered_parity_small(torch, cfg, mode, kw, top_k, top_p):
         _check(case, torch)
 
 
-@pytest.mark.parametrize("cfg,mode", [(3, "sample"), (3, "point"), (5, "sample")])
-def test_filtered_parity_full_size(torch, cfg, mode):
-    """The workloads at full size with top-k = 50, top-p = 0.9."""
+@pytest.mark.parametrize("cfg,mode,top_k,top_p", [(3, "sample", 50, 0.9), (3, "point", 50, 0.9),
+                                                  (5, "sample", 50, 0.9), (3, "sample", 0, 0.9),
+                                                  (4, "point", 0, 0.95)])
+def test_filtered_parity_full_size(torch, cfg, mode, top_k, top_p):
+    """The workloads at full size with top-k = 50, top-p = 0.9, and with
+    top-p alone."""
+    top_p = float(np.float32(top_p))
     total = parity.Report()
     for rnd in range(2):
-        case = filtered_case(cfg, 300 + rnd, mode, 50, 0.9)
+        case = filtered_case(cfg, 300 + rnd, mode, top_k, top_p)
         print(f"filtered full cfg={cfg} mode={mode} rnd={rnd}", flush=True)
         tok, n, ln, pr = run(case, torch, probe=True)
         total.merge(parity.compare(case, tok, n, ln, pr))
     print(total.summary(), flush=True)
     assert total.ok, (total.summary(), total.mismatched[:5], total.prob_errors[:5])
+
+
+@pytest.mark.parametrize("top_p", [0.9, 0.5, 0.99, 0.999])
+def test_thresholds_full_vocab_top_p(torch, top_p):
+    """Top-p alone over full 128,256-entry rows (the threshold's bin among
+    realistic bin populations), bit-exact."""
+    top_p = float(np.float32(top_p))
+    case = inputs.make_case(3, rnd=70, B=6)
+    _thresholds_match(case, torch, 0, top_p)
 
 
 def test_filtered_edges(torch):

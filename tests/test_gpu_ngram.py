@@ -61,10 +61,12 @@ def test_copy_contexts_small(rnd):
     assert len(set(want.n.tolist())) >= 3      # a mix of match lengths
 
 
-@pytest.mark.parametrize("rnd", [0, 1, 2])
-def test_full_size(rnd):
-    """The measured workload (64 rows of 16k..32k tokens), every row."""
-    cc = inputs.CONTEXT_CONFIGS["ctx32k"]
+@pytest.mark.parametrize("name,rnd", [("ctx32k", 0), ("ctx32k", 1), ("ctx32k", 2),
+                                      ("ctx128k", 0)])
+def test_full_size(name, rnd):
+    """The measured workloads (64 rows of 16k..32k and 64k..128k tokens),
+    every row."""
+    cc = inputs.CONTEXT_CONFIGS[name]
     ctx, lens = inputs.make_contexts(cc, rnd=rnd, pad="suffix")
     check(ctx, lens, cc.n_min, cc.n_max, cc.gamma)
 
