@@ -1591,7 +1591,8 @@ __device__ float fblock_max(float v, FLds& L) {
 
 // Inclusive / exclusive prefix sums over the workgroup's threads and the
 // total (unsigned 64-bit, exact).
-__device__ void fblock_scan(uint64_t v, FLds& L, uint64_t& incl, uint64_t& excl, uint64_t& total) {
+__device__ __forceinline__ void fblock_scan(uint64_t v, FLds& L, uint64_t& incl, uint64_t& excl,
+                                            uint64_t& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint64_t prev;
   const uint64_t x = wave_scan_u64(v, prev);
@@ -1612,7 +1613,8 @@ __device__ void fblock_scan(uint64_t v, FLds& L, uint64_t& incl, uint64_t& excl,
 // which the running sum reaches `need`; `above` = the sum of the digits above
 // it, `total` = the sum of all.  need <= total is the caller's guarantee; if
 // it did not hold, the lowest non-empty digit is returned.
-__device__ int find_cross(FLds& L, int nb, uint64_t need, uint64_t& above, uint64_t& total) {
+__device__ __forceinline__ int find_cross(FLds& L, int nb, uint64_t need, uint64_t& above,
+                                           uint64_t& total) {
   const int t = threadIdx.x;
   const int per = nb > kFThreads ? nb / kFThreads : 1;
   const int top = nb - 1 - t * per;  // this thread's digits: top, top-1, ..., top-per+1
@@ -1818,55 +1820,66 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
   const bool p_alone = use_p && !use_k;
   float tm2 = NEG_INF;
   unsigned mine = 0;
-  uint32_t* slots = L.cand + t * kFSlots;
-  // (two instantiations: the threshold's bin when top-p runs alone, the
-  // floor otherwise; a uniform test inside the loop would cost on every entry)
-  auto candidates = [&](auto in_bin) {
-    constexpr bool kBin = decltype(in_bin)::value;
-    const float Rp = kBin ? ref_of(mx, a.k2) : 0.f;
-    // the bin's value range, widened: only entries inside it take the
-    // exact bin test
-    float lo = NEG_INF, hi = INFINITY;
-    if (kBin) {
-      const float e_lo = -(float)(kFBins - p_bin) * 0.125f, e_hi = e_lo + 0.125f;
-      if (p_bin > 0) lo = (Rp + e_lo) / a.k2;
-      if (p_bin < kFBins - 1) hi = (Rp + e_hi) / a.k2;
-      lo -= 1e-3f * (1.f + fabsf(lo));
-      hi += 1e-3f * (1.f + fabsf(hi));
-    }
-    // bins as the histogram made them; an extra entry of zero mass at the
-    // bottom is harmless (it weighs nothing in the selection)
-    auto keep = [&](float l) {
-      if (kBin && pmass_bin(fmaf(l, a.k2, -Rp)) != p_bin) return;
-      if (mine < (unsigned)kFSlots) slots[mine] = fkey(l);
-      ++mine;
-    };
+  if (p_alone) {
+    // the threshold's bin: a few hundred entries, so each wave compacts its
+    // finds into its own region of the candidate array (a ballot per entry;
+    // the branch is wave-uniform and rarely taken).  First a range test on
+    // the values (the bin's edges, widened), then the exact bin test.
+    const float Rp = ref_of(mx, a.k2);
+    const float e_lo = -(float)(kFBins - p_bin) * 0.125f, e_hi = e_lo + 0.125f;
+    float lo = p_bin > 0 ? (Rp + e_lo) / a.k2 : NEG_INF;
+    float hi = p_bin < kFBins - 1 ? (Rp + e_hi) / a.k2 : INFINITY;
+    lo -= 1e-3f * (1.f + fabsf(lo));
+    hi += 1e-3f * (1.f + fabsf(hi));
+    constexpr unsigned kRegion = kFCand / kFWaves;
+    uint32_t* region = L.cand + (t >> 6) * kRegion;
+    unsigned cw = 0;  // this wave's finds (uniform)
     auto one = [&](float l) {
-      if (!kBin) tm2 = fmaxf(tm2, l);
-      if (kBin ? (l >= lo) & (l <= hi) : l >= floor_v) keep(l);
-    };
-    // top-p alone, per vector: a mask of the entries in the bin's range,
-    // and one (rarely taken) branch for the vector
-    row_for_each_v<DT>(row, a.V, 1, one, [&](const float* fe) {
-      if (kBin) {
-        unsigned in = 0;
-#pragma unroll
-        for (int e = 0; e < E::kVec; ++e) in |= (unsigned)((fe[e] >= lo) & (fe[e] <= hi)) << e;
+      if (__ballot((l >= lo) & (l <= hi))) {
+        const bool in = (l >= lo) & (l <= hi) && pmass_bin(fmaf(l, a.k2, -Rp)) == p_bin;
+        const unsigned long long m = __ballot(in);
         if (in) {
-#pragma unroll
-          for (int e = 0; e < E::kVec; ++e)
-            if ((in >> e) & 1u) keep(fe[e]);
+          const unsigned at = cw + (unsigned)__builtin_amdgcn_mbcnt_hi(
+                                       (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+          if (at < kRegion) region[at] = fkey(l);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < E::kVec; ++e) one(fe[e]);
+        cw += (unsigned)__popcll(m);
       }
+    };
+    // the unaligned head and tail elements come in some lanes only: kept
+    // aside, then taken with every lane (the ballots need whole waves)
+    float hv = NEG_INF, tv = NEG_INF;
+    bool got_h = false;
+    auto aside = [&](float l) {
+      if (got_h) tv = l;
+      else hv = l, got_h = true;
+    };
+    row_for_each_v<DT>(row, a.V, 1, aside, [&](const float* fe) {
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) one(fe[e]);
     });
-  };
-  if (p_alone)
-    candidates(std::integral_constant<bool, true>{});
-  else
-    candidates(std::integral_constant<bool, false>{});
+    one(hv);
+    one(tv);
+    // in the per-thread slot layout the selection reads: thread t's slots
+    // are entries [32 t', 32 t' + 32) of its wave's region, t' = t mod 64
+    const int rel = (t & 63) * kFSlots;
+    const int have = (int)cw - rel;
+    mine = cw > kRegion ? (unsigned)kFSlots + 1u  // overflow: the whole row
+                        : (unsigned)(have < 0 ? 0 : have > kFSlots ? kFSlots : have);
+  } else {
+    uint32_t* slots = L.cand + t * kFSlots;
+    auto one = [&](float l) {
+      tm2 = fmaxf(tm2, l);
+      if (l >= floor_v) {
+        if (mine < (unsigned)kFSlots) slots[mine] = fkey(l);
+        ++mine;
+      }
+    };
+    row_for_each_v<DT>(row, a.V, 1, one, [&](const float* fe) {
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) one(fe[e]);
+    });
+  }
   L.ccount[t] = mine;
   if (!p_alone) mx = fblock_max(tm2, L);  // (top-p alone: known from its first pass)
   if (mx == NEG_INF) {  // a dead row: the walk reports it
