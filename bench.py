@@ -22,9 +22,10 @@ contexts of 16k..32k tokens, n = 4..1, gamma = 4; context copies rotated like
 the logits).  --mode round times a whole model-free speculative round: the
 drafter, then the point-mode verify of its drafts against the B=64,
 V=128256 target logits, both launches on one stream; with --adapt the
-draft-length controller runs between them (capped by the draft lengths, fed
-the previous round's accepted counts).  --mode adapt times the controller
-alone over the same 64 rows.
+draft-length rule runs in the drafting launch's last step
+(spec_ngram_draft_adaptive; --unfused: as its own launch between them),
+capped by the draft lengths and fed the previous round's accepted counts.
+--mode adapt times the controller alone over the same 64 rows.
 """
 from __future__ import annotations
 
@@ -66,6 +67,9 @@ def parse():
                     help="round: insert the adaptive draft-length controller")
     ap.add_argument("--draft-cost", type=float, default=0.05,
                     help="controller: cost of one draft token, in target passes")
+    ap.add_argument("--unfused", action="store_true",
+                    help="round --adapt: the controller as its own launch instead of inside "
+                         "the drafting launch")
     ap.add_argument("--contexts", default="ctx32k", help="drafting workload (ngram, round)")
     ap.add_argument("--top-k", type=int, default=0, help="top-k filter of p and q (0: off)")
     ap.add_argument("--top-p", type=float, default=1.0, help="top-p filter of p and q (1: off)")
@@ -174,6 +178,20 @@ def bench_drafting(args):
     def control(k):
         lib.spec_gamma_control(*cargs)
 
+    fargs = [(P(c.data_ptr()), P(ln.data_ptr()), B, cc.stride, cc.n_min, cc.n_max, G,
+              P(c_nacc.data_ptr()), P(c_gam.data_ptr()), None, P(ctl.state.data_ptr()),
+              *ctl.params[1:], P(d_tok.data_ptr()), P(d_len.data_ptr()), P(d_n.data_ptr()),
+              P(d_pos.data_ptr()), P(c_gam.data_ptr()), None, P(nws.ptr), nws.nbytes, hs)
+             for c in ctxs]
+
+    def draft_adapt(k):
+        lib.spec_ngram_draft_adaptive(*fargs[k % rot_c])
+
+    fused = args.mode == "round" and args.adapt and not args.unfused
+    if fused:
+        draft_adapt(0)  # argument checks, once
+        torch.cuda.synchronize()
+
     K = args.steps
     adapt = args.mode == "adapt" or (args.mode == "round" and args.adapt)
     calls, case, step_bytes, rot_v = [draft], None, draft_bytes, 0
@@ -208,7 +226,9 @@ def bench_drafting(args):
         def verify(k):
             verifies[k % rot_v]()
 
-        if adapt:
+        if fused:
+            calls = [draft_adapt]
+        elif adapt:
             calls.append(control)
         calls.append(verify)
         # compulsory verify bytes: g_b + 1 target rows per row, g_b the draft length
@@ -222,10 +242,13 @@ def bench_drafting(args):
 
     total_ms, wall = timed(step, K, args.warmup, stream, torch)
     draft_ms, _ = timed(draft, K, args.warmup, stream, torch)
-    control_us = None
+    control_us = fused_us = None
     if adapt:
         control_ms, _ = timed(control, K, args.warmup, stream, torch)
         control_us = control_ms / K * 1e3
+    if fused:
+        fused_ms, _ = timed(draft_adapt, K, args.warmup, stream, torch)
+        fused_us = fused_ms / K * 1e3
     ms_per_step = total_ms / K
     draft_us = draft_ms / K * 1e3
     if case is not None:
@@ -234,6 +257,8 @@ def bench_drafting(args):
     g_b = d_len.cpu().numpy()
     n_b = d_n.cpu().numpy()
     line_extra = {"control_kernel_us": control_us} if adapt else {}
+    if fused:
+        line_extra["draft_and_control_kernel_us"] = fused_us
     if adapt:
         line_extra["mean_controlled_gamma"] = float(c_gam.float().mean())
     if args.mode == "round":
@@ -297,7 +322,8 @@ def bench_drafting(args):
     wl = (f"prompt-lookup drafting B={B} contexts {cc.L_lo}..{cc.stride} tokens "
           f"n={cc.n_max}..{cc.n_min} gamma={G} ({args.contexts})")
     if adapt:
-        wl += f" + adaptive gamma (draft cost {args.draft_cost})"
+        wl += (f" + adaptive gamma (draft cost {args.draft_cost}"
+               + (", in the drafting launch)" if fused else ", own launch)"))
     if args.mode == "adapt":
         wl = (f"adaptive draft length B={B} gamma_max={G} draft cost {args.draft_cost}, "
               f"capped by the {args.contexts} draft lengths")

@@ -72,6 +72,26 @@ int spec_ngram_draft(const int32_t* context, const int32_t* ctx_len, int B, int 
                      int32_t* out_n, int32_t* out_pos, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Drafting and the draft-length rule of spec_adapt.h in one call: the
+ * drafter as spec_ngram_draft, then for every row the rule
+ * (spec_gamma_control with gamma_max = gamma and gamma_limit = the row's
+ * draft length), run by the last step of the drafting launch.  out_gamma
+ * (int32 [B]) is the verify's gamma_per_row for this round; out_len keeps
+ * the drafted length.  The rule's arguments (n_accepted, gamma_used,
+ * active, state, decay, prior_alpha, prior_weight, draft_cost, batch_off,
+ * out_alpha) mean what they mean for spec_gamma_control, with the same
+ * errors; gamma must also be <= SPEC_GAMMA_MAX_LIMIT.  Results are
+ * bit-identical to spec_ngram_draft followed by spec_gamma_control.
+ * Batches above 1,024 rows run the two as separate launches on `stream`. */
+int spec_ngram_draft_adaptive(const int32_t* context, const int32_t* ctx_len, int B, int stride,
+                              int n_min, int n_max, int gamma, const int32_t* n_accepted,
+                              const int32_t* gamma_used, const int32_t* active, double* state,
+                              double decay, double prior_alpha, double prior_weight,
+                              double draft_cost, int batch_off, int32_t* out_draft,
+                              int32_t* out_len, int32_t* out_n, int32_t* out_pos,
+                              int32_t* out_gamma, double* out_alpha, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,7 @@ EXPORTS = (
     "spec_verify_diagnostics", "spec_verify_strerror", "spec_verify_version",
     "spec_probe_read", "spec_probe_read_blocks", "spec_probe_copy",
     "spec_ngram_draft", "spec_ngram_workspace_bytes", "spec_gamma_control",
+    "spec_ngram_draft_adaptive",
 )
 NGRAM_MAX_N, NGRAM_MAX_GAMMA, NGRAM_MAX_STRIDE = 64, 256, 1 << 25
 
@@ -88,6 +89,9 @@ def load():
     d = ctypes.c_double
     lib.spec_gamma_control.argtypes = [P, P, P, P, P, i32, i32, d, d, d, d, i32, P, P, P]
     lib.spec_gamma_control.restype = i32
+    lib.spec_ngram_draft_adaptive.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, d, d, d, d,
+                                              i32, P, P, P, P, P, P, P, sz, P]
+    lib.spec_ngram_draft_adaptive.restype = i32
     _lib = lib
     return lib
 
@@ -369,6 +373,40 @@ class GammaControl:
                                          pa, pw, c, off, _ptr(out), _ptr(alpha),
                                          _stream_handle(stream)), "spec_gamma_control")
         return out
+
+
+def ngram_draft_adaptive(context, ctx_len, control: GammaControl, n_accepted=None,
+                         gamma_used=None, *, active=None, n_min: int = 1, n_max: int = 4,
+                         workspace: Workspace | None = None, out=None, alpha=None, stream=None):
+    """spec_ngram_draft_adaptive: prompt-lookup drafting with the draft-length
+    rule in the same launch.  The draft length cap is the controller's
+    gamma_max; `control` holds the rule's parameters and state.
+
+    Returns (draft [B, gamma], length [B], n [B], pos [B], gamma [B]), all
+    int32: `gamma` is this round's gamma_per_row for verify(mode=POINT), and
+    the next round passes that verify's n_accepted with this `gamma` back."""
+    torch = _torch()
+    B, stride = context.shape
+    if control.B != B:
+        raise ValueError("the controller's batch differs from the context's")
+    for name, t in (("context", context), ("ctx_len", ctx_len), ("n_accepted", n_accepted),
+                    ("gamma_used", gamma_used), ("active", active)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    G, decay, pa, pw, c, off = control.params
+    dev = context.device
+    if workspace is None:
+        workspace = Workspace(ngram_workspace_bytes(B), device=dev, stream=stream)
+    if out is None:
+        out = (torch.empty((B, G), dtype=torch.int32, device=dev),
+               *(torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)))
+    draft, length, n, pos, gam = out
+    _check(load().spec_ngram_draft_adaptive(
+        _ptr(context), _ptr(ctx_len), B, stride, int(n_min), int(n_max), G, _ptr(n_accepted),
+        _ptr(gamma_used), _ptr(active), _ptr(control.state), decay, pa, pw, c, off, _ptr(draft),
+        _ptr(length), _ptr(n), _ptr(pos), _ptr(gam), _ptr(alpha), ctypes.c_void_p(workspace.ptr),
+        workspace.nbytes, _stream_handle(stream)), "spec_ngram_draft_adaptive")
+    return draft, length, n, pos, gam
 
 
 def probe_read(src, out=None, stream=None):

@@ -3,15 +3,13 @@
 // sources are in include/spec_adapt.h.
 //
 // The work is a few fp64 operations per row and at most gamma_max steps of
-// the E(gamma) / (1 + gamma c) search, so one workgroup does the whole batch:
-// it counts the active rows (the switch-off needs the batch's total), then
-// every thread decides its rows.  The operations and their order are the
-// rule's, in fp64 and built with -ffp-contract=off, so the results are
-// bit-for-bit those of any IEEE double implementation of the same steps.
+// the E(gamma) / (1 + gamma c) search (gamma_rule.h), so one workgroup does
+// the whole batch: it counts the active rows (the switch-off needs the
+// batch's total), then every thread decides its rows.
 #include <hip/hip_runtime.h>
-#include <math.h>
 #include <stdint.h>
 
+#include "gamma_rule.h"
 #include "spec_adapt.h"
 
 namespace {
@@ -24,9 +22,8 @@ struct GArgs {
   const int32_t* active;
   const int32_t* limit;
   double* state;
-  int B, gamma_max;
-  double decay, prior_alpha, prior_weight, cost;
-  int batch_off;
+  int B;
+  spec_rule::GammaParams p;
   int32_t* out_gamma;
   double* out_alpha;
 };
@@ -48,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void gamma_kernel(GArgs a) {
   int n_active = 0;
 #pragma unroll
   for (int i = 0; i < kThreads / 64; ++i) n_active += part[i];
-  const bool off = a.batch_off >= 1 && n_active >= a.batch_off;
+  const bool off = a.p.batch_off >= 1 && n_active >= a.p.batch_off;
 
   for (int b = tid; b < a.B; b += kThreads) {
     if (a.active && a.active[b] == 0) {
@@ -56,37 +53,14 @@ __global__ __launch_bounds__(kThreads) void gamma_kernel(GArgs a) {
       if (a.out_alpha) a.out_alpha[b] = 0.0;
       continue;
     }
-    double A = a.state[2 * b], T = a.state[2 * b + 1];
-    const int g = a.g_used ? a.g_used[b] : 0;
-    const int n = a.n_acc ? a.n_acc[b] : -1;
-    if (g >= 1 && n >= 0 && n <= g) {
-      const int tested = n + 1 < g ? n + 1 : g;
-      A = a.decay * A + (double)n;
-      T = a.decay * T + (double)tested;
-    } else {
-      A = a.decay * A;
-      T = a.decay * T;
-    }
-    a.state[2 * b] = A;
-    a.state[2 * b + 1] = T;
-    const double den = T + a.prior_weight;
-    const double alpha = den > 0.0 ? (A + a.prior_weight * a.prior_alpha) / den : a.prior_alpha;
+    double st[2] = {a.state[2 * b], a.state[2 * b + 1]};
+    double alpha;
+    const int g = spec_rule::gamma_rule(a.p, a.n_acc ? a.n_acc[b] : -1, a.g_used ? a.g_used[b] : 0,
+                                        st, a.limit ? a.limit[b] : a.p.gamma_max, off, &alpha);
+    a.state[2 * b] = st[0];
+    a.state[2 * b + 1] = st[1];
     if (a.out_alpha) a.out_alpha[b] = alpha;
-    int best = 0;
-    if (!off) {
-      int cap = a.gamma_max;
-      if (a.limit && a.limit[b] < cap) cap = a.limit[b] < 0 ? 0 : a.limit[b];
-      double best_e = 1.0, pw = 1.0, e = 1.0;
-      for (int k = 1; k <= cap; ++k) {
-        pw = pw * alpha;
-        e = e + pw;
-        if (e * (1.0 + (double)best * a.cost) > best_e * (1.0 + (double)k * a.cost)) {
-          best = k;
-          best_e = e;
-        }
-      }
-    }
-    a.out_gamma[b] = best;
+    a.out_gamma[b] = g;
   }
 }
 
@@ -100,10 +74,7 @@ extern "C" int spec_gamma_control(const int32_t* n_accepted, const int32_t* gamm
                                   double prior_weight, double draft_cost, int batch_off,
                                   int32_t* out_gamma, double* out_alpha, void* stream) {
   if (B < 0 || gamma_max < 0 || gamma_max > SPEC_GAMMA_MAX_LIMIT) return SPEC_ERR_SHAPE;
-  if (!(decay >= 0.0 && decay <= 1.0) || !(prior_alpha >= 0.0 && prior_alpha <= 1.0))
-    return SPEC_ERR_ARG;
-  if (!(prior_weight >= 0.0) || !isfinite(prior_weight) || !(draft_cost >= 0.0) ||
-      !isfinite(draft_cost) || batch_off < 0)
+  if (!spec_rule::gamma_params_ok(decay, prior_alpha, prior_weight, draft_cost, batch_off))
     return SPEC_ERR_ARG;
   if (B == 0) return SPEC_OK;
   if (!state || !out_gamma || (n_accepted == nullptr) != (gamma_used == nullptr))
@@ -112,8 +83,9 @@ extern "C" int spec_gamma_control(const int32_t* n_accepted, const int32_t* gamm
                         (const void*)gamma_limit, (const void*)out_gamma})
     if (p && !aligned(p, 4)) return SPEC_ERR_ALIGN;
   if (!aligned(state, 8) || (out_alpha && !aligned(out_alpha, 8))) return SPEC_ERR_ALIGN;
-  GArgs a{n_accepted, gamma_used, active, gamma_limit, state, B, gamma_max, decay, prior_alpha,
-          prior_weight, draft_cost, batch_off, out_gamma, out_alpha};
+  GArgs a{n_accepted, gamma_used, active, gamma_limit, state, B,
+          spec_rule::GammaParams{gamma_max, decay, prior_alpha, prior_weight, draft_cost, batch_off},
+          out_gamma, out_alpha};
   hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP - (int)e;

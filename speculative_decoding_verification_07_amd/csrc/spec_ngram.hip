@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gamma_rule.h"
+#include "spec_adapt.h"
 #include "spec_ngram.h"
 
 namespace {
@@ -63,7 +65,20 @@ struct NArgs {
   int32_t* dn;
   int32_t* dpos;
   unsigned* ws;  // per row: {key, ticket}
+  // the draft-length rule run in the same last step (adapt != 0)
+  int adapt;
+  const int32_t* n_acc;
+  const int32_t* g_used;
+  const int32_t* active;
+  double* state;
+  spec_rule::GammaParams gp;
+  int32_t* out_gamma;
+  double* out_alpha;
 };
+
+// Batches up to this many rows run the draft-length rule inside the
+// drafter: each row's last workgroup counts the batch's active rows itself.
+constexpr int kFuseMaxB = 1024;
 
 __device__ __forceinline__ unsigned wave_max(unsigned v) {
 #pragma unroll
@@ -71,8 +86,27 @@ __device__ __forceinline__ unsigned wave_max(unsigned v) {
   return v;
 }
 
-// Writes row b's outputs from the row's best key `w` (all threads).
-__device__ void write_row(const NArgs& a, int b, int L, bool valid, unsigned w) {
+// The rule's per-row inputs, loaded by thread 0 of every workgroup when it
+// starts, so that the row's last workgroup has them when it needs them.
+struct RuleIn {
+  int n, g, act;
+  double A, T;
+};
+
+__device__ __forceinline__ RuleIn rule_inputs(const NArgs& a, int b) {
+  RuleIn r{-1, 0, 1, 0.0, 0.0};
+  if (!a.adapt || threadIdx.x != 0) return r;
+  if (a.n_acc) r.n = a.n_acc[b], r.g = a.g_used[b];
+  if (a.active) r.act = a.active[b];
+  r.A = a.state[2 * b], r.T = a.state[2 * b + 1];
+  return r;
+}
+
+// Writes row b's outputs from the row's best key `w` (all threads), then,
+// when adapting, the row's draft length for the verify: the rule of
+// spec_adapt.h capped by the draft's length.
+__device__ void write_row(const NArgs& a, int b, int L, bool valid, unsigned w, int* part,
+                          const RuleIn& ri) {
   const int32_t* c = a.ctx + (size_t)b * a.stride;
   const int m = (int)(w >> kPosBits);
   const int pos = (int)(w & kPosMask);
@@ -85,6 +119,34 @@ __device__ void write_row(const NArgs& a, int b, int L, bool valid, unsigned w) 
     if (a.dn) a.dn[b] = !valid ? -2 : hit ? m : -1;
     if (a.dpos) a.dpos[b] = hit ? pos : -1;
   }
+  if (!a.adapt) return;
+  int n_active = a.B;  // no mask: every row is active
+  if (a.active && a.gp.batch_off >= 1) {
+    int cnt = 0;
+    for (int i = threadIdx.x; i < a.B; i += kThreads) cnt += a.active[i] != 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = cnt;
+    __syncthreads();
+    n_active = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) n_active += part[i];
+  }
+  if (threadIdx.x == 0) {
+    if (ri.act == 0) {
+      a.out_gamma[b] = 0;
+      if (a.out_alpha) a.out_alpha[b] = 0.0;
+    } else {
+      const bool off = a.gp.batch_off >= 1 && n_active >= a.gp.batch_off;
+      double st[2] = {ri.A, ri.T};
+      double alpha;
+      const int g = spec_rule::gamma_rule(a.gp, ri.n, ri.g, st, len, off, &alpha);
+      a.state[2 * b] = st[0];
+      a.state[2 * b + 1] = st[1];
+      if (a.out_alpha) a.out_alpha[b] = alpha;
+      a.out_gamma[b] = g;
+    }
+  }
 }
 
 // AL: 16-byte vector loads (aligned rows).  REG: n_max <= kRegN, so every
@@ -95,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void ngram_kernel(NArgs a) {
   __shared__ int sfx[SPEC_NGRAM_MAX_N];  // sfx[i] = c[L-1-i]
   __shared__ __align__(16) int tok[kHalo + kChunk];  // c[cbase - kHalo .. cbase + kChunk)
   __shared__ unsigned red[kThreads / 64];
+  __shared__ int part[kThreads / 64];
   __shared__ unsigned win;
   __shared__ int last_wg;
 
@@ -106,6 +169,7 @@ __global__ __launch_bounds__(kThreads) void ngram_kernel(NArgs a) {
   const int base = cbase + tid * kTok;
   const int L = a.len[b];
   const bool valid = L >= 0 && L <= a.stride;
+  const RuleIn ri = rule_inputs(a, b);
   const int last = L - 2;  // largest t with a token after it
   const bool active = valid && cbase <= last;
   // The suffix and the chunk load side by side, both after the length.
@@ -216,22 +280,15 @@ __global__ __launch_bounds__(kThreads) void ngram_kernel(NArgs a) {
     last_wg = fin;
   }
   __syncthreads();
-  if (last_wg) write_row(a, b, L, valid, win);
+  if (last_wg) write_row(a, b, L, valid, win, part, ri);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-}  // namespace
-
-extern "C" size_t spec_ngram_workspace_bytes(int B) {
-  if (B < 1) return 0;
-  return ((size_t)B * kRowWords * sizeof(unsigned) + 255) / 256 * 256;
-}
-
-extern "C" int spec_ngram_draft(const int32_t* context, const int32_t* ctx_len, int B, int stride,
-                                int n_min, int n_max, int gamma, int32_t* out_draft,
-                                int32_t* out_len, int32_t* out_n, int32_t* out_pos,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// Checks the drafting arguments and fills `a` (the rule's fields zero).
+int ngram_args(const int32_t* context, const int32_t* ctx_len, int B, int stride, int n_min,
+               int n_max, int gamma, int32_t* out_draft, int32_t* out_len, int32_t* out_n,
+               int32_t* out_pos, void* workspace, size_t workspace_bytes, NArgs& a) {
   if (B < 0 || stride < 0 || stride > SPEC_NGRAM_MAX_STRIDE) return SPEC_ERR_SHAPE;
   if (n_min < 1 || n_max < n_min || n_max > SPEC_NGRAM_MAX_N) return SPEC_ERR_ARG;
   if (gamma < 0 || gamma > SPEC_NGRAM_MAX_GAMMA) return SPEC_ERR_ARG;
@@ -247,12 +304,18 @@ extern "C" int spec_ngram_draft(const int32_t* context, const int32_t* ctx_len, 
     if (!workspace || workspace_bytes < spec_ngram_workspace_bytes(B)) return SPEC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SPEC_ERR_ALIGN;
   }
-  NArgs a{context, ctx_len, B, stride, n_min, n_max, gamma, nch,
-          out_draft, out_len, out_n, out_pos, static_cast<unsigned*>(workspace)};
-  const bool al = aligned(context, 16) && stride % 4 == 0;
-  const dim3 grid((unsigned)(B * nch));
+  a = NArgs{};
+  a.ctx = context, a.len = ctx_len, a.B = B, a.stride = stride, a.n_min = n_min;
+  a.n_max = n_max, a.gamma = gamma, a.nch = nch, a.draft = out_draft, a.dlen = out_len;
+  a.dn = out_n, a.dpos = out_pos, a.ws = static_cast<unsigned*>(workspace);
+  return SPEC_OK;
+}
+
+int ngram_launch(const NArgs& a, void* stream) {
+  const bool al = aligned(a.ctx, 16) && a.stride % 4 == 0;
+  const dim3 grid((unsigned)(a.B * a.nch));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool reg = n_max <= kRegN;
+  const bool reg = a.n_max <= kRegN;
   if (al && reg)
     hipLaunchKernelGGL((ngram_kernel<true, true>), grid, dim3(kThreads), 0, s, a);
   else if (al)
@@ -263,4 +326,57 @@ extern "C" int spec_ngram_draft(const int32_t* context, const int32_t* ctx_len, 
     hipLaunchKernelGGL((ngram_kernel<false, false>), grid, dim3(kThreads), 0, s, a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP - (int)e;
+}
+
+}  // namespace
+
+extern "C" size_t spec_ngram_workspace_bytes(int B) {
+  if (B < 1) return 0;
+  return ((size_t)B * kRowWords * sizeof(unsigned) + 255) / 256 * 256;
+}
+
+extern "C" int spec_ngram_draft(const int32_t* context, const int32_t* ctx_len, int B, int stride,
+                                int n_min, int n_max, int gamma, int32_t* out_draft,
+                                int32_t* out_len, int32_t* out_n, int32_t* out_pos,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  NArgs a;
+  const int rc = ngram_args(context, ctx_len, B, stride, n_min, n_max, gamma, out_draft, out_len,
+                            out_n, out_pos, workspace, workspace_bytes, a);
+  if (rc != SPEC_OK || B == 0) return rc;
+  return ngram_launch(a, stream);
+}
+
+extern "C" int spec_ngram_draft_adaptive(
+    const int32_t* context, const int32_t* ctx_len, int B, int stride, int n_min, int n_max,
+    int gamma, const int32_t* n_accepted, const int32_t* gamma_used, const int32_t* active,
+    double* state, double decay, double prior_alpha, double prior_weight, double draft_cost,
+    int batch_off, int32_t* out_draft, int32_t* out_len, int32_t* out_n, int32_t* out_pos,
+    int32_t* out_gamma, double* out_alpha, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (gamma > SPEC_GAMMA_MAX_LIMIT) return SPEC_ERR_ARG;
+  if (!spec_rule::gamma_params_ok(decay, prior_alpha, prior_weight, draft_cost, batch_off))
+    return SPEC_ERR_ARG;
+  NArgs a;
+  const int rc = ngram_args(context, ctx_len, B, stride, n_min, n_max, gamma, out_draft, out_len,
+                            out_n, out_pos, workspace, workspace_bytes, a);
+  if (rc != SPEC_OK || B == 0) return rc;
+  if (!state || !out_gamma || (n_accepted == nullptr) != (gamma_used == nullptr))
+    return SPEC_ERR_NULL;
+  for (const void* p : {(const void*)n_accepted, (const void*)gamma_used, (const void*)active,
+                        (const void*)out_gamma})
+    if (p && !aligned(p, 4)) return SPEC_ERR_ALIGN;
+  if (!aligned(state, 8) || (out_alpha && !aligned(out_alpha, 8))) return SPEC_ERR_ALIGN;
+  if (B > kFuseMaxB) {
+    // large batches: the drafter, then the controller over its lengths
+    const int r1 = ngram_launch(a, stream);
+    if (r1 != SPEC_OK) return r1;
+    return spec_gamma_control(n_accepted, gamma_used, active, out_len, state, B, gamma, decay,
+                              prior_alpha, prior_weight, draft_cost, batch_off, out_gamma,
+                              out_alpha, stream);
+  }
+  a.adapt = 1;
+  a.n_acc = n_accepted, a.g_used = gamma_used, a.active = active, a.state = state;
+  a.gp = spec_rule::GammaParams{gamma, decay, prior_alpha, prior_weight, draft_cost, batch_off};
+  a.out_gamma = out_gamma, a.out_alpha = out_alpha;
+  return ngram_launch(a, stream);
 }

@@ -248,3 +248,33 @@ def test_gamma_control_argument_errors(lib, kw, code):
 
 def test_gamma_control_empty_batch(lib):
     assert _gcall(lib, B=0, n=None, g=None, st=None, out=None) == sv.OK
+
+
+def _acall(lib, **kw):
+    a = dict(ctx=A, ln=A, B=4, stride=4096, n_min=1, n_max=4, gamma=4, n=A, g=A, act=None, st=A2,
+             d=0.9, pa=0.6, pw=2.0, c=0.05, off=0, draft=A, dlen=A, dn=None, dpos=None, og=A,
+             oa=None, ws=A2, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.spec_ngram_draft_adaptive(
+        a["ctx"], a["ln"], a["B"], a["stride"], a["n_min"], a["n_max"], a["gamma"], a["n"], a["g"],
+        a["act"], a["st"], a["d"], a["pa"], a["pw"], a["c"], a["off"], a["draft"], a["dlen"],
+        a["dn"], a["dpos"], a["og"], a["oa"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), sv.ERR_SHAPE), (dict(gamma=64), sv.ERR_ARG), (dict(n_min=0), sv.ERR_ARG),
+    (dict(d=2.0), sv.ERR_ARG), (dict(pa=-0.5), sv.ERR_ARG), (dict(c=float("inf")), sv.ERR_ARG),
+    (dict(off=-1), sv.ERR_ARG),
+    (dict(ctx=None), sv.ERR_NULL), (dict(st=None), sv.ERR_NULL), (dict(og=None), sv.ERR_NULL),
+    (dict(n=None), sv.ERR_NULL), (dict(g=None), sv.ERR_NULL),
+    (dict(n=A + 1), sv.ERR_ALIGN), (dict(act=A + 2), sv.ERR_ALIGN), (dict(st=A2 + 4), sv.ERR_ALIGN),
+    (dict(oa=A + 4), sv.ERR_ALIGN), (dict(og=A + 2), sv.ERR_ALIGN),
+    (dict(ws=None), sv.ERR_WORKSPACE),
+])
+def test_ngram_adaptive_argument_errors(lib, kw, code):
+    assert _acall(lib, **kw) == code
+
+
+def test_ngram_adaptive_empty_batch(lib):
+    assert _acall(lib, B=0, ctx=None, ln=None, n=None, g=None, st=None, draft=None, dlen=None,
+                  og=None, ws=None) == sv.OK

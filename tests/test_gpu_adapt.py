@@ -131,3 +131,38 @@ def test_adaptive_model_free_round():
     got = verify_run(case, torch, probe=False)
     rep = parity.compare(case, *got[:3])
     assert rep.ok, rep.summary()
+
+
+@pytest.mark.parametrize("B,stride,batch_off", [(64, 5000, 0), (16, 300, 0), (40, 2500, 30),
+                                                (1100, 700, 0)])
+def test_fused_matches_separate(B, stride, batch_off):
+    """spec_ngram_draft_adaptive against spec_ngram_draft followed by
+    spec_gamma_control, over rounds fed back with simulated acceptances:
+    every output and the state bit for bit (B = 1100: the two-launch path)."""
+    rng = np.random.default_rng(B + stride)
+    ctx, lens = inputs.make_contexts("ctx5k", rnd=B, B=B, stride=stride, V=200)
+    c, ln = _i32(ctx), _i32(lens)
+    active = (rng.random(B) < 0.85).astype(np.int32)
+    act = _i32(active)
+    params = dict(gamma_max=4, decay=0.9, prior_alpha=0.6, prior_weight=2.0, draft_cost=0.05,
+                  batch_off=batch_off)
+    sep, fused = sv.GammaControl(B, **params), sv.GammaControl(B, **params)
+    n = g = None
+    for r in range(12):
+        print(f"fused B={B} stride={stride} batch_off={batch_off} round {r}", flush=True)
+        d1, l1, n1, p1 = sv.ngram_draft(c, ln, n_min=1, n_max=4, gamma=4)
+        a1 = torch.empty(B, dtype=torch.float64, device="cuda")
+        g1 = sep(n, g, active=act, gamma_limit=l1, alpha=a1)
+        a2 = torch.empty(B, dtype=torch.float64, device="cuda")
+        d2, l2, n2, p2, g2 = sv.ngram_draft_adaptive(c, ln, fused, n, g, active=act, alpha=a2)
+        torch.cuda.synchronize()
+        for x, y in ((d1, d2), (l1, l2), (n1, n2), (p1, p2), (g1, g2), (a1, a2),
+                     (sep.state, fused.state)):
+            np.testing.assert_array_equal(x.cpu().numpy(), y.cpu().numpy(), err_msg=f"round {r}")
+        gam = g2.cpu().numpy()
+        if batch_off and int(active.sum()) >= batch_off:
+            assert (gam == 0).all()
+        acc = rng.random(B) < 0.7
+        cnt = np.where(acc, rng.integers(0, 5, size=B), 0)
+        n = _i32(np.minimum(cnt, gam))
+        g = g2.clone()
