@@ -1337,7 +1337,10 @@ __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g,
   // (the picks pass through opaque(): otherwise the optimiser merges "take
   // from the ring" and "load from memory" into one load through a pointer,
   // which sends the whole ring to scratch memory)
-  if (RING && kt >= nrows - NB) {
+  // with point-mass drafts the stream ends with t_0 and its reloads past
+  // the end read t_0 again, so a rejection at 0 finds its row in the ring
+  const bool from_ring = RING ? kt >= nrows - NB : KNOCK && kt == nrows - 1;
+  if (from_ring) {
     ring_pick(ring, kt % Ring<DT, R>::NB, st, gt);
     opaque(st);
   } else {
