@@ -1,0 +1,82 @@
+"""Calls on distinct workspaces may run concurrently (include/spec_verify.h,
+include/spec_ngram.h): two streams (default priority), each with its own
+workspace, launched back to back without synchronising, must give the
+results of the same calls run one after the other, with no diagnostic."""
+import numpy as np
+import pytest
+
+import speculative_decoding_verification_07_amd as sv
+from speculative_decoding_verification_07_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import MODES, case_to_dev  # noqa: E402
+
+
+def _prepared(case, dev, stream):
+    ws = sv.Workspace(sv.workspace_bytes(case.B, case.G, case.V,
+                                         sv.BF16 if case.target.dtype == np.uint16 else sv.F32,
+                                         MODES[case.mode]), stream=stream)
+    out = (torch.empty((case.B, case.G + 1), dtype=torch.int32, device="cuda"),
+           torch.empty(case.B, dtype=torch.int32, device="cuda"),
+           torch.empty(case.B, dtype=torch.int32, device="cuda"))
+    draft = None if case.mode == "point" else dev["draft"]
+    call = sv.Prepared(dev["target"], draft, dev["tokens"], dev["uniforms"], dev["gamma"],
+                       dev["kv"], temperature=case.T, mode=MODES[case.mode], workspace=ws, out=out,
+                       stream=stream)
+    return call, ws, out
+
+
+@pytest.mark.parametrize("sizes", ["small", "full"])
+def test_verify_on_two_streams(sizes):
+    kw = dict(B=16, V=20000) if sizes == "small" else {}
+    cases = [inputs.make_case(3, rnd=41, **kw), inputs.make_case(3, rnd=42, mode="point", **kw)]
+    devs = [case_to_dev(c, torch) for c in cases]
+    torch.cuda.synchronize()
+    # one after the other on the default stream
+    ref = []
+    for c, d in zip(cases, devs):
+        call, ws, out = _prepared(c, d, None)
+        call()
+        torch.cuda.synchronize()
+        ref.append([o.cpu().numpy() for o in out])
+        assert ws.diagnostics() == 0
+    # side by side on two streams
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    preps = [_prepared(c, d, s) for c, d, s in zip(cases, devs, streams)]
+    torch.cuda.synchronize()
+    print(f"two streams, {sizes} sizes", flush=True)
+    for it in range(20):
+        for call, _, _ in preps:
+            call()
+    torch.cuda.synchronize()
+    for (call, ws, out), want in zip(preps, ref):
+        for o, w in zip(out, want):
+            np.testing.assert_array_equal(o.cpu().numpy(), w)
+        assert ws.diagnostics() == 0
+
+
+def test_drafting_on_two_streams():
+    ctxs = [inputs.make_contexts("ctx5k", rnd=r) for r in (43, 44)]
+    devs = [(torch.from_numpy(c).cuda(), torch.from_numpy(l).cuda()) for c, l in ctxs]
+    ref = [[t.cpu().numpy() for t in sv.ngram_draft(c, l, n_min=1, n_max=4, gamma=4)]
+           for c, l in devs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [sv.Workspace(sv.ngram_workspace_bytes(c.shape[0]), stream=s)
+           for (c, _), s in zip(devs, streams)]
+    # outputs allocated once per stream: nothing is freed while a launch runs
+    outs = [(torch.empty((c.shape[0], 4), dtype=torch.int32, device="cuda"),
+             *(torch.empty(c.shape[0], dtype=torch.int32, device="cuda") for _ in range(3)))
+            for c, _ in devs]
+    torch.cuda.synchronize()
+    for it in range(20):
+        for (c, l), w, s, o in zip(devs, wss, streams, outs):
+            sv.ngram_draft(c, l, n_min=1, n_max=4, gamma=4, workspace=w, stream=s, out=o)
+    torch.cuda.synchronize()
+    for out, want in zip(outs, ref):
+        for o, w in zip(out, want):
+            np.testing.assert_array_equal(o.cpu().numpy(), w)
+    for w in wss:
+        assert int(w.tensor[w.offset:w.offset + w.nbytes].count_nonzero()) == 0
