@@ -30,24 +30,17 @@
 
 namespace {
 
-#ifndef SPEC_NGRAM_THREADS
-#define SPEC_NGRAM_THREADS 256
-#endif
-constexpr int kThreads = SPEC_NGRAM_THREADS;
-#ifndef SPEC_NGRAM_TOK
-#define SPEC_NGRAM_TOK 8
-#endif
-constexpr int kTok = SPEC_NGRAM_TOK;     // consecutive tokens per thread
+// 256 threads of 8 tokens: 4 tokens or 128 / 512 threads measure the same,
+// 16 or more tokens per thread leave too few waves to hide latency
+constexpr int kThreads = 256;
+constexpr int kTok = 8;                  // consecutive tokens per thread
 constexpr int kChunk = kThreads * kTok;  // tokens per workgroup
 constexpr int kHalo = SPEC_NGRAM_MAX_N;  // tokens before the chunk kept in LDS
 constexpr int kRegN = 8;                 // n_max up to this: matches in registers
-#ifndef SPEC_NGRAM_ROW_WORDS
-#define SPEC_NGRAM_ROW_WORDS 64
-#endif
 // Workspace words per row: {key, ticket}, padded so that rows' words lie
 // 256 bytes apart; packed together, every row's atomics would queue at the
 // same memory channel.
-constexpr int kRowWords = SPEC_NGRAM_ROW_WORDS;
+constexpr int kRowWords = 64;
 // key = m << kPosBits | (t + 1): m <= 64 needs 7 bits above the position
 constexpr int kPosBits = 25;
 constexpr unsigned kPosMask = (1u << kPosBits) - 1;
