@@ -134,3 +134,21 @@ def test_draft_feeds_point_verify():
     got = verify_run(case, torch, probe=False)
     rep = parity.compare(case, *got[:3])
     assert rep.ok, rep.summary()
+
+
+def test_random_shapes():
+    """Forty seeded random configurations: batch, stride (0 included),
+    alphabet, n range (both the register path and the LDS walk), gamma and
+    base-pointer alignment, each against the oracle."""
+    rng = np.random.default_rng(2024)
+    for k in range(40):
+        B = int(rng.integers(1, 70))
+        stride = int(rng.choice([0, 1, 7, 2047, 2048, 2049, int(rng.integers(2, 9000))]))
+        alphabet = int(rng.choice([1, 2, 3, 10, 1000]))
+        n_min = int(rng.integers(1, 6))
+        n_max = int(rng.integers(n_min, min(n_min + 12, sv.NGRAM_MAX_N) + 1))
+        gamma = int(rng.integers(0, sv.NGRAM_MAX_GAMMA + 1))
+        offset = int(rng.integers(0, 4))
+        ctx = rng.integers(0, alphabet, size=(B, stride), dtype=np.int32)
+        lens = rng.integers(-1, stride + 2, size=B).astype(np.int32)
+        check(ctx, lens, n_min, n_max, gamma, offset=offset)
