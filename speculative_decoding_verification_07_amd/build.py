@@ -19,6 +19,9 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a declared but undefined function is an error, never a library that
+    # resolves it at load time (or a kernel that calls through an empty slot)
+    "-Werror=undefined-internal", "-Wl,--no-undefined",
 ]
 
 

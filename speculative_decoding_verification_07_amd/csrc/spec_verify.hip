@@ -1582,7 +1582,7 @@ struct FLevels {
   __device__ static int bits(int) { return 8; }
 };
 
-__device__ float fblock_max(float v, FLds& L) {
+__device__ __forceinline__ float fblock_max(float v, FLds& L) {
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) L.fmax[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -1731,24 +1731,86 @@ __device__ __forceinline__ unsigned long long fixed_mass(float l, float k2, floa
   return fixed_mass_e(fmaf(l, k2, -R));
 }
 
+// Radix selection over the candidate list in LDS (listed) or over the whole
+// row: the key of the entry where the count (mass: the fixed-point masses
+// against R) from the top reaches `need`, counting keys >= floor_key2 only.
+// mass && !given: need is top_p of the mass of those keys (W when non-zero,
+// else the first level's histogram total).  packed: the list fills its
+// threads' slots in order (top-p alone), so the slots are walked across the
+// lanes; else each thread walks its own few filled slots (top-k).
 template <int DT>
-__global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
-  using E = Elt<DT>;
+__device__ __forceinline__ uint32_t radix_select(const FArgs& a, FLds& L, const char* row,
+                                                 bool listed, bool packed, float R, bool mass,
+                                                 uint64_t need, uint32_t floor_key2, uint64_t W,
+                                                 bool given) {
   using Lv = FLevels<DT>;
-  __shared__ FLds L;
-  const int t = threadIdx.x, lane = t & 63;
-  const int b = (int)(blockIdx.x / (unsigned)a.NR2), slot = (int)(blockIdx.x % (unsigned)a.NR2);
+  const int t = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  for (int lv = 0; lv < Lv::N; ++lv) {
+    const int sh = Lv::shift(lv), nb = 1 << Lv::bits(lv);
+    for (int i = t; i < nb; i += kFThreads) L.h[i] = 0;
+    __syncthreads();
+    auto add = [&](uint32_t k) {
+      if (k >= floor_key2 && (k & pmask) == prefix) {
+        const unsigned long long w = mass ? fixed_mass(funkey(k), a.k2, R) : 1ull;
+        if (w) atomicAdd(&L.h[(k >> sh) & (nb - 1)], w);
+      }
+    };
+    if (listed && packed) {
+      for (int i = t; i < kFCand; i += kFThreads)
+        if ((unsigned)(i % kFSlots) < L.ccount[i / kFSlots]) add(L.cand[i]);
+    } else if (listed) {  // this thread's filled slots
+      const int n = (int)L.ccount[t];
+      for (int j = 0; j < n; ++j) add(L.cand[t * kFSlots + j]);
+    } else {
+      row_for_each<DT>(row, a.V, [&](float l) { add(fkey(l)); });
+    }
+    __syncthreads();
+    uint64_t above, total;
+    if (mass && lv == 0 && !given) {
+      // the target: top_p of the mass kept so far, rounded up to a unit
+      if (W == 0) {
+        uint64_t sum = 0, incl, excl;
+        for (int i = t; i < nb; i += kFThreads) sum += L.h[i];
+        fblock_scan(sum, L, incl, excl, W);
+      }
+      need = (uint64_t)ceil((double)a.top_p * (double)W);
+      if (need < 1) need = 1;
+    }
+    const int d = find_cross(L, nb, need, above, total);
+    need -= above;
+    prefix |= (uint32_t)d << sh;
+    pmask |= (uint32_t)(nb - 1) << sh;
+  }
+  return prefix;
+}
+
+// The row whose threshold goes to `out`, or null when the walk cannot use
+// this vocabulary row (its threshold is -inf).
+template <int DT>
+__device__ __forceinline__ const char* filter_row_of(const FArgs& a, int b, int slot) {
+  using E = Elt<DT>;
   const int g = a.gam[b];
-  float* out = a.thr + (int64_t)b * (2 * a.G + 1) + slot;
   const bool is_t = slot <= a.G;
   const bool used =
       g >= 0 && g <= a.G && (is_t ? slot <= g : (a.drafts && slot - a.G - 1 < g));
-  if (!used) {
+  if (!used) return nullptr;
+  return is_t ? (const char*)a.tgt + ((int64_t)b * (a.G + 1) + slot) * a.V * E::kBytes
+              : (const char*)a.dft + ((int64_t)b * a.G + (slot - a.G - 1)) * a.V * E::kBytes;
+}
+
+// One workgroup finds the threshold of vocabulary row (b, slot) alone,
+// reading the row from memory (one to three passes).
+template <int DT>
+__device__ __forceinline__ void filter_row(const FArgs& a, int b, int slot, FLds& L) {
+  using E = Elt<DT>;
+  const int t = threadIdx.x, lane = t & 63;
+  float* out = a.thr + (int64_t)b * (2 * a.G + 1) + slot;
+  const char* row = filter_row_of<DT>(a, b, slot);
+  if (!row) {
     if (t == 0) *out = NEG_INF;
     return;
   }
-  const char* row = is_t ? (const char*)a.tgt + ((int64_t)b * (a.G + 1) + slot) * a.V * E::kBytes
-                         : (const char*)a.dft + ((int64_t)b * a.G + (slot - a.G - 1)) * a.V * E::kBytes;
   const bool use_k = a.top_k > 0 && a.top_k < a.V;
   const bool use_p = a.top_p < 1.f;
 
@@ -1893,46 +1955,9 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
   __syncthreads();
   const bool listed = __syncthreads_and(mine <= (unsigned)kFSlots) != 0;  // else: whole-row passes
 
-  // radix selection over the candidates (or the row): `mass` weighs each
-  // entry by its fixed-point mass, else 1; only keys >= floor_key2 count.
-  // W: the mass the top-p target is a fraction of (0: the histogram's total)
   auto select = [&](bool mass, uint64_t need, uint32_t floor_key2, uint64_t W,
                     bool given) -> uint32_t {
-    uint32_t prefix = 0, pmask = 0;
-    for (int lv = 0; lv < Lv::N; ++lv) {
-      const int sh = Lv::shift(lv), nb = 1 << Lv::bits(lv);
-      for (int i = t; i < nb; i += kFThreads) L.h[i] = 0;
-      __syncthreads();
-      auto add = [&](uint32_t k) {
-        if (k >= floor_key2 && (k & pmask) == prefix) {
-          const unsigned long long w = mass ? fixed_mass(funkey(k), a.k2, R) : 1ull;
-          if (w) atomicAdd(&L.h[(k >> sh) & (nb - 1)], w);
-        }
-      };
-      if (listed) {
-        for (int i = t; i < kFCand; i += kFThreads)
-          if ((unsigned)(i % kFSlots) < L.ccount[i / kFSlots]) add(L.cand[i]);
-      } else {
-        row_for_each<DT>(row, a.V, [&](float l) { add(fkey(l)); });
-      }
-      __syncthreads();
-      uint64_t above, total;
-      if (mass && lv == 0 && !given) {
-        // the target: top_p of the mass kept so far, rounded up to a unit
-        if (W == 0) {
-          uint64_t sum = 0, incl, excl;
-          for (int i = t; i < nb; i += kFThreads) sum += L.h[i];
-          fblock_scan(sum, L, incl, excl, W);
-        }
-        need = (uint64_t)ceil((double)a.top_p * (double)W);
-        if (need < 1) need = 1;
-      }
-      const int d = find_cross(L, nb, need, above, total);
-      need -= above;
-      prefix |= (uint32_t)d << sh;
-      pmask |= (uint32_t)(nb - 1) << sh;
-    }
-    return prefix;
+    return radix_select<DT>(a, L, row, listed, p_alone, R, mass, need, floor_key2, W, given);
   };
   uint32_t key = 0;
   if (use_k) key = select(false, (uint64_t)a.top_k, floor_key, 0, false);
@@ -1949,6 +1974,12 @@ __global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
   // a bf16 key's low 16 bits: zero for positive values, all ones for negative
   if (DT == SPEC_DTYPE_BF16) key |= (key & 0x80000000u) ? 0u : 0xffffu;
   if (t == 0) *out = (use_k || use_p) ? funkey(key) : NEG_INF;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFThreads) void filter_kernel(FArgs a) {
+  __shared__ FLds L;
+  filter_row<DT>(a, (int)(blockIdx.x / (unsigned)a.NR2), (int)(blockIdx.x % (unsigned)a.NR2), L);
 }
 
 // ------------------------------------------------------------------ probes

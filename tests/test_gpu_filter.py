@@ -53,6 +53,10 @@ def _thresholds_match(case, torch, top_k, top_p, offset=0):
         if case.mode == "sample":
             rows += [(case.draft[b, i], G + 1 + i) for i in range(g)]
         for row, slot in rows:
+            if not np.isfinite(inputs.widen(row)).any():  # no finite logit: -inf
+                assert thr[b, slot] == -np.inf, (b, slot, thr[b, slot])
+                checked += 1
+                continue
             _, tau, mg = oracle.filter_row(row, temperature=case.T, top_k=top_k, top_p=top_p,
                                            margin=True)
             if mg < parity.FILTER_MARGIN:
@@ -84,6 +88,49 @@ def test_thresholds_with_ties_and_unaligned_rows(torch):
     case.draft = inputs.f32_to_bf16_bits(np.round(d * 2) / 2)
     for top_k, top_p in ((7, 1.0), (0, 0.6), (40, 0.95), (1, 1.0)):
         top_p = float(np.float32(top_p))
+        _thresholds_match(case, torch, top_k, top_p, offset=1)
+
+
+# Full-size and larger vocabularies, bf16 and fp32, rows aligned and one
+# element off 16-byte alignment (an unaligned head and tail on every row).
+LARGE = [("bf16", 128256, 0), ("bf16", 128256, 1), ("f32", 50257, 0), ("f32", 32773, 1),
+         ("f32", 128256, 0), ("bf16", 500000, 1)]
+
+
+@pytest.mark.parametrize("dtype,V,offset", LARGE)
+@pytest.mark.parametrize("top_k,top_p", [(50, 0.9), (256, 1.0), (1, 1.0), (7, 0.5)])
+def test_thresholds_large_rows(torch, dtype, V, offset, top_k, top_p):
+    top_p = float(np.float32(top_p))
+    case = inputs.make_case(3, rnd=71, B=2, V=V, dtype=dtype)
+    print(f"thresholds {dtype} V={V} offset={offset} k={top_k} p={top_p}", flush=True)
+    _thresholds_match(case, torch, top_k, top_p, offset=offset)
+
+
+def test_thresholds_edge_rows(torch):
+    """Full-vocabulary rows that push the top-k floor off its candidate list
+    or onto special cases: a coarse grid of ties, all values equal (every
+    entry a candidate: the whole-row passes), fewer finite entries than k,
+    a few hundred finite entries in a row of -inf, a dead row, signed
+    zeros."""
+    V = 128256
+    case = inputs.make_case(3, rnd=72, B=4, V=V)
+    rng = np.random.default_rng(72)
+    t = inputs.widen(case.target).copy()
+    t[0, 0] = np.round(t[0, 0] * 2) / 2
+    t[0, 1] = 0.0
+    t[1, 0] = -np.inf
+    t[1, 0, rng.choice(V, 10, replace=False)] = rng.normal(0, 3, 10)
+    t[1, 1] = -np.inf
+    t[1, 1, rng.choice(V, 300, replace=False)] = rng.normal(0, 3, 300)
+    t[2, 0] = -np.inf
+    t[2, 1] = np.where(rng.random(V) < 0.5, -0.0, 0.0)
+    t[2, 1, rng.choice(V, 20, replace=False)] = 1.0
+    t[3, 2] = np.round(t[3, 2])
+    case.target = inputs.f32_to_bf16_bits(t)
+    for top_k, top_p in ((50, 0.9), (1, 1.0), (256, 1.0), (20, 0.3)):
+        top_p = float(np.float32(top_p))
+        print(f"edge rows k={top_k} p={top_p}", flush=True)
+        _thresholds_match(case, torch, top_k, top_p)
         _thresholds_match(case, torch, top_k, top_p, offset=1)
 
 
