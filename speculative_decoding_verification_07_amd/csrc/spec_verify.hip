@@ -9,11 +9,9 @@
 //      loads (the next row's loads in flight while the current row is
 //      reduced) and reduces each to the softmax pair (m, S) = (largest logit,
 //      sum 2^((l - m) log2e / T)); greedy: (largest logit, lowest index).
-//   2. It publishes its pairs to the workspace and counts itself in on the
-//      row's arrival counter.
-//      Greedy: the workgroup that arrives last merges the row's pairs,
-//      compares the draft tokens with the target's argmaxes and writes the
-//      row.
+//   2. It publishes its pairs to the workspace.
+//      Greedy: slice 0 waits for the group's pairs, merges them, compares
+//      the draft tokens with the target's argmaxes and writes the row.
 //      Sampling: every workgroup waits for its whole group, merges the pairs
 //      in the same fixed order (so all of them hold bit-identical statistics),
 //      runs every acceptance test u_i q_i(x_i) < p_i(x_i) at once and finds
@@ -571,10 +569,10 @@ __device__ __forceinline__ void slice_am(const Slice<DT, R>& s, const Geom& g, i
 // back or invalidating the L2 (an agent-scope release fence writes back an
 // XCD's whole L2, an acquire invalidates it; both cost microseconds).  A
 // writer stores its data with agent-scope atomic stores, which are performed
-// at the device's coherence point, waits for them to complete (publish), and
-// only then counts itself in.  A reader that has seen the count loads the
-// data with agent-scope atomic loads, served at the same coherence point.
-__device__ __forceinline__ void publish() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// at the device's coherence point.  Every stored word is non-zero, so a
+// reader needs no separate count: it polls the data words themselves with
+// agent-scope atomic loads, served at the same coherence point, until each
+// reads non-zero.
 __device__ __forceinline__ void put64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1471,9 +1469,7 @@ __device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
 template <int DT, int MODE, int R, bool AL, bool FILT>
 __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a) {
   constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // a drawn token (sample, point)
-  using E = Elt<DT>;
   __shared__ Lds L;
-  const int t = threadIdx.x;
   const int b = (int)(blockIdx.x / (unsigned)a.NC), c = (int)(blockIdx.x % (unsigned)a.NC);
   const int g = a.gam[b];
   if (g < 0 || g > a.G) {
@@ -1804,7 +1800,7 @@ __device__ __forceinline__ const char* filter_row_of(const FArgs& a, int b, int 
 template <int DT>
 __device__ __forceinline__ void filter_row(const FArgs& a, int b, int slot, FLds& L) {
   using E = Elt<DT>;
-  const int t = threadIdx.x, lane = t & 63;
+  const int t = threadIdx.x;
   float* out = a.thr + (int64_t)b * (2 * a.G + 1) + slot;
   const char* row = filter_row_of<DT>(a, b, slot);
   if (!row) {
