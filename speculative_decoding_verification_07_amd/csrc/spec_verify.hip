@@ -37,8 +37,10 @@
 
 #include <math.h>
 #include <stdint.h>
-#include <type_traits>
 #include <string.h>
+
+#include <atomic>
+#include <type_traits>
 
 #include "spec_verify.h"
 
@@ -1316,7 +1318,7 @@ __device__ __forceinline__ void ring_pick(const Ring<DT, R>& ring, int k, Slice<
   }
 }
 
-template <int DT, int R, bool RESID, bool KNOCK, bool RING, bool FILT, bool AL>
+template <int DT, int R, bool RESID, bool KNOCK, bool RING, bool FILT, bool AL, bool PRIO>
 __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
                      const Decision& dc, const Ring<DT, R>& ring) {
   using E = Elt<DT>;
@@ -1391,6 +1393,7 @@ __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g,
   };
   opaque(st), opaque(sd);
   segment_sums<DT, R, RESID>(d, st, sd, gt, v);
+  if (PRIO) __builtin_amdgcn_s_setprio(0);
   int owner = publish_sum(0);
   if (KNOCK && !(z > 0.0)) {
     // rounding left p_n without mass outside x_n: p_n is a point mass at x_n
@@ -1466,10 +1469,20 @@ __device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
 #ifndef SPEC_MIN_WAVES
 #define SPEC_MIN_WAVES 4
 #endif
-template <int DT, int MODE, int R, bool AL, bool FILT>
+template <int DT, int MODE, int R, bool AL, bool FILT, bool PRIO>
 __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a) {
   constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // a drawn token (sample, point)
   __shared__ Lds L;
+  // When the whole grid is resident (PRIO), the phases run at falling
+  // wave priority (3 streaming, 2 merge and decision, 1 draw weights, 0 the
+  // slice-sum wait and the owner's search).  A CU's four workgroups are at
+  // different phases, and issue goes to the oldest wave of the highest
+  // priority: this way a workgroup still streaming its rows does not lose
+  // issue slots to another's latency-bound tail.  Priority orders issue
+  // only; a low-priority wave still issues whenever the others wait, so
+  // every wait still ends.  With more workgroups than slots, a slowed tail
+  // holds its slot and delays the next workgroup, so plain arbitration wins.
+  if (PRIO) __builtin_amdgcn_s_setprio(3);
   const int b = (int)(blockIdx.x / (unsigned)a.NC), c = (int)(blockIdx.x % (unsigned)a.NC);
   const int g = a.gam[b];
   if (g < 0 || g > a.G) {
@@ -1484,6 +1497,7 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   Ring<DT, R> ring;
   stream_rows<DT, MODE, R, AL, FILT>(a, L, b, g, nrows, lo, len, ring);
   publish_pairs<kSample>(a, L, b, c, nrows);
+  if (PRIO) __builtin_amdgcn_s_setprio(2);
   if (kSample) gather_logits<DT, MODE, FILT>(a, b, g, in);  // in flight during the wait
 
   if (!kSample) {
@@ -1501,14 +1515,15 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   merge_group<true>(a, L, b, nrows);
   decide<DT, MODE>(a, L, b, g, in, c == 0);
   const Decision dc = L.dec;
+  if (PRIO) __builtin_amdgcn_s_setprio(1);
   if (!dc.dead) {
     constexpr bool kRing = MODE == SPEC_MODE_SAMPLE;
     if (dc.resid && MODE == SPEC_MODE_POINT)
-      draw<DT, R, false, true, false, FILT, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, false, true, false, FILT, AL, PRIO>(a, L, b, c, g, lo, len, nrows, dc, ring);
     else if (dc.resid)
-      draw<DT, R, true, false, kRing, FILT, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, true, false, kRing, FILT, AL, PRIO>(a, L, b, c, g, lo, len, nrows, dc, ring);
     else
-      draw<DT, R, false, false, kRing, FILT, AL>(a, L, b, c, g, lo, len, nrows, dc, ring);
+      draw<DT, R, false, false, kRing, FILT, AL, PRIO>(a, L, b, c, g, lo, len, nrows, dc, ring);
   } else {
     row_exit(a, L, b, nrows);
   }
@@ -2026,30 +2041,51 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP -
 
 bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
+// Compute units of the calling thread's current device, asked once per
+// device (0 if the runtime cannot tell).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64 && n > 0) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// prio: phase priorities (the whole grid resident).  Grids larger than the
+// chip come from the largest slices (R = 4) unless the tuning forces smaller
+// ones, so only R = 4 has a variant without them.
 template <int DT, int MODE, bool AL, bool FILT>
-void launch_r(int R, dim3 grid, hipStream_t s, const Args& a) {
+void launch_r(int R, bool prio, dim3 grid, hipStream_t s, const Args& a) {
   if (R == 1)
-    hipLaunchKernelGGL((verify_kernel<DT, MODE, 1, AL, FILT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 1, AL, FILT, true>), grid, dim3(kThreads), 0, s, a);
   else if (R == 2)
-    hipLaunchKernelGGL((verify_kernel<DT, MODE, 2, AL, FILT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 2, AL, FILT, true>), grid, dim3(kThreads), 0, s, a);
+  else if (prio)
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL, FILT, true>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL, FILT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL, FILT, false>), grid, dim3(kThreads), 0, s, a);
 }
 
 // greedy never filters (the filters keep the largest logit)
 template <int DT, int MODE>
-void launch(int R, bool al, bool filt, dim3 grid, hipStream_t s, const Args& a) {
+void launch(int R, bool prio, bool al, bool filt, dim3 grid, hipStream_t s, const Args& a) {
   constexpr bool kCanFilter = MODE != SPEC_MODE_GREEDY;
   if (kCanFilter && filt) {
     if (al)
-      launch_r<DT, MODE, true, kCanFilter>(R, grid, s, a);
+      launch_r<DT, MODE, true, kCanFilter>(R, prio, grid, s, a);
     else
-      launch_r<DT, MODE, false, kCanFilter>(R, grid, s, a);
+      launch_r<DT, MODE, false, kCanFilter>(R, prio, grid, s, a);
   } else {
     if (al)
-      launch_r<DT, MODE, true, false>(R, grid, s, a);
+      launch_r<DT, MODE, true, false>(R, prio, grid, s, a);
     else
-      launch_r<DT, MODE, false, false>(R, grid, s, a);
+      launch_r<DT, MODE, false, false>(R, prio, grid, s, a);
   }
 }
 
@@ -2116,6 +2152,10 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.B = B, a.G = G, a.V = V, a.NC = p.NC, a.CL = p.CL, a.NR = p.NR;
   a.k2 = draws ? (float)(1.4426950408889634 / (double)T) : 1.f;
   a.max_spin = 1u << 22;  // ~0.2 s of polling: far beyond any legitimate wait
+  // phase priorities only when every workgroup is resident from the start
+  // (four per CU is what the largest variants' registers allow)
+  const int cus = device_cus();
+  const bool prio = cus > 0 && p.total <= (int64_t)4 * cus;
   hipStream_t s = (hipStream_t)stream;
   dim3 grid((unsigned)p.total);
   // every row 16-byte aligned: both bases aligned and a row a whole number
@@ -2131,18 +2171,18 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   }
   if (dtype == SPEC_DTYPE_BF16) {
     if (sample)
-      launch<SPEC_DTYPE_BF16, SPEC_MODE_SAMPLE>(p.R, al, filt, grid, s, a);
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_SAMPLE>(p.R, prio, al, filt, grid, s, a);
     else if (draws)
-      launch<SPEC_DTYPE_BF16, SPEC_MODE_POINT>(p.R, al, filt, grid, s, a);
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_POINT>(p.R, prio, al, filt, grid, s, a);
     else
-      launch<SPEC_DTYPE_BF16, SPEC_MODE_GREEDY>(p.R, al, false, grid, s, a);
+      launch<SPEC_DTYPE_BF16, SPEC_MODE_GREEDY>(p.R, prio, al, false, grid, s, a);
   } else {
     if (sample)
-      launch<SPEC_DTYPE_F32, SPEC_MODE_SAMPLE>(p.R, al, filt, grid, s, a);
+      launch<SPEC_DTYPE_F32, SPEC_MODE_SAMPLE>(p.R, prio, al, filt, grid, s, a);
     else if (draws)
-      launch<SPEC_DTYPE_F32, SPEC_MODE_POINT>(p.R, al, filt, grid, s, a);
+      launch<SPEC_DTYPE_F32, SPEC_MODE_POINT>(p.R, prio, al, filt, grid, s, a);
     else
-      launch<SPEC_DTYPE_F32, SPEC_MODE_GREEDY>(p.R, al, false, grid, s, a);
+      launch<SPEC_DTYPE_F32, SPEC_MODE_GREEDY>(p.R, prio, al, false, grid, s, a);
   }
   return hip_status(hipGetLastError());
 }
