@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gamma_rule.h"
 #include "spec_adapt.h"
 #include "spec_ngram.h"
@@ -145,7 +147,10 @@ __device__ void write_row(const NArgs& a, int b, int L, bool valid, unsigned w, 
 // AL: 16-byte vector loads (aligned rows).  REG: n_max <= kRegN, so every
 // match length comes from a fixed set of compares over registers; otherwise
 // a thread walks back through LDS where its token equals the last one.
-template <bool AL, bool REG>
+// PRIO (the whole grid resident): staging runs at wave priority 3, the
+// scan at 2 and the hand-off at 1, so that a CU's younger workgroups still
+// loading their chunks get issue slots before older ones' scans.
+template <bool AL, bool REG, bool PRIO>
 __global__ __launch_bounds__(kThreads) void ngram_kernel(NArgs a) {
   __shared__ int sfx[SPEC_NGRAM_MAX_N];  // sfx[i] = c[L-1-i]
   __shared__ __align__(16) int tok[kHalo + kChunk];  // c[cbase - kHalo .. cbase + kChunk)
@@ -154,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void ngram_kernel(NArgs a) {
   __shared__ unsigned win;
   __shared__ int last_wg;
 
+  if (PRIO) __builtin_amdgcn_s_setprio(3);
   const int b = blockIdx.x % a.B;
   const int k = blockIdx.x / a.B;
   const int tid = threadIdx.x;
@@ -192,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void ngram_kernel(NArgs a) {
     }
   }
   __syncthreads();
+  if (PRIO) __builtin_amdgcn_s_setprio(2);
 
   unsigned best = 0;
   if (active && base <= last) {
@@ -245,6 +252,7 @@ __global__ __launch_bounds__(kThreads) void ngram_kernel(NArgs a) {
   if ((tid & 63) == 0) red[tid >> 6] = best;
   __syncthreads();
   if (tid == 0) {
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
     unsigned w = red[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) w = max(w, red[i]);
@@ -304,19 +312,45 @@ int ngram_args(const int32_t* context, const int32_t* ctx_len, int B, int stride
   return SPEC_OK;
 }
 
+// Compute units of the calling thread's current device, asked once per
+// device (0 if the runtime cannot tell).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64 && n > 0) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <bool PRIO>
+void launch_variant(bool al, bool reg, dim3 grid, hipStream_t s, const NArgs& a) {
+  if (al && reg)
+    hipLaunchKernelGGL((ngram_kernel<true, true, PRIO>), grid, dim3(kThreads), 0, s, a);
+  else if (al)
+    hipLaunchKernelGGL((ngram_kernel<true, false, PRIO>), grid, dim3(kThreads), 0, s, a);
+  else if (reg)
+    hipLaunchKernelGGL((ngram_kernel<false, true, PRIO>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((ngram_kernel<false, false, PRIO>), grid, dim3(kThreads), 0, s, a);
+}
+
 int ngram_launch(const NArgs& a, void* stream) {
   const bool al = aligned(a.ctx, 16) && a.stride % 4 == 0;
   const dim3 grid((unsigned)(a.B * a.nch));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool reg = a.n_max <= kRegN;
-  if (al && reg)
-    hipLaunchKernelGGL((ngram_kernel<true, true>), grid, dim3(kThreads), 0, s, a);
-  else if (al)
-    hipLaunchKernelGGL((ngram_kernel<true, false>), grid, dim3(kThreads), 0, s, a);
-  else if (reg)
-    hipLaunchKernelGGL((ngram_kernel<false, true>), grid, dim3(kThreads), 0, s, a);
+  // wave priorities only when every workgroup is resident from the start
+  const int cus = device_cus();
+  if (cus > 0 && (int64_t)a.B * a.nch <= (int64_t)4 * cus)
+    launch_variant<true>(al, reg, grid, s, a);
   else
-    hipLaunchKernelGGL((ngram_kernel<false, false>), grid, dim3(kThreads), 0, s, a);
+    launch_variant<false>(al, reg, grid, s, a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP - (int)e;
 }
