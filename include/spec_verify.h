@@ -37,9 +37,12 @@
  * once the stream has completed the call.  Argument errors are reported by
  * the return value before anything is launched, and then no output is
  * written.  The library allocates no memory and keeps no state other than
- * the caller's workspace (and a process-wide tuning override, see
- * spec_verify_tune).  Calls on distinct workspaces may run concurrently;
- * two calls that share a workspace must be ordered (same stream).
+ * the caller's workspace (plus a process-wide tuning override, see
+ * spec_verify_tune, and each device's compute-unit count, asked once).  The
+ * CU count picks between launch variants that differ in speed only (wave
+ * priorities when the whole grid fits on the device at once); results are
+ * the same.  Calls on distinct workspaces may run concurrently; two calls
+ * that share a workspace must be ordered (same stream).
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
