@@ -5,8 +5,8 @@
  *
  * Sources: "Speculative decoding", mhtirogla.ai, "Efficiency" (tokens per
  * pass E = sum_{i<=gamma} alpha^i and wall-clock speedup E / (1 + gamma c))
- * and "Implementation notes" (gamma adaptive per request from running
- * acceptance, speculation off once the batch is compute-bound); "Speculative
+ * and "Implementation notes" (a per-request length that follows the observed
+ * acceptance; no drafting once the batch is compute-bound); "Speculative
  * decoding: the secretary who types ahead of the boss", blog.lo0.es, "When
  * speculative does NOT help" (the large-batch crossover); "Speculative
  * decoding", inference.tusharamrit.in (adapt gamma from recent acceptance);

@@ -54,6 +54,8 @@ def _load():
         lib.oracle_draw_cdf.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, D,
                                         i32, i32, P, i32, D]
         lib.oracle_draw_cdf.restype = i32
+        lib.oracle_draw_index.argtypes = [P, i32, D, P]
+        lib.oracle_draw_index.restype = i32
         lib.oracle_filter_row.argtypes = [P, i32, i32, D, i32, D, P, P, P]
         lib.oracle_filter_row.restype = i32
         lib.oracle_ngram_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P]
@@ -161,6 +163,17 @@ def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0, mo
                               _ptr(uniforms), _ptr(gamma), None, B, G, V, float(temperature),
                               int(mode), int(row), _ptr(cdf), int(top_k), float(top_p))
     return cdf, int(pos)
+
+
+def draw_index(w, u):
+    """The oracle's inverse-CDF draw over given non-negative weights:
+    (index, Z).  Test hook for the tie-break and the fallback rule."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    z = ctypes.c_double(0.0)
+    j = _load().oracle_draw_index(_ptr(w), int(w.size), float(u), ctypes.byref(z))
+    if j < 0:
+        raise ValueError("oracle refused its arguments")
+    return int(j), float(z.value)
 
 
 def filter_row(logits, *, temperature=1.0, top_k=0, top_p=1.0, margin=False):

@@ -484,6 +484,16 @@ int oracle_draw_cdf(const void* target, const void* draft, int dtype, const int3
   return pos;
 }
 
+/* The inverse-CDF draw alone, over caller-given non-negative weights
+ * w[0..V) with uniform u (test hook: it pins the draw's tie-break and its
+ * fallback rule directly).  Writes Z = sum w; returns the drawn index. */
+int oracle_draw_index(const double* w, int V, double u, double* z_out) {
+  if (!w || V <= 0) return -1;
+  oracle_ctx c = {NULL, NULL, OR_F32, NULL, NULL, NULL, NULL, 1, 0, V, 1.0, OR_SAMPLE,
+                  OR_FAULT_NONE, 0, 1.0};
+  return draw_index(&c, w, u, z_out, NULL);
+}
+
 /* The filtered distribution of one stored logit row (what a drafter that
  * applies the same top-k / top-p would sample from): prob[0..V) and the
  * threshold tau (entries with l >= tau kept).  Returns 0, or -1 for refused
@@ -503,9 +513,9 @@ int oracle_filter_row(const void* logits, int dtype, int V, double T, int top_k,
 
 /* ---------------------------------------------------------------- drafting
  * Prompt-lookup (n-gram) drafting ("Speculative decoding", mhtirogla.ai,
- * "Implementation notes": copy the continuation of the last matching n-gram
- * from the prompt; tusharamrit, "Self-speculation": search the existing
- * context for the current suffix and propose what followed it last time).
+ * "Implementation notes"; tusharamrit, "Self-speculation"): the drafter
+ * finds where the context's latest n tokens occurred before and proposes
+ * the tokens that came after that occurrence.
  * Reading: for n = n_max down to n_min, the suffix is the last n tokens of
  * the context c[0..L); its most recent earlier occurrence is the largest j
  * with j + n <= L - 1 (so that a token follows it) and c[j..j+n) equal to
@@ -557,14 +567,15 @@ int oracle_ngram_draft(const int32_t* context, const int32_t* ctx_len, int B, in
 }
 
 /* --------------------------------------------------------------- adaptive gamma
- * Per-request draft length from running acceptance, speculation off at large
- * batch ("Speculative decoding", mhtirogla.ai, "Efficiency" and
- * "Implementation notes": expected tokens per pass, wall-clock speedup
- * E / (1 + gamma c), gamma adaptive per request from running acceptance and
- * off once the batch is compute-bound; blog.lo0.es "When speculative does
- * NOT help": the large-batch crossover; tusharamrit "Speculative decoding":
- * adapt gamma from recent acceptance, speedup table; dantp-ai "How much
- * speedup, really?": an optimal lookahead for every acceptance rate).
+ * Each request's next draft length from the acceptance it has seen so far,
+ * and no speculation once the batch is large ("Speculative decoding",
+ * mhtirogla.ai, "Efficiency" and "Implementation notes": tokens per pass,
+ * the wall-clock speedup E / (1 + gamma c), a per-request length that
+ * follows the observed acceptance, and turning drafting off when the batch
+ * is compute-bound; blog.lo0.es "When speculative does NOT help": the
+ * large-batch crossover; tusharamrit "Speculative decoding": the speedup
+ * table; dantp-ai "How much speedup, really?": the best lookahead depends
+ * on the acceptance rate).
  * Reading:
  *   state per row: discounted accepted count A and tested count T.
  *   observation of a round with g = gamma_used[b] >= 1 and n = n_acc[b] >= 0:

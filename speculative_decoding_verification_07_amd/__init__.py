@@ -139,6 +139,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on(stream):
+    """Allocation context of the stream a call runs on.  Temporaries (a
+    workspace, outputs, probes) are allocated on that stream, so torch's
+    caching allocator hands their blocks to nothing else until the work
+    queued there with them has run."""
+    import contextlib
+    return contextlib.nullcontext() if stream is None else _torch().cuda.stream(stream)
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.float32:
@@ -204,14 +213,18 @@ def _filtering(top_k, top_p) -> bool:
 
 def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in=None,
            *, temperature: float = 1.0, mode: int = SAMPLE, workspace: Workspace | None = None,
-           out=None, stream=None, probe: bool = False, top_k: int = 0, top_p: float = 1.0):
+           out=None, stream=None, probe: bool = False, top_k: int = 0, top_p: float = 1.0,
+           check: bool = False):
     """Run spec_verify (spec_verify_filtered when top_k or top_p filter) on
     torch device tensors.
 
     Returns (tokens [B, G+1] int32, n_accepted [B] int32, new_len [B] int32),
     plus a dict of probe tensors (px, qx, z, m, s) when probe=True.  `out`
     may pass preallocated (tokens, n_accepted, new_len).  The call is
-    asynchronous on `stream` (default: torch's current stream)."""
+    asynchronous on `stream` (default: torch's current stream).  Temporaries
+    are allocated on that stream.  check=True waits for the call and reads
+    the workspace's diagnostic word, raising WaitGaveUp if a workgroup gave
+    up waiting (which a correct launch never does)."""
     torch = _torch()
     lib = load()
     B, G, V = _shape_check(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row,
@@ -219,12 +232,13 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, k
     dt = _dtype_code(target_logits)
     dev = target_logits.device
     need = workspace_bytes(B, G, V, dt, mode)
-    if workspace is None:
-        workspace = Workspace(need, device=dev, stream=stream)
-    if out is None:
-        out = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
-               torch.empty(B, dtype=torch.int32, device=dev),
-               torch.empty(B, dtype=torch.int32, device=dev))
+    with _on(stream):
+        if workspace is None:
+            workspace = Workspace(need, device=dev, stream=stream)
+        if out is None:
+            out = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+                   torch.empty(B, dtype=torch.int32, device=dev),
+                   torch.empty(B, dtype=torch.int32, device=dev))
     tok, nacc, nlen = out
     filt = _filtering(top_k, top_p)
     head = [_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
@@ -237,19 +251,36 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, k
             _check(lib.spec_verify_filtered(*args), "spec_verify_filtered")
         else:
             _check(lib.spec_verify(*args), "spec_verify")
+        if check:
+            _check_diagnostics(workspace, stream)
         return tok, nacc, nlen
     nan = float("nan")
-    pr = {
-        "px": torch.full((B, G), nan, dtype=torch.float32, device=dev),
-        "qx": torch.full((B, G), nan, dtype=torch.float32, device=dev),
-        "z": torch.full((B,), nan, dtype=torch.float32, device=dev),
-        "m": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
-        "s": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
-    }
+    with _on(stream):
+        pr = {
+            "px": torch.full((B, G), nan, dtype=torch.float32, device=dev),
+            "qx": torch.full((B, G), nan, dtype=torch.float32, device=dev),
+            "z": torch.full((B,), nan, dtype=torch.float32, device=dev),
+            "m": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
+            "s": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
+        }
     fn = lib.spec_verify_filtered_probe if filt else lib.spec_verify_probe
     _check(fn(*args, _ptr(pr["px"]), _ptr(pr["qx"]), _ptr(pr["z"]), _ptr(pr["m"]),
               _ptr(pr["s"])), "spec_verify_probe")
+    if check:
+        _check_diagnostics(workspace, stream)
     return tok, nacc, nlen, pr
+
+
+class WaitGaveUp(RuntimeError):
+    """A workgroup of the call gave up waiting for the rest of its batch row
+    (diagnostic bit 0): the rows it served hold the sentinel, and the
+    workspace must be zero-filled again before its next use."""
+
+
+def _check_diagnostics(workspace, stream):
+    flags = workspace.diagnostics(stream)
+    if flags & 1:
+        raise WaitGaveUp(f"a verify workgroup gave up waiting (diagnostics 0x{flags:x})")
 
 
 def filter_thresholds(target_logits, draft_logits, gamma_per_row, *, temperature: float = 1.0,
@@ -260,7 +291,8 @@ def filter_thresholds(target_logits, draft_logits, gamma_per_row, *, temperature
     torch = _torch()
     B, G, V = _shape_check(target_logits, draft_logits, None, None, gamma_per_row, None, mode)
     if out is None:
-        out = torch.empty((B, 2 * G + 1), dtype=torch.float32, device=target_logits.device)
+        with _on(stream):
+            out = torch.empty((B, 2 * G + 1), dtype=torch.float32, device=target_logits.device)
     _check(load().spec_filter_thresholds(_ptr(target_logits), _ptr(draft_logits),
                                          _ptr(gamma_per_row), B, G, V,
                                          _dtype_code(target_logits), float(temperature),
@@ -325,11 +357,12 @@ def ngram_draft(context, ctx_len, *, n_min: int = 1, n_max: int = 4, gamma: int 
             raise ValueError(f"{name} must be a contiguous device tensor")
     B, stride = context.shape
     dev = context.device
-    if workspace is None:
-        workspace = Workspace(ngram_workspace_bytes(B), device=dev, stream=stream)
-    if out is None:
-        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
-               *(torch.empty(B, dtype=torch.int32, device=dev) for _ in range(3)))
+    with _on(stream):
+        if workspace is None:
+            workspace = Workspace(ngram_workspace_bytes(B), device=dev, stream=stream)
+        if out is None:
+            out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+                   *(torch.empty(B, dtype=torch.int32, device=dev) for _ in range(3)))
     draft, length, n, pos = out
     _check(load().spec_ngram_draft(_ptr(context), _ptr(ctx_len), B, stride, int(n_min),
                                    int(n_max), int(gamma), _ptr(draft), _ptr(length), _ptr(n),
@@ -366,7 +399,8 @@ class GammaControl:
         if alpha is not None and (alpha.dtype != torch.float64 or tuple(alpha.shape) != (self.B,)):
             raise ValueError("alpha must be float64 [B]")
         if out is None:
-            out = torch.empty(self.B, dtype=torch.int32, device=self.state.device)
+            with _on(stream):
+                out = torch.empty(self.B, dtype=torch.int32, device=self.state.device)
         g, decay, pa, pw, c, off = self.params
         _check(load().spec_gamma_control(_ptr(n_accepted), _ptr(gamma_used), _ptr(active),
                                          _ptr(gamma_limit), _ptr(self.state), self.B, g, decay,
@@ -395,11 +429,12 @@ def ngram_draft_adaptive(context, ctx_len, control: GammaControl, n_accepted=Non
             raise ValueError(f"{name} must be a contiguous int32 device tensor")
     G, decay, pa, pw, c, off = control.params
     dev = context.device
-    if workspace is None:
-        workspace = Workspace(ngram_workspace_bytes(B), device=dev, stream=stream)
-    if out is None:
-        out = (torch.empty((B, G), dtype=torch.int32, device=dev),
-               *(torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)))
+    with _on(stream):
+        if workspace is None:
+            workspace = Workspace(ngram_workspace_bytes(B), device=dev, stream=stream)
+        if out is None:
+            out = (torch.empty((B, G), dtype=torch.int32, device=dev),
+                   *(torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)))
     draft, length, n, pos, gam = out
     _check(load().spec_ngram_draft_adaptive(
         _ptr(context), _ptr(ctx_len), B, stride, int(n_min), int(n_max), G, _ptr(n_accepted),
@@ -415,7 +450,8 @@ def probe_read(src, out=None, stream=None):
     nbytes = src.numel() * src.element_size()
     nb = int(load().spec_probe_read_blocks(nbytes))
     if out is None:
-        out = torch.empty(nb, dtype=torch.float32, device=src.device)
+        with _on(stream):
+            out = torch.empty(nb, dtype=torch.float32, device=src.device)
     _check(load().spec_probe_read(_ptr(src), nbytes, _ptr(out), _stream_handle(stream)),
            "spec_probe_read")
     return out

@@ -54,6 +54,7 @@ constexpr int kStage = 1024;          // LDS entries for staging a group's pairs
 constexpr int kMaxVocab = 1 << 20;
 constexpr int kDefaultTargetWorkgroups = 1024;
 constexpr unsigned kDiagSpin = 1u, kDiagZeroResid = 2u;
+constexpr int kWsWords = 5;  // draw words per slice (residual: W0, D, S_t, S_d; exact W)
 // Per-row exit counter, on its own 128-byte line.
 constexpr int kLine = 32;
 enum { kExit = 0 };
@@ -117,7 +118,7 @@ int make_plan(int B, int G, int V, int dtype, int mode, Plan* p) {
   p->off_ctr = off; off = align256(off + sizeof(unsigned) * kRowWords * (size_t)B);
   p->off_part = off; off = align256(off + sizeof(uint64_t) * (size_t)B * p->NC * p->NR);
   p->off_wsum = off;
-  if (draws) off = align256(off + sizeof(uint64_t) * 2 * (size_t)B * p->NC);
+  if (draws) off = align256(off + sizeof(uint64_t) * kWsWords * (size_t)B * p->NC);
   p->off_thr = off;  // filter thresholds, written by the filtered calls only
   if (draws) off = align256(off + sizeof(float) * (size_t)B * (2 * G + 1));
   p->bytes = off;
@@ -143,10 +144,11 @@ struct Args {
   unsigned* hdr;
   unsigned* ctr;   // [B][kRowWords]
   uint64_t* part;  // [B][NC][NR] pairs of each slice: (m, S) or (max, argmax + 1)
-  uint64_t* wsum;  // [B][2][NC] draw weight sums of each slice (two attempts)
+  uint64_t* wsum;  // [B][5][NC] draw sums of each slice (see the draw)
   const float* thr;  // [B][2G+1] filter thresholds (entries below are cut), or null
   int B, G, V, NC, CL, NR;
   float k2;        // log2(e) / T
+  double k2d;      // log2(e) / T in double precision (the draw)
   unsigned max_spin;
 };
 
@@ -598,19 +600,45 @@ __device__ __forceinline__ void after(unsigned v) { asm volatile("" ::"v"(v) : "
 
 // Waits (in the calling thread) for a published word: every published word
 // is non-zero and a completed call leaves the workspace zero, so the load
-// that returns non-zero returns the data.  Gives up after max_spin polls
-// and flags the diagnostic word.
-__device__ uint64_t poll64(const Args& a, const uint64_t* p) {
+// that returns non-zero returns the data.  Gives up after max_spin polls:
+// flags the diagnostic word and *gave_up (the workgroup's flag in LDS, from
+// which the workgroup writes its row's sentinel instead of using the word).
+__device__ uint64_t poll64(const Args& a, const uint64_t* p, int* gave_up) {
   uint64_t v = get64(p);
   for (unsigned n = 0; v == 0; ++n) {
     if (n > a.max_spin) {
       atomicOr(&a.hdr[1], kDiagSpin);
+      *gave_up = 1;
       break;
     }
     __builtin_amdgcn_s_sleep(1);
     v = get64(p);
   }
   return v;
+}
+
+// The same for N words p[0], p[stride], ..., all loads in flight at once: one
+// round trip per attempt instead of one per word.
+template <int N>
+__device__ void poll_n(const Args& a, const uint64_t* p, int stride, uint64_t (&v)[N],
+                       int* gave_up) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = get64(p + (int64_t)k * stride);
+  for (unsigned n = 0;; ++n) {
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) all = all && v[k] != 0;
+    if (all) return;
+    if (n > a.max_spin) {
+      atomicOr(&a.hdr[1], kDiagSpin);
+      *gave_up = 1;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if (v[k] == 0) v[k] = get64(p + (int64_t)k * stride);
+  }
 }
 
 // ------------------------------------------------------------------ LDS
@@ -620,31 +648,48 @@ struct Decision {
   int resid;    // 1: draw from the residual at n, 0: bonus draw from p_g
   int xn;       // x_n (point-mass drafts: the token the residual excludes)
   float ustar;  // uniform of the draw
+  float tx;     // target logit at x_n (point-mass drafts: the excluded token)
   float mt, st, md, sd;  // (max, exp-sum) of target row n and draft row n
 };
 
-// Result of the search over a row's slice sums: the slice holding tau (-1:
-// none has weight), whether rounding forced the fallback, the sum of the
-// slices before it, and the total Z.
+// Result of the search over a row's published slice sums, in every thread.
 struct Owner {
-  int r;
-  int fallback;
-  double base, z;
+  int r;         // slice holding tau (-1: no slice has weight)
+  int fallback;  // rounding left no slice whose running sum exceeds tau
+  int zero;      // residual without mass: drawn from p_n instead
+  int retry;     // residual (nearly) without mass: search again with the exact rho
+  double base;   // sum of the slices before r
+  double z;      // Z in units of e (residual: S_t Z)
+  double drho;   // rho - rho0 (residual)
+  double st;     // S_t (residual)
+  double rho;    // S_t / S_d (residual)
 };
 
+constexpr int kMaxSeg = 6;  // draw segments of a thread: head, up to 4 body rounds, tail
+
 struct Lds {
-  float wm[kMaxRows][kWaves];  // per-row wave partials: m (greedy: max)
-  float ws[kMaxRows][kWaves];  // S (greedy: argmax bits)
+  union {
+    struct {                       // streaming and merging
+      float wm[kMaxRows][kWaves];  // per-row wave partials: m (greedy: max)
+      float ws[kMaxRows][kWaves];  // S (greedy: argmax bits)
+      uint64_t stage[kStage];      // a group's published pairs
+    } sm;
+    struct {                       // the draw: each thread's segment sums
+      double w[kMaxSeg][kThreads];
+      double dd[kMaxSeg][kThreads];
+    } dr;
+  };
   float tau[kMaxRows];         // filter threshold of each vocabulary row (filtered calls)
   float M[kMaxRows];           // merged row statistics, row r = target i (r = i)
   float S[kMaxRows];           //   or draft i (r = g + 1 + i); greedy: argmax bits
-  uint64_t stage[kStage];
   double red_d[8 * kWaves];
+  uint4 vt, vd;                // the owner thread's vector, for the element search
   unsigned long long mask[kWaves];
   Decision dec;
   Owner own;
   double dbl;
   int pick, last;
+  int bad;  // a poll of this workgroup gave up waiting
 };
 
 // ------------------------------------------------------------------ block helpers
@@ -851,14 +896,14 @@ __device__ __forceinline__ void stream_rows(const Args& a, Lds& L, int b, int g,
         wave_slice_ms<DT, R, FILT>(buf[j], geo[j], a.k2, tau, m, sm);
         if (lane == 0 && r < nrows) {
           const int rr = stream_row<MODE>(r, g);
-          L.wm[rr][w] = m, L.ws[rr][w] = sm;
+          L.sm.wm[rr][w] = m, L.sm.ws[rr][w] = sm;
         }
       } else {
         float v;
         int ix;
         slice_am<DT, R>(buf[j], geo[j], lo, v, ix);
         wave_am_dpp(v, ix);
-        if (lane == 0 && r < nrows) L.wm[r][w] = v, L.ws[r][w] = __int_as_float(ix);
+        if (lane == 0 && r < nrows) L.sm.wm[r][w] = v, L.sm.ws[r][w] = __int_as_float(ix);
       }
     }
   }
@@ -866,24 +911,29 @@ __device__ __forceinline__ void stream_rows(const Args& a, Lds& L, int b, int g,
   for (int j = 0; j < NB; ++j) ring.buf[j] = buf[j], ring.geo[j] = geo[j];
   __syncthreads();
   for (int r = t; r < nrows; r += kThreads) {
-    float m = L.wm[r][0], s = L.ws[r][0];
+    float m = L.sm.wm[r][0], s = L.sm.ws[r][0];
     for (int k = 1; k < kWaves; ++k) {
       if (kSample) {
-        ms_merge(m, s, L.wm[r][k], L.ws[r][k], a.k2);
+        ms_merge(m, s, L.sm.wm[r][k], L.sm.ws[r][k], a.k2);
       } else {
         int i = __float_as_int(s);
-        am_merge(m, i, L.wm[r][k], __float_as_int(L.ws[r][k]));
+        am_merge(m, i, L.sm.wm[r][k], __float_as_int(L.sm.ws[r][k]));
         s = __int_as_float(i);
       }
     }
+    // filtered: a slice whose entries are all cut publishes the identity
+    // (-inf, 0), whatever its raw maximum (which could be +0, whose pair
+    // would be an all-zero word that readers take for "not yet published")
+    if (FILT && kSample && s == 0.f) m = NEG_INF;
     L.M[r] = m, L.S[r] = s;
   }
   __syncthreads();
 }
 
 // Publishes this slice's pairs (entry r of the slice's record).  No written
-// word is zero: S >= 1 whenever m is finite, m = -inf has non-zero bits, and
-// the argmax is stored plus one.  Nothing waits for the stores: readers poll
+// word is zero: S >= 1 whenever m is finite (a slice whose filter cut every
+// entry publishes m = -inf), m = -inf has non-zero bits, and the argmax is
+// stored plus one.  Nothing waits for the stores: readers poll
 // the words themselves.
 template <bool kSample>
 __device__ void publish_pairs(const Args& a, Lds& L, int b, int c, int nrows) {
@@ -905,7 +955,7 @@ __device__ void merge_rows_grouped(const Args& a, Lds& L, int r0, int r1, int nc
   for (int rb = r0 + w * kRowsPerWave; rb < r1; rb += kWaves * kRowsPerWave) {
     const int r = rb + sub;
     const bool have = r < r1 && c < nc;
-    const uint64_t st = have ? L.stage[(r - r0) * nc + c] : 0;
+    const uint64_t st = have ? L.sm.stage[(r - r0) * nc + c] : 0;
     if (kSample) {
       float m = have ? lo_f(st) : NEG_INF, s = have ? hi_f(st) : 0.f;
       group_ms<LPR>(m, s, a.k2);
@@ -926,7 +976,7 @@ template <bool kSample>
 __device__ void merge_rows_wide(const Args& a, Lds& L, int r0, int r1, int nc) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int r = r0 + w; r < r1; r += kWaves) {
-    const uint64_t* st = &L.stage[(r - r0) * nc];
+    const uint64_t* st = &L.sm.stage[(r - r0) * nc];
     if (kSample) {
       float m = NEG_INF, s = 0.f;
       for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
@@ -956,7 +1006,7 @@ __device__ void merge_group(const Args& a, Lds& L, int b, int nrows) {
     const int cnt = (r1 - r0) * nc;
     for (int k = t; k < cnt; k += kThreads) {
       const int r = r0 + k / nc, c = k % nc;
-      L.stage[k] = poll64(a, &base[(int64_t)c * a.NR + r]);
+      L.sm.stage[k] = poll64(a, &base[(int64_t)c * a.NR + r], &L.bad);
     }
     __syncthreads();
     if (nc <= 4)
@@ -1060,6 +1110,7 @@ __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, 
     // n is uniform (from the ballot): lane reads, not shuffles
     const float ustar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in.u), n < g ? n + 1 : g));
     const int xn = __builtin_amdgcn_readlane(in.x, n < g ? n : 0);
+    const float tx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in.tv), n < g ? n : 0));
     if (write_out) {
       // gamma_max <= 63, so lane i owns output position i (and holds x_i)
       if (lane <= a.G && !(kSample && lane == n && !sentinel)) {
@@ -1078,7 +1129,7 @@ __device__ void decide(const Args& a, Lds& L, int b, int g, const Gathered& in, 
     }
     if (lane == 0) {
       Decision d;
-      d.n = n, d.dead = sentinel, d.resid = n < g, d.xn = xn, d.ustar = ustar;
+      d.n = n, d.dead = sentinel, d.resid = n < g, d.xn = xn, d.ustar = ustar, d.tx = tx;
       d.mt = L.M[n], d.st = L.S[n];
       d.md = !kPoint && n < g ? L.M[g + 1 + n] : 0.f;
       d.sd = !kPoint && n < g ? L.S[g + 1 + n] : 1.f;
@@ -1097,151 +1148,320 @@ __device__ void write_sentinel(const Args& a, int b) {
 }
 
 // ------------------------------------------------------------------ draw
-// Draw weights.  Residual after a rejection at n (RESID):
-// p_j = 2^((t_j - mt) k2) / St, q_j likewise, w_j = max(0, p_j - q_j).
-// Otherwise w_j = 2^((t_j - mt) k2) * scale: the bonus draw (scale 1, the
-// bonus row's own sum being the normaliser) or p_j for a residual that
-// rounding left without mass (scale 1/St).  Weights are fp32; their sums and
-// prefix sums are accumulated in fp64 so that the CDF is as exact as the fp32
-// weights allow.  Absent elements (-inf) weigh 0.
+// The drawn distribution is formed in double precision from the logits of
+// the row(s) it is drawn from.  An fp32 weight carries ~1e-7 relative
+// rounding (more through the rounding of its exponent), and at V ~ 10^5 the
+// CDF steps are ~1e-5 apart, so fp32 weights move enough boundaries past u
+// to change a few draws in 10^4; in fp64 the boundaries sit within ~1e-10
+// of the exact ones.
+//
+// Weights, in units of e(l) = 2^(l k2 - R), k2 = log2(e)/T and R = m k2 in
+// fp64 for the row's largest logit m:
+//   bonus draw (all drafts accepted):        w_j = e_t(j)  (its sum is Z)
+//   point-mass draft rejected at n:          w_j = e_t(j), x_n set to -inf
+//   residual after a rejection at n:         w_j = max(0, e_t(j) - rho e_d(j))
+// with rho = S_t / S_d, the ratio of the two rows' sums of e, so that
+// w_j = S_t max(0, p_n(j) - q_n(j)).  S_t and S_d are known only once every
+// slice has summed its share, so each slice forms its weights against the
+// provisional ratio rho0 of the fp32 statistics and publishes, besides its
+// sums of e_t and e_d, W0 = sum_j max(0, e_t - rho0 e_d) and D = the sum of
+// e_d over the entries with positive weight.  Then
+//   W(rho) = W0 - (rho - rho0) D,
+// exact but for entries whose ratio e_t/e_d lies between rho0 and rho
+// (|rho - rho0| ~ 1e-6 rho), each off by at most |rho - rho0| e_d(j).  A
+// residual whose corrected mass is below 2^-30 S_t (zero, or nearly, in
+// exact arithmetic) is formed again against the exact rho.
+//
+// The code of this step runs once per row and vocabulary slice, so it is
+// kept compact (one copy of each loop body, flags at run time): the whole
+// kernel must stay small enough for the instruction cache that the four
+// workgroups of a compute unit, each in a different phase, share.
+//
+// Sources: "Speculative decoding" (mhtirogla.ai), "How it works" steps 3-4
+// and the `sample` routine of "Code"; tusharamrit, the modified
+// rejection-sampling rule (the residual norm(max(0, p - q))).
 struct DrawParams {
-  float rt, st_inv, rd, sd_inv, k2;  // references R(m) of target/draft row n, 1/S
-  float scale;                       // plain weights: 1 (bonus) or 1/St (fallback)
+  double k2;    // log2(e) / T
+  double rt;    // R of target row n (bonus: row g)
+  double rd;    // R of draft row n (residual)
+  double rho0;  // ratio the residual weights are formed against
+  int resid;    // 1: residual of two rows; 0: the weights e_t of one row
 };
 
-template <bool RESID>
-__device__ __forceinline__ float draw_weight(const DrawParams& d, float t, float q_logit) {
-  const float et = ex2(fmaf(t, d.k2, -d.rt));
-  if (RESID) {
-    const float p = et * d.st_inv;
-    const float q = ex2(fmaf(q_logit, d.k2, -d.rd)) * d.sd_inv;
-    return fmaxf(p - q, 0.f);
+// Minimax polynomial (relative error) for 2^r on [-1/2, 1/2], degree 7, from
+// the Remez exchange (csrc/exp2_poly.py derives them): largest relative error
+// 4.0e-11, coefficients of r^0 .. r^7.
+constexpr double kExp2Poly[8] = {
+    0.999999999961682,
+    0.6931471807284468,
+    0.24022651198157982,
+    0.05550410353449052,
+    0.009618027253625058,
+    0.0013333922562610663,
+    0.00015469291153107813,
+    1.5201921815236906e-05,
+};
+
+// 2^x in double precision: x = n + r with n the nearest integer, so
+// |r| <= 1/2 and r is exact; 2^r from the polynomial in Horner form, then the
+// exact scaling by 2^n.  Arguments below -1100, and -inf, give 0 (the exact
+// value is below the smallest subnormal).  Here x <= 0 always (logits never
+// exceed their row's maximum).
+__device__ __forceinline__ double exp2_f64(double x) {
+  x = fmax(x, -1100.0);
+  const double n = __builtin_rint(x);
+  const double r = x - n;
+  double p = kExp2Poly[7];
+#pragma unroll
+  for (int k = 6; k >= 0; --k) p = fma(p, r, kExp2Poly[k]);
+  return __builtin_ldexp(p, (int)n);
+}
+
+__device__ __forceinline__ double e_of(float l, double k2, double ref) {
+  return exp2_f64(fma((double)l, k2, -ref));
+}
+
+// One element pair of the residual against rho0: adds to the running sums.
+__device__ __forceinline__ void add_pair(const DrawParams& d, float t, float q, double& w,
+                                         double& dd, double& st, double& sd) {
+  const double et = e_of(t, d.k2, d.rt), ed = e_of(q, d.k2, d.rd);
+  st += et;
+  sd += ed;
+  const double x = fma(-d.rho0, ed, et);
+  const bool pos = x > 0.0;
+  w += pos ? x : 0.0;
+  dd += pos ? ed : 0.0;
+}
+
+// Vector k of a slice selected at run time (register by register), -inf
+// where the slice has none.
+template <int DT, int R>
+__device__ __forceinline__ uint4 vsel(const Slice<DT, R>& s, int k, const Geom& g) {
+  uint4 v = s.v[0];
+#pragma unroll
+  for (int j = 1; j < R; ++j) {
+    const bool take = k == j;
+    v.x = take ? s.v[j].x : v.x, v.y = take ? s.v[j].y : v.y;
+    v.z = take ? s.v[j].z : v.z, v.w = take ? s.v[j].w : v.w;
   }
-  return et * d.scale;
-}
-
-template <int DT, bool RESID>
-__device__ __forceinline__ void vec_weights(const DrawParams& d, const uint4& vt, const uint4& vd,
-                                            float* w) {
   using E = Elt<DT>;
-  float ft[E::kVec], fd[E::kVec];
-  E::unpack(vt, ft);
-  if (RESID) E::unpack(vd, fd);
-#pragma unroll
-  for (int e = 0; e < E::kVec; ++e) w[e] = draw_weight<RESID>(d, ft[e], RESID ? fd[e] : 0.f);
+  const uint4 ninf = make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+  return k * kThreads + (int)threadIdx.x < g.nv ? v : ninf;
 }
 
-// This thread's weight sums by segment: [0] head, [1 + k] body round k,
-// [R + 1] tail (index order of the slice).  A vector's weights are added in
-// fp32, in element order (a rounding of a few units in 1e-7 of the vector's
-// own sum), and the search within a vector repeats exactly those additions.
-template <int DT, int R, bool RESID>
-__device__ __forceinline__ void segment_sums(const DrawParams& d, const Slice<DT, R>& st,
-                                             const Slice<DT, R>& sd, const Geom& g,
-                                             double (&v)[R + 2]) {
+// This thread's sums of one slice, by segment in index order: [0] the head,
+// [1 + k] body round k (one 16-byte vector), [R + 1] the tail.  The segment
+// values go to LDS (L.dr.w: the weights against rho0 -- plain draws: the e_t;
+// L.dr.dd: residual, the e_d where that weight is positive) for the owner's
+// search; the thread's totals {W0, D, S_t, S_d} are returned.
+template <int DT, int R, bool AL>
+__device__ void slice_sums(const DrawParams& d, const Slice<DT, R>& st, const Slice<DT, R>& sd,
+                           const Geom& g, Lds& L, double (&tot)[4]) {
   using E = Elt<DT>;
-  v[0] = (double)draw_weight<RESID>(d, st.hd, sd.hd);
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    float w[E::kVec];
-    vec_weights<DT, RESID>(d, vget(st, k, g), vget(sd, k, g), w);
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < E::kVec; ++e) s += w[e];
-    v[1 + k] = (double)s;
-    __builtin_amdgcn_sched_barrier(0);  // one vector's weights live at a time
-  }
-  v[R + 1] = (double)draw_weight<RESID>(d, st.tl, sd.tl);
-}
-
-// Finds the slice holding tau = u * Z from the group's published slice sums
-// (one per thread).  Returns the slice and the sum of the slices before it
-// (base); z_out = Z.  When rounding leaves no slice whose running sum exceeds
-// tau, returns the last slice with positive weight and sets fallback; -1 if
-// no slice has weight.
-__device__ int find_owner(const Args& a, const uint64_t* ws, int nc, float u, Lds& L,
-                          double& base, double& z_out, bool& fallback) {
   const int t = threadIdx.x;
-  if (nc <= 64) {
-    // every slice sum fits one wave: wave 0 scans and searches, and hands the
-    // result to the others through LDS (one barrier instead of a block scan)
-    if (t < 64) {
-      const double v = t < nc ? __longlong_as_double((long long)~poll64(a, &ws[t])) : 0.0;
-      double excl;
-      const double incl = wave_scan_d(v, excl);
-      const double z = readlane_d(incl, 63);
-      const double tau = (double)u * z;
-      const unsigned long long hit = __ballot(v > 0.0 && tau < incl);
-      const unsigned long long pos = __ballot(v > 0.0);
-      const int r = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : -1);
-      const double bs = r >= 0 ? readlane_d(excl, r) : 0.0;
-      if (t == 0) L.own = Owner{r, hit == 0, bs, z};
+  double W = 0.0, D = 0.0, ST = 0.0, SD = 0.0;
+  // head and tail: one element each (rows that are not 16-byte aligned)
+  double hw = 0.0, hd = 0.0, tw = 0.0, td = 0.0;
+  if (!AL) {
+    if (d.resid) {
+      add_pair(d, st.hd, sd.hd, hw, hd, ST, SD);
+      add_pair(d, st.tl, sd.tl, tw, td, ST, SD);
+    } else {
+      hw = e_of(st.hd, d.k2, d.rt);
+      tw = e_of(st.tl, d.k2, d.rt);
     }
+  }
+  L.dr.w[0][t] = hw, L.dr.dd[0][t] = hd;
+  L.dr.w[R + 1][t] = tw, L.dr.dd[R + 1][t] = td;
+  W = hw + tw, D = hd + td;
+#pragma unroll 1
+  for (int k = 0; k < R; ++k) {
+    float ft[E::kVec], fd[E::kVec];
+    E::unpack(vsel(st, k, g), ft);
+    double w = 0.0, dd = 0.0;
+    if (d.resid) {
+      E::unpack(vsel(sd, k, g), fd);
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) add_pair(d, ft[e], fd[e], w, dd, ST, SD);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) w += e_of(ft[e], d.k2, d.rt);
+    }
+    L.dr.w[1 + k][t] = w, L.dr.dd[1 + k][t] = dd;
+    W += w, D += dd;
+  }
+  if (!d.resid) ST = W;
+  tot[0] = W, tot[1] = D, tot[2] = ST, tot[3] = SD;
+}
+
+// The published words of slice c, word k at ws[k * NC + c]:
+//   plain draws:  [0] W = sum of e_t
+//   residual:     [0] W0, [1] D, [2] S_t, [3] S_d (against rho0), and, when a
+//                 second pass against the exact rho is needed, [4] W.
+// Each is a non-negative double stored as the complement of its bits (sign
+// bit set, so never zero).
+constexpr int kWs = kWsWords;
+__device__ __forceinline__ uint64_t enc_d(double x) { return ~(uint64_t)__double_as_longlong(x); }
+__device__ __forceinline__ double dec_d(uint64_t v) { return __longlong_as_double((long long)~v); }
+
+// Kinds of search over the published words.
+enum { kPlain = 0, kLinear = 1, kExact = 2 };
+
+// Waits for the group's published slice words and finds the slice holding
+// tau = u Z, the same way in every workgroup (fixed-order sums).  Slices run
+// one per lane of wave 0 (NC <= 64) or one per thread (NC <= 256).
+//   kPlain:  the weights of word 0.
+//   kLinear: the residual against rho0, corrected to the exact rho.  When the
+//            corrected Z is below 2^-30 S_t (a residual that is zero, or
+//            nearly, in exact arithmetic, where the rounding of the
+//            correction is no longer small against Z) the search is not
+//            done and `retry` asks for the exact pass.
+//   kExact:  the residual of word 4, formed against the exact rho; if it has
+//            no mass at all, p_n (its weights e_t are word 2) instead.
+__device__ Owner find_owner(const Args& a, const uint64_t* ws, int kind, double rho0, float u,
+                            Lds& L) {
+  const int t = threadIdx.x, nc = a.NC;
+  const bool one_wave = nc <= 64;
+  if (one_wave && t >= 64) {
     __syncthreads();
     const Owner o = L.own;
-    z_out = o.z;
-    fallback = o.fallback;
-    base = o.r >= 0 ? o.base : 0.0;
-    return o.r;
+    __syncthreads();
+    return o;
   }
-  const double v = t < nc ? __longlong_as_double((long long)~poll64(a, &ws[t])) : 0.0;
-  double incl, excl, z;
-  block_scan_d(v, L, incl, excl, z);
-  z_out = z;
-  const double tau = (double)u * z;
-  int r = block_first(v > 0.0 && tau < incl, L);
-  fallback = r < 0;
-  if (r < 0) r = block_last(v > 0.0, L);
-  if (r < 0) {
-    base = 0.0;
-    return -1;
+  const bool mine = t < nc;
+  auto total = [&](double x) -> double {
+    if (one_wave) return wave_sum_d(x);
+    double tot[1];
+    const double v[1] = {x};
+    block_sums_n<1>(v, tot, L);
+    return tot[0];
+  };
+  auto scan = [&](double x, double& excl, double& z) -> double {
+    if (one_wave) {
+      const double incl = wave_scan_d(x, excl);
+      z = readlane_d(incl, 63);
+      return incl;
+    }
+    double incl;
+    block_scan_d(x, L, incl, excl, z);
+    return incl;
+  };
+  Owner o{-1, 0, 0, 0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  // one round trip for all the words of the slice: words 0..3 (linear),
+  // words 2 and 4 (exact: S_t, W), word 0 (plain)
+  uint64_t v[4] = {0, 0, 0, 0};
+  if (mine) {
+    if (kind == kLinear)
+      poll_n<4>(a, &ws[t], nc, v, &L.bad);
+    else if (kind == kExact)
+      poll_n<2>(a, &ws[2 * nc + t], 2 * nc, *(uint64_t(*)[2])v, &L.bad);
+    else
+      poll_n<1>(a, &ws[t], nc, *(uint64_t(*)[1])v, &L.bad);
   }
-  if (t == r) L.dbl = excl;
+  auto dv = [&](int k) { return mine ? dec_d(v[k]) : 0.0; };
+  double w, s_t = 0.0;  // this slice's weight and (residual) its S_t
+  if (kind == kLinear) {
+    s_t = dv(2);
+    o.st = total(s_t);
+    o.rho = o.st / total(dv(3));
+    o.drho = o.rho - rho0;
+    w = fma(-o.drho, dv(1), dv(0));  // the slice's weight against rho
+  } else if (kind == kExact) {
+    s_t = dv(0);
+    w = dv(1);
+    o.st = total(s_t);
+  } else {
+    w = dv(0);
+  }
+  double excl, z;
+  double incl = scan(w, excl, z);
+  if (kind == kLinear && !(z > __builtin_ldexp(o.st, -30))) {
+    o.retry = 1;
+  } else {
+    if (kind == kExact && !(z > 0.0)) {
+      // rounding left the residual without mass (exact arithmetic never
+      // does): draw from p_n, whose weights are e_t, with the same uniform
+      o.zero = 1;
+      w = s_t;
+      incl = scan(w, excl, z);
+    }
+    const double tau = (double)u * z;
+    auto first = [&](bool pred) {
+      if (one_wave) {
+        const unsigned long long m = __ballot(pred);
+        return m ? __ffsll((long long)m) - 1 : -1;
+      }
+      return block_first(pred, L);
+    };
+    auto last = [&](bool pred) {
+      if (one_wave) {
+        const unsigned long long m = __ballot(pred);
+        return m ? 63 - __clzll((long long)m) : -1;
+      }
+      return block_last(pred, L);
+    };
+    o.r = first(w > 0.0 && tau < incl);
+    o.fallback = o.r < 0;
+    if (o.r < 0) o.r = last(w > 0.0);
+  }
+  o.z = z;
+  // the chosen slice's exclusive sum, from its own lane / thread
+  if (t == (o.r < 0 ? 0 : o.r)) {
+    o.base = o.r >= 0 ? excl : 0.0;
+    L.own = o;
+  }
   __syncthreads();
-  base = L.dbl;
+  o = L.own;
   __syncthreads();
-  return r;
+  return o;
 }
 
 // Inverse CDF inside the owner's slice: the first element of positive weight
 // whose running sum (base + the weights before it, in index order) exceeds
-// tau; if rounding leaves none, the last element with positive weight.
-// v: this thread's segment sums, tot: their block totals (the ones the
-// slice's published sum was formed from).  Returns the index in the row.
-template <int DT, int R, bool RESID>
+// tau; if rounding leaves none, the last element with positive weight.  Each
+// thread's segment values (from LDS) are its weights against the final rho;
+// the segment holding tau comes from their block totals, the thread from a
+// block scan of that segment, and the element from a scan over the weights
+// of that thread's elements, one per lane of wave 0, formed as slice_sums
+// formed them.  Returns the index in the row.
+template <int DT, int R>
 __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const Slice<DT, R>& sd,
-                            const Geom& g, int lo, const double (&v)[R + 2],
-                            const double (&tot)[R + 2], double base, double tau, Lds& L) {
+                            const Geom& g, int lo, double drho, double base, double tau, bool fb,
+                            Lds& L) {
   using E = Elt<DT>;
   constexpr int NS = R + 2;
   const int t = threadIdx.x;
+  double v[NS], tot[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k)
+    v[k] = d.resid ? fma(-drho, L.dr.dd[k][t], L.dr.w[k][t]) : L.dr.w[k][t];
+  block_sums_n<NS>(v, tot, L);
   // the segment holding tau (all threads alike)
   double carry = base;
   int seg = -1, lastseg = -1;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (tot[s] > 0.0) lastseg = s;
-    if (seg < 0) {
-      if (tot[s] > 0.0 && tau < carry + tot[s])
-        seg = s;
+  for (int k = 0; k < NS; ++k) {
+    if (tot[k] > 0.0) lastseg = k;
+    if (seg < 0 && !fb) {
+      if (tot[k] > 0.0 && tau < carry + tot[k])
+        seg = k;
       else
-        carry += tot[s];
+        carry += tot[k];
     }
   }
-  bool fb = false;
   if (seg < 0) {
     if (lastseg < 0) return lo;  // no mass in the slice (cannot happen for an owner)
     fb = true;
     seg = lastseg;
     carry = base;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      if (s < seg) carry += tot[s];
+    for (int k = 0; k < NS; ++k)
+      if (k < seg) carry += tot[k];
   }
   double vs = 0.0;
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (s == seg) vs = v[s];
+  for (int k = 0; k < NS; ++k)
+    if (k == seg) vs = v[k];
   double incl, excl, ts;
   block_scan_d(vs, L, incl, excl, ts);
   int th = fb ? -1 : block_first(vs > 0.0 && tau < carry + incl, L);
@@ -1250,34 +1470,41 @@ __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const S
     th = block_last(vs > 0.0, L);
   }
   if (th < 0) th = 0;
+  if (seg == 0) return lo + th;              // a head element
+  if (seg == NS - 1) return lo + g.jb + th;  // a tail element
+  // thread th's vector of round seg - 1, handed to wave 0 through LDS
   if (t == th) {
-    Slice<DT, R> st2 = st, sd2 = sd;
-    opaque(st2), opaque(sd2);
-    int j;
-    if (seg == 0) {
-      j = lo + t;
-    } else if (seg == NS - 1) {
-      j = lo + g.jb + t;
-    } else {
-      // thread th scans its vector of round seg - 1
-      float w[E::kVec];
+    L.vt = vsel(st, seg - 1, g);
+    L.vd = d.resid ? vsel(sd, seg - 1, g) : L.vt;
+    L.dbl = carry + excl;  // the sum of everything before the vector
+  }
+  __syncthreads();
+  if (t < 64) {
+    float ft[E::kVec], fd[E::kVec];
+    E::unpack(L.vt, ft);
+    E::unpack(L.vd, fd);
+    float lt = NEG_INF, lq = NEG_INF;
 #pragma unroll
-      for (int k = 0; k < R; ++k)
-        if (k == seg - 1) vec_weights<DT, RESID>(d, vget(st2, k, g), vget(sd2, k, g), w);
-      const double before = carry + excl;
-      float ps = 0.f;  // the vector's running sum, as segment_sums forms it
-      int pick = -1, lp = 0;
-#pragma unroll
-      for (int e = 0; e < E::kVec; ++e) {
-        ps += w[e];
-        if (w[e] > 0.f) {
-          lp = e;
-          if (pick < 0 && !fb && tau < before + (double)ps) pick = e;
-        }
+    for (int e = 0; e < E::kVec; ++e)
+      if (t == e) lt = ft[e], lq = fd[e];
+    double wl = 0.0;  // the element's weight against rho
+    if (t < E::kVec) {
+      const double et = e_of(lt, d.k2, d.rt);
+      if (d.resid) {
+        const double ed = e_of(lq, d.k2, d.rd);
+        const double x = fma(-d.rho0, ed, et);
+        wl = x > 0.0 ? fma(-drho, ed, x) : 0.0;
+      } else {
+        wl = et;
       }
-      j = lo + g.head + ((seg - 1) * kThreads + t) * E::kVec + (pick >= 0 ? pick : lp);
     }
-    L.pick = j;
+    double ex;
+    const double run = wave_scan_d(wl, ex);
+    const double before = L.dbl;
+    const unsigned long long hit = __ballot(wl > 0.0 && !fb && tau < before + run);
+    const unsigned long long pos = __ballot(wl > 0.0);
+    const int e = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+    if (t == 0) L.pick = lo + g.head + ((seg - 1) * kThreads + th) * E::kVec + e;
   }
   __syncthreads();
   const int j = L.pick;
@@ -1286,9 +1513,9 @@ __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const S
 }
 
 // Step 3 of a live sampled row: every workgroup of the group sums its slice
-// of the drawn distribution and publishes the sum; the workgroup whose slice
-// holds tau = u * Z writes the token.  KNOCK (point-mass drafts, after a
-// rejection): the residual max(0, p_n - q_n) with q_n the indicator of x_n is
+// of the drawn distribution and publishes the sums; the workgroup whose slice
+// holds tau = u * Z writes the token.  KNOCK (point-mass drafts): after a
+// rejection the residual max(0, p_n - q_n) with q_n the indicator of x_n is
 // p_n without x_n, drawn as the plain weights of row n with x_n set to -inf.
 __device__ void row_exit(const Args& a, Lds& L, int b, int nrows);
 
@@ -1318,20 +1545,50 @@ __device__ __forceinline__ void ring_pick(const Ring<DT, R>& ring, int k, Slice<
   }
 }
 
-template <int DT, int R, bool RESID, bool KNOCK, bool RING, bool FILT, bool AL, bool PRIO>
-__device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
+// The softmax sum of a merged pair relative to the raw maximum m, i.e. with
+// the rounding of its reference R(m) undone: sum_j 2^((l_j - m) k2).
+__device__ __forceinline__ float s_rel(float m, float s, float k2) {
+  return m == NEG_INF ? s : s * ex2(-fmaf(m, k2, -ref_of(m, k2)));
+}
+
+// Publishes this slice's totals {W0, D, S_t, S_d} (nw = 4) or {W} (nw = 1)
+// at word `w0` onward.
+__device__ __forceinline__ void publish_sums(const Args& a, uint64_t* ws, int c, int w0, int nw,
+                                             const double (&mine)[4], Lds& L) {
+  double tot[4];
+  block_sums_n<4>(mine, tot, L);
+  const int t = threadIdx.x;
+  if (t < nw) {
+    double x = tot[0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k)
+      if (t == k) x = tot[k];
+    put64(&ws[(w0 + t) * a.NC + c], enc_d(x));
+  }
+}
+
+// KNOCK: point-mass drafts (q_i is the indicator of x_i); RING: the ring
+// holds the last rows streamed (sampling).
+template <int DT, int R, bool KNOCK, bool RING, bool FILT, bool AL, bool PRIO>
+__device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
                      const Decision& dc, const Ring<DT, R>& ring) {
   using E = Elt<DT>;
-  // RING: the ring holds the last NB rows streamed (sampling)
   constexpr int NB = RING ? Ring<DT, R>::NB : 0;
   const int t = threadIdx.x;
-  DrawParams d{ref_of(dc.mt, a.k2), 1.f / dc.st, ref_of(dc.md, a.k2), 1.f / dc.sd, a.k2, 1.f};
   const int n = dc.n;
+  const bool resid = !KNOCK && dc.resid;  // a residual of two rows
+  const bool knock = KNOCK && dc.resid;   // point-mass draft rejected at n
+  DrawParams d;
+  d.k2 = a.k2d;
+  d.rt = (double)dc.mt * a.k2d;
+  d.rd = resid ? (double)dc.md * a.k2d : 0.0;
+  d.rho0 = resid ? (double)s_rel(dc.mt, dc.st, a.k2) / (double)s_rel(dc.md, dc.sd, a.k2) : 0.0;
+  d.resid = resid;
   // stream indices of the rows drawn from (the inverse of stream_row): t_n
   // and d_n at 2(g-1-n)+1 and +2 when sampling, t_n at g-n with point-mass
   // drafts, t_g first of all for the bonus draw
-  const int kt = RESID ? 2 * (g - 1 - n) + 1 : (KNOCK ? g - n : 0);
-  const int kd = RESID ? kt + 1 : kt;
+  const int kt = resid ? 2 * (g - 1 - n) + 1 : (knock ? g - n : 0);
+  const int kd = kt + 1;
   Slice<DT, R> st, sd;
   Geom gt;
   // (the picks pass through opaque(): otherwise the optimiser merges "take
@@ -1339,16 +1596,17 @@ __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g,
   // which sends the whole ring to scratch memory)
   // with point-mass drafts the stream ends with t_0 and its reloads past
   // the end read t_0 again, so a rejection at 0 finds its row in the ring
-  const bool from_ring = RING ? kt >= nrows - NB : KNOCK && kt == nrows - 1;
+  const bool from_ring = RING ? kt >= nrows - NB : knock && kt == nrows - 1;
   if (from_ring) {
     ring_pick(ring, kt % Ring<DT, R>::NB, st, gt);
     opaque(st);
   } else {
-    const char* tp = row_of<DT>(a, b, g, n) + (int64_t)lo * E::kBytes;
+    const char* tp = row_of<DT>(a, b, g, resid || knock ? n : g) + (int64_t)lo * E::kBytes;
     gt = geom_of<DT, AL>(tp, len);
     load_slice<DT, R, AL>(tp, gt, st);
   }
-  if (RESID) {
+  sd = st;
+  if (resid) {
     // the weights pair element j of both rows: the draft slice takes the
     // target slice's register layout
     Geom gd;
@@ -1364,38 +1622,39 @@ __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g,
       else
         load_slice_as<DT, R>(dp, gt, sd);
     }
-  } else {
-    sd = st;
   }
   if (FILT) {  // the filtered rows: cut entries weigh 0
     const float* th = a.thr + (int64_t)b * (2 * a.G + 1);
-    mask_slice(st, th[n]);
-    if (RESID) mask_slice(sd, th[a.G + 1 + n]);
+    mask_slice(st, th[resid || knock ? n : g]);
+    if (resid) mask_slice(sd, th[a.G + 1 + n]);
   }
-  if (KNOCK) knock_out(st, gt, dc.xn - lo);
-  uint64_t* ws = a.wsum + (int64_t)b * 2 * a.NC;
-  double base = 0.0, z = 0.0;
-  bool fallback = false;
-  // attempt 0: the weights of the call; attempt 1 (residual only): p_n, when
-  // rounding left the residual without mass (exact arithmetic never does)
-  // a slice sum is stored as the complement of its bits: never zero (the sum
-  // is non-negative, so its sign bit is clear)
-  // this thread's segment sums v and their block totals tot are kept for
-  // the search; the slice sum is the totals added in segment order
-  double v[R + 2], tot[R + 2];
-  auto publish_sum = [&](int attempt) {
-    block_sums_n<R + 2>(v, tot, L);
-    double acc = 0.0;
-#pragma unroll
-    for (int s = 0; s < R + 2; ++s) acc += tot[s];
-    if (t == 0) put64(&ws[attempt * a.NC + c], ~(uint64_t)__double_as_longlong(acc));
-    return find_owner(a, ws + attempt * a.NC, a.NC, dc.ustar, L, base, z, fallback);
-  };
+  if (KNOCK && knock) knock_out(st, gt, dc.xn - lo);
+  uint64_t* ws = a.wsum + (int64_t)b * kWs * a.NC;
   opaque(st), opaque(sd);
-  segment_sums<DT, R, RESID>(d, st, sd, gt, v);
-  if (PRIO) __builtin_amdgcn_s_setprio(0);
-  int owner = publish_sum(0);
-  if (KNOCK && !(z > 0.0)) {
+  double mine[4];
+  slice_sums<DT, R, AL>(d, st, sd, gt, L, mine);
+  // the rest is latency-bound: above the other workgroups' draw weights
+  if (PRIO) __builtin_amdgcn_s_setprio(2);
+  publish_sums(a, ws, c, 0, resid ? 4 : 1, mine, L);
+  Owner o = find_owner(a, ws, resid ? kLinear : kPlain, d.rho0, dc.ustar, L);
+  bool exact = false;
+  if (o.retry && !L.bad) {
+    // a residual without mass, or nearly, in exact arithmetic: form the
+    // weights again against the exact rho and search those (rare: the
+    // correction's rounding could otherwise decide the draw)
+    exact = true;
+    d.rho0 = o.rho;
+    opaque(st), opaque(sd);
+    slice_sums<DT, R, AL>(d, st, sd, gt, L, mine);
+    publish_sums(a, ws, c, 4, 1, mine, L);
+    o = find_owner(a, ws, kExact, 0.0, dc.ustar, L);
+  }
+  if (L.bad) {  // a slice's sums never arrived (cannot happen in a correct launch)
+    write_sentinel(a, b);
+    row_exit(a, L, b, nrows);
+    return;
+  }
+  if (knock && !(o.z > 0.0)) {
     // rounding left p_n without mass outside x_n: p_n is a point mass at x_n
     // (the same published sums give every workgroup the same z)
     if (c == 0 && t == 0) {
@@ -1406,31 +1665,39 @@ __device__ __forceinline__ void draw(const Args& a, Lds& L, int b, int c, int g,
     row_exit(a, L, b, nrows);
     return;
   }
-  bool resid = RESID;
-  if (RESID && !(z > 0.0)) {
-    if (c == 0 && t == 0) atomicOr(&a.hdr[1], kDiagZeroResid);
-    resid = false;
-    d.scale = d.st_inv;
-    opaque(st);
-    segment_sums<DT, R, false>(d, st, st, gt, v);
-    owner = publish_sum(1);
-  }
+  if (o.zero && c == 0 && t == 0) atomicOr(&a.hdr[1], kDiagZeroResid);
+  int owner = o.r;
+  bool fallback = o.fallback;
   if (owner < 0) {  // no weight anywhere (cannot happen for a live row)
     owner = 0;
     fallback = true;
   }
   // every read of the row's workspace entries is done: leave the row now, so
   // that the exit ticket and the clearing overlap the owner's search (which
-  // uses only its registers)
+  // uses only its registers and LDS)
   row_exit(a, L, b, nrows);
   if (c != owner) return;
   opaque(st), opaque(sd);
-  const double tau = fallback ? __builtin_inf() : (double)dc.ustar * z;
-  const int j = resid ? slice_search<DT, R, true>(d, st, sd, gt, lo, v, tot, base, tau, L)
-                      : slice_search<DT, R, false>(d, st, st, gt, lo, v, tot, base, tau, L);
+  if (o.zero) {
+    // residual without mass: the weights of p_n, e_t alone
+    d.resid = 0;
+    slice_sums<DT, R, AL>(d, st, sd, gt, L, mine);
+  }
+  const double tau = (double)dc.ustar * o.z;
+  // linear: the weights against rho0 corrected by drho; exact: the weights
+  // against rho itself (d.rho0 = rho, no correction)
+  const int j = slice_search<DT, R>(d, st, sd, gt, lo, exact ? 0.0 : o.drho, o.base, tau,
+                                    fallback, L);
   if (t == 0) {
     a.out_tok[(int64_t)b * (a.G + 1) + n] = j;
-    if (a.pr_z) a.pr_z[b] = (float)(RESID ? z : z * (double)d.st_inv);
+    if (a.pr_z) {
+      // Z of the drawn distribution in probability units: residual W / S_t;
+      // bonus 1; point-mass draft 1 - p_n(x_n) = W / (W + e_t(x_n))
+      double zp = 1.0;
+      if (resid && !o.zero) zp = o.z / o.st;
+      if (knock) zp = o.z / (o.z + e_of(dc.tx, d.k2, d.rt));
+      a.pr_z[b] = (float)zp;
+    }
   }
 }
 
@@ -1458,8 +1725,8 @@ __device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
   __syncthreads();
   if (!L.last) return;
   clear_pairs(a, b, nrows);
-  uint64_t* ws = a.wsum + (int64_t)b * 2 * a.NC;
-  for (int k = threadIdx.x; k < 2 * a.NC; k += kThreads) put64(&ws[k], 0);
+  uint64_t* ws = a.wsum + (int64_t)b * kWs * a.NC;
+  for (int k = threadIdx.x; k < kWs * a.NC; k += kThreads) put64(&ws[k], 0);
   if (threadIdx.x == 0) put_u(rc + kExit, 0u);
 }
 
@@ -1483,6 +1750,7 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   // every wait still ends.  With more workgroups than slots, a slowed tail
   // holds its slot and delays the next workgroup, so plain arbitration wins.
   if (PRIO) __builtin_amdgcn_s_setprio(3);
+  if (threadIdx.x == 0) L.bad = 0;  // read after stream_rows' barriers
   const int b = (int)(blockIdx.x / (unsigned)a.NC), c = (int)(blockIdx.x % (unsigned)a.NC);
   const int g = a.gam[b];
   if (g < 0 || g > a.G) {
@@ -1506,24 +1774,27 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
     // done
     if (c != 0) return;
     merge_group<false>(a, L, b, nrows);
-    decide<DT, MODE>(a, L, b, g, in, true);
+    if (L.bad)  // a slice's pairs never arrived (cannot happen in a correct launch)
+      write_sentinel(a, b);
+    else
+      decide<DT, MODE>(a, L, b, g, in, true);
     clear_pairs(a, b, nrows);
     return;
   }
 
   // sampling: wait for the group, merge, decide (every workgroup alike)
   merge_group<true>(a, L, b, nrows);
+  if (L.bad) {  // a slice's pairs never arrived (cannot happen in a correct launch)
+    write_sentinel(a, b);
+    row_exit(a, L, b, nrows);
+    return;
+  }
   decide<DT, MODE>(a, L, b, g, in, c == 0);
   const Decision dc = L.dec;
   if (PRIO) __builtin_amdgcn_s_setprio(1);
   if (!dc.dead) {
-    constexpr bool kRing = MODE == SPEC_MODE_SAMPLE;
-    if (dc.resid && MODE == SPEC_MODE_POINT)
-      draw<DT, R, false, true, false, FILT, AL, PRIO>(a, L, b, c, g, lo, len, nrows, dc, ring);
-    else if (dc.resid)
-      draw<DT, R, true, false, kRing, FILT, AL, PRIO>(a, L, b, c, g, lo, len, nrows, dc, ring);
-    else
-      draw<DT, R, false, false, kRing, FILT, AL, PRIO>(a, L, b, c, g, lo, len, nrows, dc, ring);
+    draw<DT, R, MODE == SPEC_MODE_POINT, MODE == SPEC_MODE_SAMPLE, FILT, AL, PRIO>(
+        a, L, b, c, g, lo, len, nrows, dc, ring);
   } else {
     row_exit(a, L, b, nrows);
   }
@@ -2150,7 +2421,8 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.wsum = (uint64_t*)(w + p.off_wsum);
   a.thr = filt ? (const float*)(w + p.off_thr) : nullptr;
   a.B = B, a.G = G, a.V = V, a.NC = p.NC, a.CL = p.CL, a.NR = p.NR;
-  a.k2 = draws ? (float)(1.4426950408889634 / (double)T) : 1.f;
+  a.k2d = draws ? 1.4426950408889634 / (double)T : 1.0;
+  a.k2 = (float)a.k2d;
   a.max_spin = 1u << 22;  // ~0.2 s of polling: far beyond any legitimate wait
   // phase priorities only when every workgroup is resident from the start
   // (four per CU is what the largest variants' registers allow)

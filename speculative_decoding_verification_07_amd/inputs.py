@@ -90,7 +90,9 @@ class Case:
 
     @property
     def T(self):
-        return self.config.T
+        """The temperature as the C ABI carries it (fp32): both the GPU and
+        the oracle are given this value."""
+        return float(np.float32(self.config.T))
 
 
 def rng(cfg: int, rnd: int, k: int) -> np.random.Generator:
@@ -260,6 +262,17 @@ def fresh_uniforms(case: Case, rnd: int) -> Case:
     """Same logits and draft tokens, fresh verify uniforms."""
     c = case.config
     return replace(case, uniforms=rng(c.cfg, rnd, 4).random((c.B, c.G + 1), dtype=np.float32))
+
+
+def stack_cases(cases: list) -> Case:
+    """Concatenate batches of one workload (same gamma_max, V, dtype, T and
+    mode) along the batch axis, so that many small calls can be checked in
+    one multi-row comparison."""
+    c0 = cases[0]
+    cat = lambda k: np.concatenate([getattr(c, k) for c in cases], axis=0)
+    cfg = replace(c0.config, B=sum(c.B for c in cases))
+    return Case(cfg, c0.mode, cat("target"), cat("draft"), cat("tokens"), cat("uniforms"),
+                cat("gamma"), cat("kv_len"), dict(c0.extra))
 
 
 def algorithmic_bytes(case: Case) -> int:

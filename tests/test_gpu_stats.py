@@ -22,7 +22,6 @@ from gpu_util import case_to_dev
 
 pytestmark = pytest.mark.gpu
 PASS_P = 1e-3
-FULL = os.environ.get("SPEC_FULL_PARITY") == "1"
 
 
 @pytest.fixture(scope="module")
@@ -80,7 +79,7 @@ def test_gpu_expected_tokens_per_pass_full_size(torch):
     base = inputs.make_case(5, rnd=0)
     alphas = base.extra["alpha_b"]
     dev = case_to_dev(base, torch)
-    rounds = 10_000 if FULL else 2_000
+    rounds = 10_000
     B = base.B
     ws = sv.Workspace(sv.workspace_bytes(B, base.G, base.V, sv.F32, sv.SAMPLE))
     nbuf = torch.empty((rounds, B), dtype=torch.int32, device="cuda")

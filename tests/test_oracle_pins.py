@@ -506,3 +506,61 @@ def test_acceptance_rate_is_one_minus_total_variation():
     p, q = np.array(g["p"]), np.array(g["q"])
     assert cf.acceptance_rate(p, q) == pytest.approx(g["acceptance_rate"], abs=1e-12)
     assert cf.acceptance_rate(p, q) == pytest.approx(1 - 0.5 * np.abs(p - q).sum(), abs=1e-12)
+
+
+# ---------------------------------------------------------------- the draw itself
+def test_draw_index_is_the_textbook_inverse_cdf():
+    """The oracle's draw over given weights equals numpy's searchsorted over
+    the cumulative sum (first j with u Z < C_j), including zero weights,
+    which are never chosen ("Speculative decoding", mhtirogla.ai, the
+    `sample` routine of "Code")."""
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        V = int(rng.integers(1, 300))
+        w = rng.random(V) * (rng.random(V) < 0.6)
+        if not w.any():
+            w[int(rng.integers(V))] = 1.0
+        u = float(rng.random())
+        j, z = oracle.draw_index(w, u)
+        assert z == pytest.approx(w.sum(), rel=1e-12)
+        assert j == _inverse_cdf(w, u), (trial, V, u)
+        assert w[j] > 0
+
+
+def test_draw_index_fallback_is_last_positive_weight():
+    """When no running sum exceeds u Z (here u = 1, one past the uniforms'
+    range) the draw returns the last index of positive weight -- not V-1,
+    which the page's `sample` would return even when it has weight 0."""
+    w = np.array([0.0, 0.3, 0.0, 0.7, 0.0, 0.0])
+    j, z = oracle.draw_index(w, 1.0)
+    assert j == 3 and z == pytest.approx(1.0)
+    # a single positive weight anywhere
+    for k in range(6):
+        e = np.zeros(6)
+        e[k] = 2.5
+        assert oracle.draw_index(e, 1.0)[0] == k
+        assert oracle.draw_index(e, 0.0)[0] == k
+
+
+def test_zero_residual_falls_back_to_p():
+    """Identical target and draft logits with the drafted token at a -inf
+    logit: p(x) = q(x) = 0, so u q(x) < p(x) fails and the walk rejects at
+    0, yet max(0, p - q) is 0 everywhere.  The oracle then draws from p_0
+    with the next uniform (the reading for a residual without mass) and
+    flags the row; the token is numpy's inverse CDF of softmax(t_0)."""
+    rng = np.random.default_rng(11)
+    B, G, V = 6, 3, 257
+    lt = rng.normal(0, 2, size=(B, G + 1, V)).astype(np.float32)
+    xs = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    for b in range(B):
+        lt[b, 0, xs[b, 0]] = -np.inf
+    ld = lt[:, :G].copy()
+    us = rng.random((B, G + 1), dtype=np.float32)
+    gam = np.full(B, G, np.int32)
+    r = oracle.verify(lt, ld, xs, us, gam, temperature=0.9)
+    p0 = softmax(lt[:, 0].astype(np.float64) / 0.9, axis=-1)
+    for b in range(B):
+        assert r.n_accepted[b] == 0 and r.zero_resid[b] == 1
+        assert r.tokens[b, 0] == _inverse_cdf(p0[b], us[b, 1])
+        assert np.all(r.tokens[b, 1:] == -1)
+        assert r.z[b] == pytest.approx(1.0, rel=1e-12)
