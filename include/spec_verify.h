@@ -120,6 +120,30 @@ int spec_verify(const void* target_logits, const void* draft_logits,
                 int32_t* out_n_accepted, int32_t* out_new_len, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* Largest workspace spec_verify_noalloc can use (8 MiB; spec_verify_workspace_bytes
+ * of the call must not exceed it).  At 1024 workgroups per call this covers,
+ * e.g., B = 256, gamma_max = 8, V = 151936 (about 0.9 MiB). */
+#define SPEC_NOALLOC_WORKSPACE_BYTES (8u << 20)
+
+/* spec_verify without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments (less the workspace), semantics and
+ * errors as spec_verify.  The workspace is a device array inside the library,
+ * SPEC_NOALLOC_WORKSPACE_BYTES per device, held until the process ends; the
+ * call allocates and frees nothing.  Each call first clears the part it uses
+ * (a fill kernel on `stream`), then runs spec_verify on it.  Every call on a
+ * device shares that device's array: calls that may overlap on one device
+ * (different streams, different host threads) race and give undefined
+ * results -- order them on one stream.  Returns SPEC_ERR_WORKSPACE when the
+ * call needs more than SPEC_NOALLOC_WORKSPACE_BYTES (nothing is launched),
+ * SPEC_ERR_HIP - e if the array's device address cannot be obtained. */
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
+                        int gamma_max, int V, int dtype, float temperature, int mode,
+                        int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_new_len,
+                        void* stream);
+
 /* spec_verify plus the intermediate values, for parity checks (same
  * arguments and semantics, slower).  Each probe pointer may be NULL:
  *   out_px, out_qx  fp32 [B, gamma_max]: p_i(x_i), q_i(x_i) for every

@@ -22,7 +22,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ARG, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = 0, -1, -2,
 GAMMA_MAX_LIMIT = 63
 
 EXPORTS = (
-    "spec_verify", "spec_verify_probe", "spec_verify_filtered", "spec_verify_filtered_probe",
+    "spec_verify", "spec_verify_noalloc", "spec_verify_probe", "spec_verify_filtered", "spec_verify_filtered_probe",
     "spec_filter_thresholds", "spec_verify_workspace_bytes",
     "spec_verify_workspace_reset", "spec_verify_plan", "spec_verify_tune",
     "spec_verify_diagnostics", "spec_verify_strerror", "spec_verify_version",
@@ -53,6 +53,8 @@ def load():
     verify_args = [P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, P, P, P, P, sz, P]
     lib.spec_verify.argtypes = verify_args
     lib.spec_verify.restype = i32
+    lib.spec_verify_noalloc.argtypes = verify_args[:15] + [P]
+    lib.spec_verify_noalloc.restype = i32
     lib.spec_verify_probe.argtypes = verify_args + [P, P, P, P, P]
     lib.spec_verify_probe.restype = i32
     filtered_args = verify_args[:12] + [i32, f32] + verify_args[12:]
@@ -269,6 +271,27 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, k
     if check:
         _check_diagnostics(workspace, stream)
     return tok, nacc, nlen, pr
+
+
+NOALLOC_WORKSPACE_BYTES = 8 << 20
+
+
+def verify_noalloc(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row,
+                   kv_len_in=None, *, temperature: float = 1.0, mode: int = SAMPLE, out,
+                   stream=None):
+    """spec_verify_noalloc: the verify step with the library's own static
+    workspace (no allocation in the call; `out` = preallocated (tokens,
+    n_accepted, new_len) is required).  Calls that may overlap on one device
+    race for that workspace."""
+    B, G, V = _shape_check(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row,
+                           kv_len_in, mode)
+    tok, nacc, nlen = out
+    _check(load().spec_verify_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
+        _ptr(gamma_per_row), _ptr(kv_len_in), B, G, V, _dtype_code(target_logits),
+        float(temperature), int(mode), _ptr(tok), _ptr(nacc), _ptr(nlen),
+        _stream_handle(stream)), "spec_verify_noalloc")
+    return tok, nacc, nlen
 
 
 class WaitGaveUp(RuntimeError):

@@ -2459,6 +2459,33 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   return hip_status(hipGetLastError());
 }
 
+// ------------------------------------------------------------------ static workspace
+// The workspace of spec_verify_noalloc: one array per device, loaded with the
+// library's code object (zero-initialised) and held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): it uses the address hipGetSymbolAddress
+// returns for the current device, asked once per device.
+__device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_WORKSPACE_BYTES];
+
+// Device address of this device's copy of `scratch` (nullptr on error, with
+// the HIP error in *err).
+void* scratch_ptr(int dev, hipError_t* err) {
+  static std::atomic<void*> cached[64];
+  *err = hipSuccess;
+  if (dev >= 0 && dev < 64) {
+    void* p = cached[dev].load(std::memory_order_acquire);
+    if (p) return p;
+  }
+  void* p = nullptr;
+  *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || !p) {
+    if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  if (dev >= 0 && dev < 64) cached[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -2494,6 +2521,37 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
              gamma_max, V, dtype, temperature, mode, 0, 1.f, out_tokens, out_n_accepted,
              out_new_len, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr,
              nullptr);
+}
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
+                        int gamma_max, int V, int dtype, float temperature, int mode,
+                        int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_new_len,
+                        void* stream) {
+  Plan p;
+  const int st = make_plan(B, gamma_max, V, dtype, mode, &p);
+  if (st != SPEC_OK) return st;
+  if (p.bytes > (size_t)SPEC_NOALLOC_WORKSPACE_BYTES) return SPEC_ERR_WORKSPACE;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  void* ws = scratch_ptr(dev, &e);
+  if (!ws) return hip_status(e);
+  // the previous call on this device left the region zero unless it gave up
+  // waiting; clear it anyway (a fill kernel: no memset node in a graph)
+  const size_t n16 = p.bytes / 16;
+  size_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, (uint4*)ws, n16, (unsigned char*)ws + n16 * 16,
+                     (int)(p.bytes % 16));
+  const int hs = hip_status(hipGetLastError());
+  if (hs != SPEC_OK) return hs;
+  return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
+             gamma_max, V, dtype, temperature, mode, 0, 1.f, out_tokens, out_n_accepted,
+             out_new_len, ws, p.bytes, stream, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
 int spec_verify_probe(const void* target_logits, const void* draft_logits,
