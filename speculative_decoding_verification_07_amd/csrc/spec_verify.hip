@@ -415,7 +415,17 @@ __device__ __forceinline__ int id_i(int x) { return x; }
 __device__ __forceinline__ float add_f(float x, float y) { return x + y; }
 __device__ __forceinline__ int min_i(int x, int y) { return x < y ? x : y; }
 __device__ __forceinline__ float wave_sum(float v) SPEC_WAVE_REDUCE(float, as_i, as_f, add_f, 0.f)
-__device__ __forceinline__ float wave_max(float v) SPEC_WAVE_REDUCE(float, as_i, as_f, fmaxf, NEG_INF)
+__device__ __forceinline__ int max_i(int x, int y) { return x > y ? x : y; }
+__device__ __forceinline__ int wave_max_i(int v) SPEC_WAVE_REDUCE(int, id_i, id_i, max_i, (int)0x80000000)
+// Floats ordered as signed integers: the bits, with the magnitude bits
+// flipped when negative (-inf lowest, -0 just below +0).  A wave max over
+// these keys is one integer max per step (no NaN canonicalisation).
+__device__ __forceinline__ int fkey_i(float f) {
+  const int i = __float_as_int(f);
+  return i ^ ((i >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float fkey_f(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
+__device__ __forceinline__ float wave_max(float v) { return fkey_f(wave_max_i(fkey_i(v))); }
 __device__ __forceinline__ int wave_min(int v) SPEC_WAVE_REDUCE(int, id_i, id_i, min_i, 0x7fffffff)
 
 // (m, S) pairs of the lanes merged over the wave (result in every lane): the
@@ -787,11 +797,12 @@ __device__ __forceinline__ int probe_slot(const Args& a, int g, int r) {
 // instruction-level parallelism, then the wave sum.
 // FILT: entries below tau are cut (they weigh 0; the raw maximum, which a
 // filter always keeps, is unchanged).
-template <int DT, int R, bool FILT>
+template <int DT, int R, bool AL, bool FILT>
 __device__ __forceinline__ void wave_slice_ms(const Slice<DT, R>& s, const Geom& g, float k2,
                                               float tau, float& m, float& S) {
   using E = Elt<DT>;
-  float mx = fmaxf(s.hd, s.tl);
+  // (aligned rows have no head or tail element)
+  float mx = AL ? NEG_INF : fmaxf(s.hd, s.tl);
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     float f[E::kVec];
@@ -804,8 +815,10 @@ __device__ __forceinline__ void wave_slice_ms(const Slice<DT, R>& s, const Geom&
   if (mx != NEG_INF) {  // uniform across the wave
     const float Rf = ref_of(mx, k2);
     auto cut = [&](float x) { return FILT && !(x >= tau) ? NEG_INF : x; };
-    acc[0] = ex2(fmaf(cut(s.hd), k2, -Rf));
-    acc[1] = ex2(fmaf(cut(s.tl), k2, -Rf));
+    if (!AL) {
+      acc[0] = ex2(fmaf(cut(s.hd), k2, -Rf));
+      acc[1] = ex2(fmaf(cut(s.tl), k2, -Rf));
+    }
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       float f[E::kVec];
@@ -893,7 +906,7 @@ __device__ __forceinline__ void stream_rows(const Args& a, Lds& L, int b, int g,
       if (kSample) {
         float m, sm;
         const float tau = FILT ? L.tau[stream_row<MODE>(r < nrows ? r : nrows - 1, g)] : NEG_INF;
-        wave_slice_ms<DT, R, FILT>(buf[j], geo[j], a.k2, tau, m, sm);
+        wave_slice_ms<DT, R, AL, FILT>(buf[j], geo[j], a.k2, tau, m, sm);
         if (lane == 0 && r < nrows) {
           const int rr = stream_row<MODE>(r, g);
           L.sm.wm[rr][w] = m, L.sm.ws[rr][w] = sm;
@@ -1740,15 +1753,18 @@ template <int DT, int MODE, int R, bool AL, bool FILT, bool PRIO>
 __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a) {
   constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // a drawn token (sample, point)
   __shared__ Lds L;
-  // When the whole grid is resident (PRIO), the phases run at falling
-  // wave priority (3 streaming, 2 merge and decision, 1 draw weights, 0 the
-  // slice-sum wait and the owner's search).  A CU's four workgroups are at
+  // When the whole grid is resident (PRIO), the phases run at set wave
+  // priorities: 3 for streaming and the wait for the group's pairs (a poll
+  // that loses issue to other workgroups' streaming waits whole memory round
+  // trips longer), 2 for the merge and decision, 1 for the draw weights (2
+  // in the youngest quarter of the grid, whose rows finish last), 2 for the
+  // slice-sum wait and the owner's search.  A CU's four workgroups are at
   // different phases, and issue goes to the oldest wave of the highest
   // priority: this way a workgroup still streaming its rows does not lose
-  // issue slots to another's latency-bound tail.  Priority orders issue
-  // only; a low-priority wave still issues whenever the others wait, so
-  // every wait still ends.  With more workgroups than slots, a slowed tail
-  // holds its slot and delays the next workgroup, so plain arbitration wins.
+  // issue slots to another's draw.  Priority orders issue only; a
+  // low-priority wave still issues whenever the others wait, so every wait
+  // still ends.  With more workgroups than slots, a slowed tail holds its
+  // slot and delays the next workgroup, so plain arbitration wins.
   if (PRIO) __builtin_amdgcn_s_setprio(3);
   if (threadIdx.x == 0) L.bad = 0;  // read after stream_rows' barriers
   const int b = (int)(blockIdx.x / (unsigned)a.NC), c = (int)(blockIdx.x % (unsigned)a.NC);
@@ -1765,7 +1781,6 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   Ring<DT, R> ring;
   stream_rows<DT, MODE, R, AL, FILT>(a, L, b, g, nrows, lo, len, ring);
   publish_pairs<kSample>(a, L, b, c, nrows);
-  if (PRIO) __builtin_amdgcn_s_setprio(2);
   if (kSample) gather_logits<DT, MODE, FILT>(a, b, g, in);  // in flight during the wait
 
   if (!kSample) {
@@ -1782,8 +1797,11 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
     return;
   }
 
-  // sampling: wait for the group, merge, decide (every workgroup alike)
+  // sampling: wait for the group, merge, decide (every workgroup alike);
+  // the polls keep the streaming priority (a poll behind other workgroups'
+  // streaming waits whole memory round trips longer), the merge does not
   merge_group<true>(a, L, b, nrows);
+  if (PRIO) __builtin_amdgcn_s_setprio(2);
   if (L.bad) {  // a slice's pairs never arrived (cannot happen in a correct launch)
     write_sentinel(a, b);
     row_exit(a, L, b, nrows);
@@ -1791,7 +1809,15 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   }
   decide<DT, MODE>(a, L, b, g, in, c == 0);
   const Decision dc = L.dec;
-  if (PRIO) __builtin_amdgcn_s_setprio(1);
+  // draw weights below the streaming; the youngest quarter of the grid
+  // (served last by the memory system, so its rows finish last) above the
+  // other quarters' draws
+  if (PRIO) {
+    if (blockIdx.x * 4 >= 3 * gridDim.x)
+      __builtin_amdgcn_s_setprio(2);
+    else
+      __builtin_amdgcn_s_setprio(1);
+  }
   if (!dc.dead) {
     draw<DT, R, MODE == SPEC_MODE_POINT, MODE == SPEC_MODE_SAMPLE, FILT, AL, PRIO>(
         a, L, b, c, g, lo, len, nrows, dc, ring);
