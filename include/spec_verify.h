@@ -154,14 +154,21 @@ int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
  *                   rows 0..gamma_max, then draft rows 0..gamma_max-1) the
  *                   largest raw logit and S = sum_j exp((l_j - max) / T)
  *                   (GREEDY: out_m only, out_s holds the argmax as float;
- *                   GREEDY and POINT leave the draft slots untouched) */
+ *                   GREEDY and POINT leave the draft slots untouched)
+ *   out_f_lo,       fp32 [B]: the CDF bracket of the drawn token j, i.e. the
+ *   out_f_hi        normalised cumulative weight of the tokens before j and
+ *                   through j (u lies in [f_lo, f_hi) unless the fallback
+ *                   rule chose j); both NULL or both given; SAMPLE and POINT
+ *                   only, untouched for rows with a data error.
+ * The CDF values are formed in double precision and rounded to fp32 here. */
 int spec_verify_probe(const void* target_logits, const void* draft_logits,
                       const int32_t* draft_tokens, const float* uniforms,
                       const int32_t* gamma_per_row, const int32_t* kv_len_in, int B,
                       int gamma_max, int V, int dtype, float temperature, int mode,
                       int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_new_len,
                       void* workspace, size_t workspace_bytes, void* stream, float* out_px,
-                      float* out_qx, float* out_z, float* out_m, float* out_s);
+                      float* out_qx, float* out_z, float* out_m, float* out_s, float* out_f_lo,
+                      float* out_f_hi);
 
 /* spec_verify with the same top-k / top-p filtering applied to p and q
  * before the walk (sources: mhtirogla.ai "Implementation notes";
@@ -202,7 +209,8 @@ int spec_verify_filtered_probe(const void* target_logits, const void* draft_logi
                                int top_k, float top_p, int32_t* out_tokens,
                                int32_t* out_n_accepted, int32_t* out_new_len, void* workspace,
                                size_t workspace_bytes, void* stream, float* out_px, float* out_qx,
-                               float* out_z, float* out_m, float* out_s);
+                               float* out_z, float* out_m, float* out_s, float* out_f_lo,
+                               float* out_f_hi);
 
 /* The thresholds alone: out_thr fp32 [B, 2*gamma_max+1] (device; target rows
  * 0..gamma_max, then draft rows 0..gamma_max-1), the value tau of each

@@ -49,7 +49,8 @@ def _load():
         i32 = ctypes.c_int
         D = ctypes.c_double
         lib.oracle_verify.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, D,
-                                      i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i32, D, P]
+                                      i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i32, D, P,
+                                      P, P]
         lib.oracle_verify.restype = i32
         lib.oracle_draw_cdf.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, D,
                                         i32, i32, P, i32, D]
@@ -91,6 +92,8 @@ class OracleResult:
     draw_pos: np.ndarray    # int32 [B]; position drawn from, -1 if none
     zero_resid: np.ndarray  # int32 [B]; 1 where the residual mass was exactly 0
     fmargin: np.ndarray     # float64 [B]; smallest top-p margin (relative mass) of the rows
+    flo: np.ndarray         # float64 [B]; normalised CDF just below the drawn token (NaN: none)
+    fhi: np.ndarray         # float64 [B]; normalised CDF at the drawn token
 
 
 def _c(a, dt):
@@ -136,14 +139,17 @@ def verify(target, draft, tokens, uniforms, gamma, kv_len=None, *, temperature=1
     pos = np.empty(B, np.int32)
     zr = np.empty(B, np.int32)
     fm = np.empty(B, np.float64)
+    flo = np.empty(B, np.float64)
+    fhi = np.empty(B, np.float64)
     rc = lib.oracle_verify(_ptr(target), _ptr(draft), dt, _ptr(tokens), _ptr(uniforms),
                            _ptr(gamma), _ptr(kv_len), B, G, V, float(temperature), int(mode),
                            int(fault), int(threads), _ptr(out_tokens), _ptr(out_n),
                            _ptr(out_len), _ptr(px), _ptr(qx), _ptr(z), _ptr(m), _ptr(s),
-                           _ptr(pos), _ptr(zr), int(top_k), float(top_p), _ptr(fm))
+                           _ptr(pos), _ptr(zr), int(top_k), float(top_p), _ptr(fm),
+                           _ptr(flo), _ptr(fhi))
     if rc != 0:
         raise ValueError(f"oracle refused its arguments (code {rc})")
-    return OracleResult(out_tokens, out_n, out_len, px, qx, z, m, s, pos, zr, fm)
+    return OracleResult(out_tokens, out_n, out_len, px, qx, z, m, s, pos, zr, fm, flo, fhi)
 
 
 def draw_cdf(target, draft, tokens, uniforms, gamma, row, *, temperature=1.0, mode=SAMPLE,

@@ -28,6 +28,7 @@ import oracle
 
 TOL = 1e-5
 TINY, TINY_ABS = 1e-30, 1e-35
+CDF_TOL = 2e-7  # the GPU's bracket is fp64, rounded to fp32 (half an ulp below 1: 3e-8)
 MISMATCH_RATE = 1e-4
 
 
@@ -44,6 +45,7 @@ class Report:
     prob_errors: list = field(default_factory=list)     # (row, pos, what, gpu, oracle)
     max_rel_p: float = 0.0
     max_rel_stats: float = 0.0
+    max_cdf_err: float = 0.0
 
     @property
     def ok(self) -> bool:
@@ -58,12 +60,14 @@ class Report:
         self.prob_errors += other.prob_errors
         self.max_rel_p = max(self.max_rel_p, other.max_rel_p)
         self.max_rel_stats = max(self.max_rel_stats, other.max_rel_stats)
+        self.max_cdf_err = max(self.max_cdf_err, other.max_cdf_err)
 
     def summary(self) -> str:
         return (f"rows={self.rows} mismatched={len(self.mismatched)} "
                 f"(allowed {allowed_mismatches(self.rows)}) "
                 f"attributed={len(self.attributed)} prob_errors={len(self.prob_errors)} "
-                f"max_rel_p={self.max_rel_p:.2e} max_rel_stats={self.max_rel_stats:.2e}")
+                f"max_rel_p={self.max_rel_p:.2e} max_rel_stats={self.max_rel_stats:.2e} "
+                f"max_cdf_err={self.max_cdf_err:.2e}")
 
 
 def _close(gpu, ref):
@@ -138,6 +142,21 @@ def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) ->
             zr, zg = ref.z[b], probe["z"][b]
             if not (abs(zg - zr) <= TOL * abs(zr) + 1e-6):
                 rep.prob_errors.append((row_offset + b, -1, "Z", float(zg), float(zr)))
+            # the drawn token's CDF bracket, where both sides drew the same
+            # token: the GPU's fp64 CDF (rounded to fp32 on output) against
+            # the oracle's, and the GPU's own bracket holds its uniform
+            if "flo" in probe and np.array_equal(tokens[b], ref.tokens[b]):
+                for what, gv, ov in (("F_lo", probe["flo"][b], ref.flo[b]),
+                                     ("F_hi", probe["fhi"][b], ref.fhi[b])):
+                    err = abs(float(gv) - float(ov))
+                    rep.max_cdf_err = max(rep.max_cdf_err, err)
+                    if not err <= CDF_TOL:
+                        rep.prob_errors.append((row_offset + b, -1, what, float(gv), float(ov)))
+                n = int(ref.n_accepted[b])
+                us = float(case.uniforms[b, n + 1 if n < g[b] else g[b]])
+                if not (probe["flo"][b] - CDF_TOL <= us <= probe["fhi"][b] + CDF_TOL):
+                    rep.prob_errors.append((row_offset + b, -1, "u outside [F_lo, F_hi]",
+                                            float(probe["flo"][b]), us))
 
     for b in range(case.B):
         same = (n_acc[b] == ref.n_accepted[b] and new_len[b] == ref.new_len[b]

@@ -223,23 +223,30 @@ static int argmax_row(const oracle_ctx* c, size_t off) {
 
 /* Inverse-CDF draw over non-negative weights w[0..V): tau = u * Z, the
  * smallest j with tau < C_j; fallback: the last index with w > 0.
- * Writes Z.  cdf_out (optional) receives C_j / Z. */
+ * Writes Z.  cdf_out (optional) receives C_j / Z; flo_out and fhi_out
+ * (optional) the drawn index's bracket C_{j-1} / Z and C_j / Z. */
 static int draw_index(const oracle_ctx* c, const double* w, double u,
-                      double* z_out, double* cdf_out) {
+                      double* z_out, double* cdf_out, double* flo_out, double* fhi_out) {
   const int V = c->V;
   double z = 0.0;
   for (int j = 0; j < V; ++j) z += w[j];
   if (z_out) *z_out = z;
   double tau = (c->fault == OR_FAULT_UNSCALED_TAU) ? u : u * z;
   int pick = -1, last_pos = -1;
-  double acc = 0.0;
+  double acc = 0.0, pick_lo = 0.0, pick_hi = 0.0, last_lo = 0.0, last_hi = 0.0;
   for (int j = 0; j < V; ++j) {
+    const double before = acc;
     acc += w[j];
     if (cdf_out) cdf_out[j] = acc / z;
-    if (w[j] > 0.0) last_pos = j;
-    if (pick < 0 && tau < acc) pick = j;
+    if (w[j] > 0.0) last_pos = j, last_lo = before, last_hi = acc;
+    if (pick < 0 && tau < acc) pick = j, pick_lo = before, pick_hi = acc;
   }
-  if (pick < 0) pick = (last_pos >= 0) ? last_pos : V - 1;
+  if (pick < 0) {
+    pick = (last_pos >= 0) ? last_pos : V - 1;
+    pick_lo = last_lo, pick_hi = last_hi;
+  }
+  if (flo_out) *flo_out = pick_lo / z;
+  if (fhi_out) *fhi_out = pick_hi / z;
   return pick;
 }
 
@@ -253,6 +260,8 @@ typedef struct {
   int32_t* zero_resid; /* [1] 1 when the residual mass was exactly 0         */
   double* cdf;      /* [V] normalised CDF of the drawn distribution, or NULL */
   double* fmargin;  /* [1] smallest top-p margin over the rows the walk used */
+  double* flo;      /* [1] normalised CDF just below the drawn token          */
+  double* fhi;      /* [1] normalised CDF at the drawn token                  */
 } row_diag;
 
 static void write_sentinel(const oracle_ctx* c, int b, int32_t* tok, int32_t* n_out,
@@ -394,7 +403,7 @@ static void verify_row(const oracle_ctx* c, int b, int32_t* out_tokens, int32_t*
   } else {
     memcpy(w, pn, sizeof(double) * (size_t)V);
   }
-  int j = draw_index(c, w, ustar, d->z, d->cdf);
+  int j = draw_index(c, w, ustar, d->z, d->cdf, d->flo, d->fhi);
   if (d->draw_pos) *d->draw_pos = n;
 
   for (int i = 0; i < n; ++i) tok[i] = x[i];
@@ -414,7 +423,7 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
                   int32_t* out_tokens, int32_t* out_n, int32_t* out_len, double* out_px,
                   double* out_qx, double* out_z, double* out_m, double* out_s,
                   int32_t* out_draw_pos, int32_t* out_zero_resid, int top_k, double top_p,
-                  double* out_fmargin) {
+                  double* out_fmargin, double* out_flo, double* out_fhi) {
   if (!target || !tokens || !gamma || !out_tokens || !out_n || !out_len) return -1;
   if (B < 0 || G < 0 || V <= 0) return -2;
   if (dtype != OR_F32 && dtype != OR_BF16) return -3;
@@ -439,6 +448,10 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
     for (size_t k = 0; k < (size_t)B * nr; ++k) out_s[k] = NAN;
   if (out_fmargin)
     for (int b = 0; b < B; ++b) out_fmargin[b] = INFINITY;
+  for (int b = 0; b < B; ++b) {
+    if (out_flo) out_flo[b] = NAN;
+    if (out_fhi) out_fhi[b] = NAN;
+  }
 #ifdef _OPENMP
   if (threads > 0) omp_set_num_threads(threads);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -452,7 +465,9 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
                   out_draw_pos ? out_draw_pos + b : NULL,
                   out_zero_resid ? out_zero_resid + b : NULL,
                   NULL,
-                  out_fmargin ? out_fmargin + b : NULL};
+                  out_fmargin ? out_fmargin + b : NULL,
+                  out_flo ? out_flo + b : NULL,
+                  out_fhi ? out_fhi + b : NULL};
     verify_row(&c, b, out_tokens, out_n, out_len, &d);
   }
   (void)threads;
@@ -478,7 +493,7 @@ int oracle_draw_cdf(const void* target, const void* draft, int dtype, const int3
   int32_t* nn = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
   int32_t* ln = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
   int32_t pos = -1;
-  row_diag d = {NULL, NULL, NULL, NULL, NULL, &pos, NULL, cdf, NULL};
+  row_diag d = {NULL, NULL, NULL, NULL, NULL, &pos, NULL, cdf, NULL, NULL, NULL};
   verify_row(&c, b, tok, nn, ln, &d);
   free(tok), free(nn), free(ln);
   return pos;
@@ -491,7 +506,7 @@ int oracle_draw_index(const double* w, int V, double u, double* z_out) {
   if (!w || V <= 0) return -1;
   oracle_ctx c = {NULL, NULL, OR_F32, NULL, NULL, NULL, NULL, 1, 0, V, 1.0, OR_SAMPLE,
                   OR_FAULT_NONE, 0, 1.0};
-  return draw_index(&c, w, u, z_out, NULL);
+  return draw_index(&c, w, u, z_out, NULL, NULL, NULL);
 }
 
 /* The filtered distribution of one stored logit row (what a drafter that

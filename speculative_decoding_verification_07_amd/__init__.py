@@ -55,12 +55,12 @@ def load():
     lib.spec_verify.restype = i32
     lib.spec_verify_noalloc.argtypes = verify_args[:15] + [P]
     lib.spec_verify_noalloc.restype = i32
-    lib.spec_verify_probe.argtypes = verify_args + [P, P, P, P, P]
+    lib.spec_verify_probe.argtypes = verify_args + [P, P, P, P, P, P, P]
     lib.spec_verify_probe.restype = i32
     filtered_args = verify_args[:12] + [i32, f32] + verify_args[12:]
     lib.spec_verify_filtered.argtypes = filtered_args
     lib.spec_verify_filtered.restype = i32
-    lib.spec_verify_filtered_probe.argtypes = filtered_args + [P, P, P, P, P]
+    lib.spec_verify_filtered_probe.argtypes = filtered_args + [P, P, P, P, P, P, P]
     lib.spec_verify_filtered_probe.restype = i32
     lib.spec_filter_thresholds.argtypes = [P, P, P, i32, i32, i32, i32, f32, i32, i32, f32, P, P]
     lib.spec_filter_thresholds.restype = i32
@@ -221,7 +221,7 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, k
     torch device tensors.
 
     Returns (tokens [B, G+1] int32, n_accepted [B] int32, new_len [B] int32),
-    plus a dict of probe tensors (px, qx, z, m, s) when probe=True.  `out`
+    plus a dict of probe tensors (px, qx, z, m, s, flo, fhi) when probe=True.  `out`
     may pass preallocated (tokens, n_accepted, new_len).  The call is
     asynchronous on `stream` (default: torch's current stream).  Temporaries
     are allocated on that stream.  check=True waits for the call and reads
@@ -264,10 +264,12 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, k
             "z": torch.full((B,), nan, dtype=torch.float32, device=dev),
             "m": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
             "s": torch.full((B, 2 * G + 1), nan, dtype=torch.float32, device=dev),
+            "flo": torch.full((B,), nan, dtype=torch.float32, device=dev),
+            "fhi": torch.full((B,), nan, dtype=torch.float32, device=dev),
         }
     fn = lib.spec_verify_filtered_probe if filt else lib.spec_verify_probe
     _check(fn(*args, _ptr(pr["px"]), _ptr(pr["qx"]), _ptr(pr["z"]), _ptr(pr["m"]),
-              _ptr(pr["s"])), "spec_verify_probe")
+              _ptr(pr["s"]), _ptr(pr["flo"]), _ptr(pr["fhi"])), "spec_verify_probe")
     if check:
         _check_diagnostics(workspace, stream)
     return tok, nacc, nlen, pr

@@ -141,6 +141,8 @@ struct Args {
   float* pr_z;
   float* pr_m;
   float* pr_s;
+  float* pr_flo;
+  float* pr_fhi;
   unsigned* hdr;
   unsigned* ctr;   // [B][kRowWords]
   uint64_t* part;  // [B][NC][NR] pairs of each slice: (m, S) or (max, argmax + 1)
@@ -694,6 +696,7 @@ struct Lds {
   float S[kMaxRows];           //   or draft i (r = g + 1 + i); greedy: argmax bits
   double red_d[8 * kWaves];
   uint4 vt, vd;                // the owner thread's vector, for the element search
+  double brk[2];               // the drawn token's CDF bracket (sums before / through it)
   unsigned long long mask[kWaves];
   Decision dec;
   Owner own;
@@ -1483,8 +1486,17 @@ __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const S
     th = block_last(vs > 0.0, L);
   }
   if (th < 0) th = 0;
-  if (seg == 0) return lo + th;              // a head element
-  if (seg == NS - 1) return lo + g.jb + th;  // a tail element
+  if (seg == 0 || seg == NS - 1) {
+    // a head or tail element: the thread's one element of the segment
+    if (t == th) {
+      L.pick = seg == 0 ? lo + th : lo + g.jb + th;
+      L.brk[0] = carry + excl, L.brk[1] = carry + incl;
+    }
+    __syncthreads();
+    const int j = L.pick;
+    __syncthreads();
+    return j;
+  }
   // thread th's vector of round seg - 1, handed to wave 0 through LDS
   if (t == th) {
     L.vt = vsel(st, seg - 1, g);
@@ -1517,7 +1529,10 @@ __device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const S
     const unsigned long long hit = __ballot(wl > 0.0 && !fb && tau < before + run);
     const unsigned long long pos = __ballot(wl > 0.0);
     const int e = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-    if (t == 0) L.pick = lo + g.head + ((seg - 1) * kThreads + th) * E::kVec + e;
+    if (t == e) {
+      L.pick = lo + g.head + ((seg - 1) * kThreads + th) * E::kVec + e;
+      L.brk[0] = before + ex, L.brk[1] = before + run;
+    }
   }
   __syncthreads();
   const int j = L.pick;
@@ -1674,6 +1689,7 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
       atomicOr(&a.hdr[1], kDiagZeroResid);
       a.out_tok[(int64_t)b * (a.G + 1) + n] = dc.xn;
       if (a.pr_z) a.pr_z[b] = 1.f;
+      if (a.pr_flo) a.pr_flo[b] = 0.f, a.pr_fhi[b] = 1.f;
     }
     row_exit(a, L, b, nrows);
     return;
@@ -1710,6 +1726,10 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
       if (resid && !o.zero) zp = o.z / o.st;
       if (knock) zp = o.z / (o.z + e_of(dc.tx, d.k2, d.rt));
       a.pr_z[b] = (float)zp;
+    }
+    if (a.pr_flo) {  // the normalised CDF just below and at the drawn token
+      a.pr_flo[b] = (float)(L.brk[0] / o.z);
+      a.pr_fhi[b] = (float)(L.brk[1] / o.z);
     }
   }
 }
@@ -2415,7 +2435,8 @@ FArgs filter_args(const void* tgt, const void* dft, const int32_t* gam, float* t
 int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const int32_t* gam,
         const int32_t* kv, int B, int G, int V, int dtype, float T, int mode, int top_k,
         float top_p, int32_t* out_tok, int32_t* out_n, int32_t* out_len, void* ws,
-        size_t ws_bytes, void* stream, float* px, float* qx, float* pz, float* pm, float* ps) {
+        size_t ws_bytes, void* stream, float* px, float* qx, float* pz, float* pm, float* ps,
+        float* pflo, float* pfhi) {
   Plan p;
   int st = make_plan(B, G, V, dtype, mode, &p);
   if (st != SPEC_OK) return st;
@@ -2431,7 +2452,8 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   const size_t e = dtype == SPEC_DTYPE_F32 ? 4 : 2;
   if (!sample) dft = nullptr;  // only sampling reads draft logits
   if (!aligned(tgt, e) || (dft && !aligned(dft, e))) return SPEC_ERR_ALIGN;
-  const void* four[] = {tok, uni, gam, kv, out_tok, out_n, out_len, px, qx, pz, pm, ps};
+  if ((pflo == nullptr) != (pfhi == nullptr)) return SPEC_ERR_NULL;
+  const void* four[] = {tok, uni, gam, kv, out_tok, out_n, out_len, px, qx, pz, pm, ps, pflo, pfhi};
   for (const void* q : four)
     if (q && !aligned(q, 4)) return SPEC_ERR_ALIGN;
   if (!aligned(ws, 256)) return SPEC_ERR_ALIGN;
@@ -2440,6 +2462,7 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.tgt = tgt, a.dft = dft ? dft : tgt, a.tok = tok, a.uni = uni, a.gam = gam, a.kv = kv;
   a.out_tok = out_tok, a.out_n = out_n, a.out_len = out_len;
   a.pr_px = px, a.pr_qx = qx, a.pr_z = pz, a.pr_m = pm, a.pr_s = ps;
+  a.pr_flo = pflo, a.pr_fhi = pfhi;
   char* w = (char*)ws;
   a.hdr = (unsigned*)w;
   a.ctr = (unsigned*)(w + p.off_ctr);
@@ -2546,7 +2569,7 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
              gamma_max, V, dtype, temperature, mode, 0, 1.f, out_tokens, out_n_accepted,
              out_new_len, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr,
-             nullptr);
+             nullptr, nullptr, nullptr);
 }
 
 int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
@@ -2577,7 +2600,8 @@ int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
   if (hs != SPEC_OK) return hs;
   return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
              gamma_max, V, dtype, temperature, mode, 0, 1.f, out_tokens, out_n_accepted,
-             out_new_len, ws, p.bytes, stream, nullptr, nullptr, nullptr, nullptr, nullptr);
+             out_new_len, ws, p.bytes, stream, nullptr, nullptr, nullptr, nullptr, nullptr,
+             nullptr, nullptr);
 }
 
 int spec_verify_probe(const void* target_logits, const void* draft_logits,
@@ -2586,11 +2610,13 @@ int spec_verify_probe(const void* target_logits, const void* draft_logits,
                       int gamma_max, int V, int dtype, float temperature, int mode,
                       int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_new_len,
                       void* workspace, size_t workspace_bytes, void* stream, float* out_px,
-                      float* out_qx, float* out_z, float* out_m, float* out_s) {
+                      float* out_qx, float* out_z, float* out_m, float* out_s, float* out_f_lo,
+                      float* out_f_hi) {
   if ((out_px == nullptr) != (out_qx == nullptr)) return SPEC_ERR_NULL;
   return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
              gamma_max, V, dtype, temperature, mode, 0, 1.f, out_tokens, out_n_accepted,
-             out_new_len, workspace, workspace_bytes, stream, out_px, out_qx, out_z, out_m, out_s);
+             out_new_len, workspace, workspace_bytes, stream, out_px, out_qx, out_z, out_m, out_s,
+             out_f_lo, out_f_hi);
 }
 
 int spec_verify_filtered(const void* target_logits, const void* draft_logits,
@@ -2603,7 +2629,7 @@ int spec_verify_filtered(const void* target_logits, const void* draft_logits,
   return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
              gamma_max, V, dtype, temperature, mode, top_k, top_p, out_tokens, out_n_accepted,
              out_new_len, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr,
-             nullptr);
+             nullptr, nullptr, nullptr);
 }
 
 int spec_verify_filtered_probe(const void* target_logits, const void* draft_logits,
@@ -2613,11 +2639,13 @@ int spec_verify_filtered_probe(const void* target_logits, const void* draft_logi
                                int top_k, float top_p, int32_t* out_tokens,
                                int32_t* out_n_accepted, int32_t* out_new_len, void* workspace,
                                size_t workspace_bytes, void* stream, float* out_px, float* out_qx,
-                               float* out_z, float* out_m, float* out_s) {
+                               float* out_z, float* out_m, float* out_s, float* out_f_lo,
+                               float* out_f_hi) {
   if ((out_px == nullptr) != (out_qx == nullptr)) return SPEC_ERR_NULL;
   return run(target_logits, draft_logits, draft_tokens, uniforms, gamma_per_row, kv_len_in, B,
              gamma_max, V, dtype, temperature, mode, top_k, top_p, out_tokens, out_n_accepted,
-             out_new_len, workspace, workspace_bytes, stream, out_px, out_qx, out_z, out_m, out_s);
+             out_new_len, workspace, workspace_bytes, stream, out_px, out_qx, out_z, out_m, out_s,
+             out_f_lo, out_f_hi);
 }
 
 int spec_filter_thresholds(const void* target_logits, const void* draft_logits,

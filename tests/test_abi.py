@@ -119,7 +119,11 @@ def test_null_tolerated_where_documented(lib):
 
 def test_probe_pointer_pairing(lib):
     r = lib.spec_verify_probe(A, A, A, A, A, None, 4, 4, 1000, sv.BF16, 1.0, sv.SAMPLE, A, A, A,
-                              A2, 1 << 30, None, A, None, None, None, None)
+                              A2, 1 << 30, None, A, None, None, None, None, None, None)
+    assert r == sv.ERR_NULL
+    # the CDF bracket outputs come in pairs too
+    r = lib.spec_verify_probe(A, A, A, A, A, None, 4, 4, 1000, sv.BF16, 1.0, sv.SAMPLE, A, A, A,
+                              A2, 1 << 30, None, None, None, None, None, None, A, None)
     assert r == sv.ERR_NULL
 
 

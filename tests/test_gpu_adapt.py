@@ -166,3 +166,32 @@ def test_fused_matches_separate(B, stride, batch_off):
         cnt = np.where(acc, rng.integers(0, 5, size=B), 0)
         n = _i32(np.minimum(cnt, gam))
         g = g2.clone()
+
+
+def test_choice_matches_closed_form_on_gpu():
+    """The device's draft length against the pages' closed form directly
+    (numpy, with division: argmax over g of (1 - a^(g+1)) / (1 - a) / (1 + g c),
+    smallest g on ties), not against the oracle's loop.  Each row's running
+    acceptance is set through its state (A = a T, no prior) and read back."""
+    from test_oracle_gamma import best_gamma
+    rng = np.random.default_rng(77)
+    alphas = np.concatenate([rng.random(2000), [0.0, 1.0, 0.5, 0.999999, 1e-9]])
+    B = alphas.size
+    T = 1e6
+    checked = 0
+    for cap in (1, 4, 8, 63):
+        for c in (0.0, 0.001, 0.05, 0.15, 0.3, 1.0):
+            state = np.stack([alphas * T, np.full(B, T)], 1)
+            ctl = sv.GammaControl(B, gamma_max=cap, decay=1.0, prior_alpha=0.5,
+                                  prior_weight=0.0, draft_cost=c)
+            ctl.state.copy_(torch.from_numpy(state))
+            alpha = torch.empty(B, dtype=torch.float64, device="cuda")
+            gam = ctl(alpha=alpha).cpu().numpy()
+            a = alpha.cpu().numpy()
+            np.testing.assert_allclose(a, alphas, rtol=1e-15, atol=1e-15)
+            for b in range(B):
+                want, close = best_gamma(a[b], c, cap)
+                if not close:
+                    assert gam[b] == want, (a[b], c, cap, gam[b], want)
+                    checked += 1
+    assert checked > 40_000

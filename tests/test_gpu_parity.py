@@ -333,3 +333,27 @@ def test_handoff_stress_alternating_data(torch, mode):
             for key in ("m", "s", "z"):
                 np.testing.assert_array_equal(got[3][key], refs[j][3][key], err_msg=f"call {k} {key}")
     assert ws.diagnostics() == 0
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 257), ("bf16", 4096), ("f32", 5003), ("bf16", 50001)])
+def test_edge_zero_residual(torch, dtype, V):
+    """Identical target and draft logits with the drafted token at -inf in
+    both rows: p(x) = q(x) = 0, so the walk rejects at 0 while max(0, p - q)
+    has no mass at all.  The draw then comes from p_0 with the next uniform
+    (the reading the oracle follows, pinned there against numpy's inverse
+    CDF), the probes match, and the diagnostic word reports the fallback."""
+    case = inputs.make_case(1, rnd=17, B=6, V=V, dtype=dtype)
+    G = case.G
+    t = case.target.copy()
+    ninf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    for b in range(case.B):
+        t[b, 0, case.tokens[b, 0]] = ninf
+    case.target, case.draft = t, np.ascontiguousarray(t[:, :G])
+    ws = sv.Workspace(sv.workspace_bytes(case.B, G, V, sv.BF16 if dtype == "bf16" else sv.F32,
+                                         sv.SAMPLE))
+    tok, n, ln, pr = run(case, torch, workspace=ws)
+    ref = parity.run_oracle(case)
+    assert np.all(ref.zero_resid == 1) and np.all(ref.n_accepted == 0)
+    rep = parity.compare(case, tok, n, ln, pr, ref=ref)
+    assert rep.ok and not rep.mismatched, (rep.summary(), rep.prob_errors[:5])
+    assert ws.diagnostics() & 2
