@@ -75,11 +75,23 @@ def parse():
     ap.add_argument("--top-p", type=float, default=1.0, help="top-p filter of p and q (1: off)")
     ap.add_argument("--rotate", type=int, default=0, help="device copies (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=18.0)
     ap.add_argument("--with-copy", action="store_true",
                     help="also run the reference copy kernel (counter calibration)")
     ap.add_argument("--tune", default="", help="vectors[,target_workgroups]")
     return ap.parse_args()
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def source_hash(path=KERNEL_SRC) -> str:
@@ -503,21 +515,32 @@ def main():
     cpu = None
     if not args.no_cpu:
         import oracle
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-        reps, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and reps < 10000:
+        omode = {sv.SAMPLE: oracle.SAMPLE, sv.GREEDY: oracle.GREEDY, sv.POINT: oracle.POINT}[mode]
+
+        def oracle_rate(threads, batches):
             c0 = time.perf_counter()
-            oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
-                          case.kv_len, temperature=case.T,
-                          mode={sv.SAMPLE: oracle.SAMPLE, sv.GREEDY: oracle.GREEDY,
-                                sv.POINT: oracle.POINT}[mode],
-                          threads=threads, top_k=args.top_k if filt else 0,
-                          top_p=args.top_p if filt else 1.0)
-            t_cpu += time.perf_counter() - c0
-            reps += 1
-        cpu = {"value": B * reps / t_cpu, "unit": "rows/s", "cores": threads, "kind": "oracle",
-               "sample": f"{reps} full batches of this workload ({B} rows each), "
-                         f"{t_cpu:.1f} s of double-precision oracle work"}
+            for _ in range(batches):
+                oracle.verify(case.target, case.draft, case.tokens, case.uniforms, case.gamma,
+                              case.kv_len, temperature=case.T, mode=omode, threads=threads,
+                              top_k=args.top_k if filt else 0,
+                              top_p=args.top_p if filt else 1.0)
+            return B * batches / (time.perf_counter() - c0)
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+        # size each run from one timed batch: about cpu_seconds / 6 per run,
+        # three runs on one thread and three on all threads (median of each)
+        t1 = B / oracle_rate(1, 1)
+        n1 = max(1, int(args.cpu_seconds / 6 / t1))
+        one = sorted(oracle_rate(1, n1) for _ in range(3))
+        tn = B / oracle_rate(threads, 1)
+        nn = max(1, int(args.cpu_seconds / 6 / tn))
+        alln = sorted(oracle_rate(threads, nn) for _ in range(3))
+        cpu = {"value": alln[1], "unit": "rows/s", "cores": threads, "kind": "oracle",
+               "value_1_thread": one[1], "runs_1_thread": one, "runs_all_threads": alln,
+               "cpu_model": cpu_model(),
+               "sample": f"median of 3 runs of {nn} full batches ({B} rows each) on {threads} "
+                         f"threads, and of 3 runs of {n1} batches on 1 thread; "
+                         f"double-precision oracle"}
 
     ftxt = f" top_k={args.top_k} top_p={args.top_p}" if filt else ""
     cfgd = {"workload": f"verify B={B} gamma={G} V={V} "

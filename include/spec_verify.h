@@ -186,10 +186,15 @@ int spec_verify_probe(const void* target_logits, const void* draft_logits,
  *   cuts from q_i has q_i(x_i) = 0 and is accepted iff p_i(x_i) > 0).
  * top_k = 0 and top_p = 1 turn a filter off; with both off this is
  * spec_verify.  GREEDY ignores both (the filters keep the largest logit).
- * POINT filters p only (there is no q).  Masses are compared in fixed point
- * (units of 2^-42 of the row's largest weight), so a row whose top-p cut lies
- * within about 1e-12 of its mass from the boundary may cut one value apart
- * from an exact computation.  Two launches on `stream`: the thresholds (into
+ * POINT filters p only (there is no q).  Masses are fp32 exponentials
+ * 2^(l k2 - R) (k2 = log2(e)/T rounded to fp32), summed exactly in fixed point
+ * (units of 2^-42 of the row's largest weight).  Each mass is within about
+ * 1e-7 relative of exp((l - max)/T) near the top of the row and within
+ * |l - max|/T * 1e-7 further down (the rounding of the exponent and of k2), so
+ * a cumulative mass is within about 1e-6 of the row's kept mass from the
+ * exact one: a row whose top-p cut lies that close to the boundary may cut
+ * one value apart from an exact computation.  Two launches on `stream`: the
+ * thresholds (into
  * the workspace), then the verify.  Errors: those of spec_verify, and
  * SPEC_ERR_ARG for top_k < 0 or top_p outside (0, 1]. */
 int spec_verify_filtered(const void* target_logits, const void* draft_logits,

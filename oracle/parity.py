@@ -83,7 +83,12 @@ def _close(gpu, ref):
 _MODES = {"sample": oracle.SAMPLE, "greedy": oracle.GREEDY, "point": oracle.POINT}
 
 
-FILTER_MARGIN = 1e-6   # top-p cuts closer than this (relative mass) may differ by one value
+# Top-p cuts closer than this to the boundary (relative to the kept mass) may
+# differ by one value: the GPU's masses are fp32 exponentials, each within
+# ~1e-7 relative near the top of the row and ~|l - max|/T * 1e-7 further down
+# (the exponent's and k2's fp32 rounding), which bounds the error of a
+# cumulative mass by a few 1e-7 of the kept mass; 1e-6 covers it.
+FILTER_MARGIN = 1e-6
 
 
 def _filters(case):

@@ -46,9 +46,12 @@ def load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it first (__graft_entry__.build())")
-    lib = ctypes.CDLL(LIB_PATH)
+    # SPEC_VERIFY_LIB: another build of this library's sources to load
+    # instead (the host-sanitizer build of tests/run_sanitized.py)
+    path = os.environ.get("SPEC_VERIFY_LIB") or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (__graft_entry__.build())")
+    lib = ctypes.CDLL(path)
     P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     verify_args = [P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, P, P, P, P, sz, P]
     lib.spec_verify.argtypes = verify_args
