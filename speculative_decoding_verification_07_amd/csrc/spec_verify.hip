@@ -695,12 +695,9 @@ struct Lds {
   float M[kMaxRows];           // merged row statistics, row r = target i (r = i)
   float S[kMaxRows];           //   or draft i (r = g + 1 + i); greedy: argmax bits
   double red_d[8 * kWaves];
-  uint4 vt, vd;                // the owner thread's vector, for the element search
-  double brk[2];               // the drawn token's CDF bracket (sums before / through it)
   unsigned long long mask[kWaves];
   Decision dec;
   Owner own;
-  double dbl;
   int pick, last;
   int bad;  // a poll of this workgroup gave up waiting
 };
@@ -1434,110 +1431,111 @@ __device__ Owner find_owner(const Args& a, const uint64_t* ws, int kind, double 
 
 // Inverse CDF inside the owner's slice: the first element of positive weight
 // whose running sum (base + the weights before it, in index order) exceeds
-// tau; if rounding leaves none, the last element with positive weight.  Each
-// thread's segment values (from LDS) are its weights against the final rho;
-// the segment holding tau comes from their block totals, the thread from a
-// block scan of that segment, and the element from a scan over the weights
-// of that thread's elements, one per lane of wave 0, formed as slice_sums
-// formed them.  Returns the index in the row.
+// tau; if rounding leaves none, the last element with positive weight.  The
+// slice's order is segment by segment (head, body rounds, tail), threads in
+// order inside a segment.  Each thread's segment values (from LDS) are its
+// weights against the final rho.  Every wave sums its threads' values per
+// segment; after one barrier each wave finds, from those totals, the
+// (segment, wave) block that holds tau.  Only that wave goes on: a scan over
+// its lanes gives the thread, whose elements (its vector, read from its lane)
+// are weighed one per lane, formed as slice_sums formed them, and scanned.
+struct Pick {
+  int j;        // the drawn index in the row
+  double blo;   // running sum before the drawn element
+  double bhi;   // running sum through it
+  bool mine;    // the one lane of the workgroup that writes the token
+};
+
 template <int DT, int R>
-__device__ int slice_search(const DrawParams& d, const Slice<DT, R>& st, const Slice<DT, R>& sd,
-                            const Geom& g, int lo, double drho, double base, double tau, bool fb,
-                            Lds& L) {
+__device__ Pick slice_search(const DrawParams& d, const Slice<DT, R>& st, const Slice<DT, R>& sd,
+                             const Geom& g, int lo, double drho, double base, double tau, bool fb,
+                             Lds& L) {
   using E = Elt<DT>;
   constexpr int NS = R + 2;
-  const int t = threadIdx.x;
-  double v[NS], tot[NS];
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  double v[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k)
     v[k] = d.resid ? fma(-drho, L.dr.dd[k][t], L.dr.w[k][t]) : L.dr.w[k][t];
-  block_sums_n<NS>(v, tot, L);
-  // the segment holding tau (all threads alike)
-  double carry = base;
-  int seg = -1, lastseg = -1;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    if (tot[k] > 0.0) lastseg = k;
-    if (seg < 0 && !fb) {
-      if (tot[k] > 0.0 && tau < carry + tot[k])
-        seg = k;
-      else
-        carry += tot[k];
-    }
+    const double x = wave_sum_d(v[k]);
+    if (lane == 0) L.red_d[k * kWaves + w] = x;
   }
-  if (seg < 0) {
-    if (lastseg < 0) return lo;  // no mass in the slice (cannot happen for an owner)
-    fb = true;
-    seg = lastseg;
-    carry = base;
-#pragma unroll
-    for (int k = 0; k < NS; ++k)
-      if (k < seg) carry += tot[k];
+  __syncthreads();
+  // the (segment, wave) block holding tau, the same in every wave: lane i
+  // holds block i's total (segment i / kWaves, wave i % kWaves, which is the
+  // slice's order), and a scan over the lanes gives the running sums; the
+  // fallback takes the last block with weight
+  const double x = lane < NS * kWaves ? L.red_d[lane] : 0.0;
+  double xe;
+  const double xi = wave_scan_d(x, xe);
+  const unsigned long long bh = __ballot(!fb && x > 0.0 && tau < base + xi);
+  const unsigned long long bp = __ballot(x > 0.0);
+  Pick p{lo, base, base, false};
+  if (!bp) {  // no mass in the slice (cannot happen for an owner)
+    p.mine = t == 0;
+    return p;
   }
+  if (!bh) fb = true;
+  const int bi = bh ? __ffsll((long long)bh) - 1 : 63 - __clzll((long long)bp);
+  const int ks = bi / kWaves, ws = bi % kWaves;
+  const double before = base + readlane_d(xe, bi);
+  if (w != ws) return p;
   double vs = 0.0;
 #pragma unroll
   for (int k = 0; k < NS; ++k)
-    if (k == seg) vs = v[k];
-  double incl, excl, ts;
-  block_scan_d(vs, L, incl, excl, ts);
-  int th = fb ? -1 : block_first(vs > 0.0 && tau < carry + incl, L);
-  if (th < 0) {
-    fb = true;
-    th = block_last(vs > 0.0, L);
-  }
-  if (th < 0) th = 0;
-  if (seg == 0 || seg == NS - 1) {
+    if (k == ks) vs = v[k];
+  double excl;
+  const double incl = wave_scan_d(vs, excl);
+  const unsigned long long hit = __ballot(!fb && vs > 0.0 && tau < before + incl);
+  const unsigned long long pos = __ballot(vs > 0.0);
+  if (!hit) fb = true;
+  const int ln = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+  const int th = w * 64 + ln;
+  const double b0 = before + readlane_d(excl, ln);  // the sum before the thread's elements
+  if (ks == 0 || ks == NS - 1) {
     // a head or tail element: the thread's one element of the segment
-    if (t == th) {
-      L.pick = seg == 0 ? lo + th : lo + g.jb + th;
-      L.brk[0] = carry + excl, L.brk[1] = carry + incl;
-    }
-    __syncthreads();
-    const int j = L.pick;
-    __syncthreads();
-    return j;
+    p.j = ks == 0 ? lo + th : lo + g.jb + th;
+    p.blo = b0, p.bhi = before + readlane_d(incl, ln);
+    p.mine = lane == ln;
+    return p;
   }
-  // thread th's vector of round seg - 1, handed to wave 0 through LDS
-  if (t == th) {
-    L.vt = vsel(st, seg - 1, g);
-    L.vd = d.resid ? vsel(sd, seg - 1, g) : L.vt;
-    L.dbl = carry + excl;  // the sum of everything before the vector
-  }
-  __syncthreads();
-  if (t < 64) {
-    float ft[E::kVec], fd[E::kVec];
-    E::unpack(L.vt, ft);
-    E::unpack(L.vd, fd);
-    float lt = NEG_INF, lq = NEG_INF;
+  // the thread's vector of body round ks - 1, from its lane
+  const uint4 mt = vsel(st, ks - 1, g);
+  const uint4 md = d.resid ? vsel(sd, ks - 1, g) : mt;
+  uint4 xt, xd;
+  xt.x = __builtin_amdgcn_readlane(mt.x, ln), xt.y = __builtin_amdgcn_readlane(mt.y, ln);
+  xt.z = __builtin_amdgcn_readlane(mt.z, ln), xt.w = __builtin_amdgcn_readlane(mt.w, ln);
+  xd.x = __builtin_amdgcn_readlane(md.x, ln), xd.y = __builtin_amdgcn_readlane(md.y, ln);
+  xd.z = __builtin_amdgcn_readlane(md.z, ln), xd.w = __builtin_amdgcn_readlane(md.w, ln);
+  float ft[E::kVec], fd[E::kVec];
+  E::unpack(xt, ft);
+  E::unpack(xd, fd);
+  float lt = NEG_INF, lq = NEG_INF;
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e)
-      if (t == e) lt = ft[e], lq = fd[e];
-    double wl = 0.0;  // the element's weight against rho
-    if (t < E::kVec) {
-      const double et = e_of(lt, d.k2, d.rt);
-      if (d.resid) {
-        const double ed = e_of(lq, d.k2, d.rd);
-        const double x = fma(-d.rho0, ed, et);
-        wl = x > 0.0 ? fma(-drho, ed, x) : 0.0;
-      } else {
-        wl = et;
-      }
-    }
-    double ex;
-    const double run = wave_scan_d(wl, ex);
-    const double before = L.dbl;
-    const unsigned long long hit = __ballot(wl > 0.0 && !fb && tau < before + run);
-    const unsigned long long pos = __ballot(wl > 0.0);
-    const int e = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-    if (t == e) {
-      L.pick = lo + g.head + ((seg - 1) * kThreads + th) * E::kVec + e;
-      L.brk[0] = before + ex, L.brk[1] = before + run;
+  for (int e = 0; e < E::kVec; ++e)
+    if (lane == e) lt = ft[e], lq = fd[e];
+  double wl_ = 0.0;  // the element's weight against rho
+  if (lane < E::kVec) {
+    const double et = e_of(lt, d.k2, d.rt);
+    if (d.resid) {
+      const double ed = e_of(lq, d.k2, d.rd);
+      const double x = fma(-d.rho0, ed, et);
+      wl_ = x > 0.0 ? fma(-drho, ed, x) : 0.0;
+    } else {
+      wl_ = et;
     }
   }
-  __syncthreads();
-  const int j = L.pick;
-  __syncthreads();
-  return j;
+  double ex;
+  const double run = wave_scan_d(wl_, ex);
+  const unsigned long long eh = __ballot(wl_ > 0.0 && !fb && tau < b0 + run);
+  const unsigned long long ep = __ballot(wl_ > 0.0);
+  const int e = eh ? __ffsll((long long)eh) - 1 : (ep ? 63 - __clzll((long long)ep) : 0);
+  p.j = lo + g.head + ((ks - 1) * kThreads + th) * E::kVec + e;
+  p.blo = b0 + ex, p.bhi = b0 + run;
+  p.mine = lane == e;
+  return p;
 }
 
 // Step 3 of a live sampled row: every workgroup of the group sums its slice
@@ -1580,17 +1578,22 @@ __device__ __forceinline__ float s_rel(float m, float s, float k2) {
 }
 
 // Publishes this slice's totals {W0, D, S_t, S_d} (nw = 4) or {W} (nw = 1)
-// at word `w0` onward.
+// at word `w0` onward: wave totals through LDS, one barrier, then thread k
+// adds the four waves' totals of word k in a fixed order and stores it.
 __device__ __forceinline__ void publish_sums(const Args& a, uint64_t* ws, int c, int w0, int nw,
                                              const double (&mine)[4], Lds& L) {
-  double tot[4];
-  block_sums_n<4>(mine, tot, L);
-  const int t = threadIdx.x;
-  if (t < nw) {
-    double x = tot[0];
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
 #pragma unroll
-    for (int k = 1; k < 4; ++k)
-      if (t == k) x = tot[k];
+  for (int k = 0; k < 4; ++k) {
+    if (k < nw) {
+      const double x = wave_sum_d(mine[k]);
+      if (lane == 0) L.red_d[k * kWaves + w] = x;
+    }
+  }
+  __syncthreads();
+  if (t < nw) {
+    double x = L.red_d[t * kWaves];
+    for (int q = 1; q < kWaves; ++q) x += L.red_d[t * kWaves + q];
     put64(&ws[(w0 + t) * a.NC + c], enc_d(x));
   }
 }
@@ -1715,10 +1718,10 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
   const double tau = (double)dc.ustar * o.z;
   // linear: the weights against rho0 corrected by drho; exact: the weights
   // against rho itself (d.rho0 = rho, no correction)
-  const int j = slice_search<DT, R>(d, st, sd, gt, lo, exact ? 0.0 : o.drho, o.base, tau,
-                                    fallback, L);
-  if (t == 0) {
-    a.out_tok[(int64_t)b * (a.G + 1) + n] = j;
+  const Pick pk = slice_search<DT, R>(d, st, sd, gt, lo, exact ? 0.0 : o.drho, o.base, tau,
+                                      fallback, L);
+  if (pk.mine) {
+    a.out_tok[(int64_t)b * (a.G + 1) + n] = pk.j;
     if (a.pr_z) {
       // Z of the drawn distribution in probability units: residual W / S_t;
       // bonus 1; point-mass draft 1 - p_n(x_n) = W / (W + e_t(x_n))
@@ -1728,8 +1731,8 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
       a.pr_z[b] = (float)zp;
     }
     if (a.pr_flo) {  // the normalised CDF just below and at the drawn token
-      a.pr_flo[b] = (float)(L.brk[0] / o.z);
-      a.pr_fhi[b] = (float)(L.brk[1] / o.z);
+      a.pr_flo[b] = (float)(pk.blo / o.z);
+      a.pr_fhi[b] = (float)(pk.bhi / o.z);
     }
   }
 }
