@@ -238,14 +238,26 @@ int spec_filter_thresholds(const void* target_logits, const void* draft_logits,
  * workgroup count}.  Returns SPEC_OK or an argument error. */
 int spec_verify_plan(int B, int gamma_max, int V, int dtype, int mode, int64_t* out);
 
+/* Flags of spec_verify_tune. */
+enum spec_tune_flags {
+  /* Unfiltered SAMPLE calls stream every vocabulary row of a batch row in one
+   * pass and decide all positions at once, instead of the default: reading
+   * the rows position by position, (t_i, d_i) for i = 0, 1, ..., and
+   * stopping at the walk's first rejection (the rows after it are never
+   * used), at the cost of one hand-off between a row's workgroups per
+   * position.  Results are the same either way. */
+  SPEC_TUNE_ONE_PASS = 1
+};
+
 /* Process-wide override of the launch tuning (for benchmarking sweeps).
  * vectors: 16-byte vectors per thread and vocabulary row, which sets the
  * slice length (vectors * 4 KiB of logits): 1, 2 or 4, or 0 to choose it
  * from the sizes -- the largest slices that still
  * give at least target_workgroups workgroups.  target_workgroups: 0 keeps
- * the default (1024).  reserved: must be 0.  Changes
- * spec_verify_workspace_bytes; not thread-safe against concurrent calls. */
-int spec_verify_tune(int vectors, int target_workgroups, int reserved);
+ * the default (1024).  flags: 0 or SPEC_TUNE_ONE_PASS (any other bit is
+ * SPEC_ERR_ARG).  Changes spec_verify_workspace_bytes; not thread-safe
+ * against concurrent calls. */
+int spec_verify_tune(int vectors, int target_workgroups, int flags);
 
 /* Reads the workspace's diagnostic word (device -> host copy on `stream`,
  * synchronous): bit 0 set if a workgroup ever gave up waiting for the rest

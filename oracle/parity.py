@@ -103,8 +103,15 @@ def run_oracle(case, threads=0):
                          top_k=k, top_p=p)
 
 
-def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) -> Report:
-    """Compare GPU outputs (numpy) for one batch with the oracle."""
+def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0,
+            all_rows=False) -> Report:
+    """Compare GPU outputs (numpy) for one batch with the oracle.
+
+    Probe statistics are checked for the rows the walk uses -- positions
+    0..n of the oracle's stop n (p_i, q_i at x_i; the pairs of t_i and d_i;
+    t_g when every draft is accepted) -- since the walk reads no row after
+    its stop; all_rows=True checks every row of every batch row (for kernels
+    that stream them all)."""
     if ref is None:
         ref = run_oracle(case)
     rep = Report(rows=case.B)
@@ -122,7 +129,9 @@ def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) ->
         for b in range(case.B):
             if ref.n_accepted[b] < 0 or near_cut[b]:
                 continue
-            for i in range(int(g[b])):
+            n_or = int(ref.n_accepted[b])
+            tested = int(g[b]) if all_rows else min(n_or + 1, int(g[b]))
+            for i in range(tested):
                 if np.isnan(ref.px[b, i]):
                     continue
                 for what, gv, ov in (("p", probe["px"][b, i], ref.px[b, i]),
@@ -132,9 +141,13 @@ def compare(case, tokens, n_acc, new_len, probe=None, ref=None, row_offset=0) ->
                     if not ok:
                         rep.prob_errors.append((row_offset + b, i, what, float(gv), float(ov)))
             # per vocabulary row statistics: max exact, S within 1e-5 relative
-            nr = 2 * int(g[b]) + 1 if case.mode == "sample" else int(g[b]) + 1
-            slots = list(range(int(g[b]) + 1)) + [case.G + 1 + i for i in range(int(g[b]))]
-            for sl in slots[:nr]:
+            gb = int(g[b])
+            nt = gb + 1 if all_rows else min(n_or, gb) + 1  # t_0 .. t_n
+            nd = gb if all_rows else min(n_or + 1, gb)      # d_0 .. d_n (d_g does not exist)
+            slots = list(range(nt))
+            if case.mode == "sample":
+                slots += [case.G + 1 + i for i in range(nd)]
+            for sl in slots:
                 if probe["m"][b, sl] != np.float32(ref.m[b, sl]):
                     rep.prob_errors.append((row_offset + b, sl, "m", float(probe["m"][b, sl]),
                                             float(ref.m[b, sl])))

@@ -64,6 +64,7 @@ constexpr int kRowWords = kLine;
 struct Tuning {
   int vectors = 0;  // 16-byte vectors per thread and row; 0: chosen from the sizes
   int target_workgroups = kDefaultTargetWorkgroups;
+  int flags = 0;    // SPEC_TUNE_ONE_PASS: sampling streams every row in one pass
 };
 Tuning g_tune;
 
@@ -1600,6 +1601,10 @@ __device__ __forceinline__ void publish_sums(const Args& a, uint64_t* ws, int c,
 
 // KNOCK: point-mass drafts (q_i is the indicator of x_i); RING: the ring
 // holds the last rows streamed (sampling).
+template <int DT, int R, bool KNOCK, bool FILT, bool AL, bool PRIO>
+__device__ void draw_body(const Args& a, Lds& L, int b, int c, int g, int lo, int nrows,
+                          const Decision& dc, Slice<DT, R> st, Slice<DT, R> sd, const Geom& gt);
+
 template <int DT, int R, bool KNOCK, bool RING, bool FILT, bool AL, bool PRIO>
 __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len, int nrows,
                      const Decision& dc, const Ring<DT, R>& ring) {
@@ -1609,12 +1614,6 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
   const int n = dc.n;
   const bool resid = !KNOCK && dc.resid;  // a residual of two rows
   const bool knock = KNOCK && dc.resid;   // point-mass draft rejected at n
-  DrawParams d;
-  d.k2 = a.k2d;
-  d.rt = (double)dc.mt * a.k2d;
-  d.rd = resid ? (double)dc.md * a.k2d : 0.0;
-  d.rho0 = resid ? (double)s_rel(dc.mt, dc.st, a.k2) / (double)s_rel(dc.md, dc.sd, a.k2) : 0.0;
-  d.resid = resid;
   // stream indices of the rows drawn from (the inverse of stream_row): t_n
   // and d_n at 2(g-1-n)+1 and +2 when sampling, t_n at g-n with point-mass
   // drafts, t_g first of all for the bonus draw
@@ -1654,6 +1653,24 @@ __device__ void draw(const Args& a, Lds& L, int b, int c, int g, int lo, int len
         load_slice_as<DT, R>(dp, gt, sd);
     }
   }
+  draw_body<DT, R, KNOCK, FILT, AL, PRIO>(a, L, b, c, g, lo, nrows, dc, st, sd, gt);
+}
+
+// The draw from the slices of the rows drawn from, in registers: st (t_n, or
+// t_g for the bonus draw) and, for a residual, sd (d_n in st's layout).
+template <int DT, int R, bool KNOCK, bool FILT, bool AL, bool PRIO>
+__device__ void draw_body(const Args& a, Lds& L, int b, int c, int g, int lo, int nrows,
+                          const Decision& dc, Slice<DT, R> st, Slice<DT, R> sd, const Geom& gt) {
+  const int t = threadIdx.x;
+  const int n = dc.n;
+  const bool resid = !KNOCK && dc.resid;  // a residual of two rows
+  const bool knock = KNOCK && dc.resid;   // point-mass draft rejected at n
+  DrawParams d;
+  d.k2 = a.k2d;
+  d.rt = (double)dc.mt * a.k2d;
+  d.rd = resid ? (double)dc.md * a.k2d : 0.0;
+  d.rho0 = resid ? (double)s_rel(dc.mt, dc.st, a.k2) / (double)s_rel(dc.md, dc.sd, a.k2) : 0.0;
+  d.resid = resid;
   if (FILT) {  // the filtered rows: cut entries weigh 0
     const float* th = a.thr + (int64_t)b * (2 * a.G + 1);
     mask_slice(st, th[resid || knock ? n : g]);
@@ -1847,6 +1864,239 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   } else {
     row_exit(a, L, b, nrows);
   }
+}
+
+// ------------------------------------------------------------------ sampling, row by row
+// The walk stops at its first rejection n and uses no row after it: only
+// (t_i, d_i) for i <= n, and t_g when every draft is accepted ("Speculative
+// decoding", mhtirogla.ai, "How it works" steps 3-4; tusharamrit, the
+// acceptance loop of the proof).  This kernel reads the rows position by
+// position: every workgroup of a row's group loads its slice of t_i and d_i,
+// publishes their (m, S), waits for the group's pairs of those two rows,
+// merges them and runs the test at i -- the same test, from the same merged
+// statistics, as the one-pass kernel -- and goes on to position i + 1 only
+// when x_i is accepted.  A rejection draws from the pair still in registers.
+// Each position costs a group hand-off; in exchange no row after the stop is
+// read at all.
+
+// Merges the staged pairs of k <= 2 rows (stage[j * nc + c]) into L.M / L.S
+// at rows ra (j = 0) and rb (j = 1), with the reduction of the one-pass merge
+// (so a row's merged pair is the same bits in both kernels).  Wave 0.
+template <int LPR>
+__device__ void merge_two(const Args& a, Lds& L, int k, int nc, int ra, int rb) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane / LPR, c = lane % LPR;
+  const bool have = j < k && c < nc;
+  const uint64_t st = have ? L.sm.stage[j * nc + c] : 0;
+  float m = have ? lo_f(st) : NEG_INF, s = have ? hi_f(st) : 0.f;
+  group_ms<LPR>(m, s, a.k2);
+  if (c == 0 && j < k) {
+    const int r = j == 0 ? ra : rb;
+    L.M[r] = m, L.S[r] = s;
+  }
+}
+
+__device__ void merge_two_wide(const Args& a, Lds& L, int k, int nc, int ra, int rb) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (w >= k) return;
+  const uint64_t* st = &L.sm.stage[w * nc];
+  float m = NEG_INF, s = 0.f;
+  for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
+  wave_ms_dpp(m, s, a.k2);
+  if (lane == 0) {
+    const int r = w == 0 ? ra : rb;
+    L.M[r] = m, L.S[r] = s;
+  }
+}
+
+// This workgroup's (m, S) of its slices of rows ra (and rb when k = 2), as
+// per-wave partials in L.sm.wm / L.sm.ws.
+template <int DT, int R, bool AL>
+__device__ void slice_pairs(const Args& a, Lds& L, const Slice<DT, R>& st, const Geom& gt,
+                            const Slice<DT, R>& sd, const Geom& gd, int k, int ra, int rb) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float m, sm;
+  wave_slice_ms<DT, R, AL, false>(st, gt, a.k2, NEG_INF, m, sm);
+  if (lane == 0) L.sm.wm[ra][w] = m, L.sm.ws[ra][w] = sm;
+  if (k == 2) {
+    wave_slice_ms<DT, R, AL, false>(sd, gd, a.k2, NEG_INF, m, sm);
+    if (lane == 0) L.sm.wm[rb][w] = m, L.sm.ws[rb][w] = sm;
+  }
+}
+
+// Publishes this workgroup's pairs of rows ra (and rb): the four waves'
+// partials merged in a fixed order.
+__device__ void publish_rows(const Args& a, Lds& L, int b, int c, int k, int ra, int rb) {
+  const int t = threadIdx.x;
+  __syncthreads();
+  if (t < k) {
+    const int r = t == 0 ? ra : rb;
+    float m = L.sm.wm[r][0], sm = L.sm.ws[r][0];
+    for (int q = 1; q < kWaves; ++q) ms_merge(m, sm, L.sm.wm[r][q], L.sm.ws[r][q], a.k2);
+    put64(&a.part[((int64_t)b * a.NC + c) * a.NR + r], pack2(m, sm));
+  }
+}
+
+// Waits for the group's pairs of rows ra (and rb) and merges them into
+// L.M / L.S.
+__device__ void gather_rows(const Args& a, Lds& L, int b, int k, int ra, int rb) {
+  const int t = threadIdx.x, nc = a.NC;
+  const uint64_t* base = a.part + (int64_t)b * nc * a.NR;
+  for (int q = t; q < k * nc; q += kThreads) {
+    const int r = q < nc ? ra : rb, cc = q < nc ? q : q - nc;
+    L.sm.stage[q] = poll64(a, &base[(int64_t)cc * a.NR + r], &L.bad);
+  }
+  __syncthreads();
+  if (nc <= 16) {
+    if (t < 64) {
+      if (nc <= 4)
+        merge_two<4>(a, L, k, nc, ra, rb);
+      else if (nc <= 8)
+        merge_two<8>(a, L, k, nc, ra, rb);
+      else
+        merge_two<16>(a, L, k, nc, ra, rb);
+    }
+  } else {
+    merge_two_wide(a, L, k, nc, ra, rb);
+  }
+  __syncthreads();
+}
+
+template <int DT, int R, bool AL>
+__global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(Args a) {
+  using E = Elt<DT>;
+  __shared__ Lds L;
+  const int t = threadIdx.x, lane = t & 63;
+  if (t == 0) L.bad = 0;
+  const int b = (int)(blockIdx.x / (unsigned)a.NC), c = (int)(blockIdx.x % (unsigned)a.NC);
+  const int g = a.gam[b];
+  if (g < 0 || g > a.G) {
+    if (c == 0) write_sentinel(a, b);
+    return;
+  }
+  const int nrows = 2 * g + 1;
+  const int lo = c * a.CL;
+  const int len = min(a.V - lo, a.CL);
+  // The walk (reads, hand-offs, tests) runs at wave priority 3, the draw's
+  // weights at 1 (2 from its slice-sum wait on): a row still walking is on
+  // the path to the call's end, and issue goes first to its waves; the
+  // draws of rows already stopped take the slots the walk leaves.
+  __builtin_amdgcn_s_setprio(3);
+  // x_i, u_i and the logits at x_i, all in flight while the first rows load
+  Gathered in = gather_small<SPEC_MODE_SAMPLE>(a, b, g);
+  gather_logits<DT, SPEC_MODE_SAMPLE, false>(a, b, g, in);
+  Slice<DT, R> st, sd;
+  Geom gt, gd;
+  int n = 0, verdict = 0;  // verdict: 0 accepted, 1 rejected, 2 sentinel
+  // position i's rows: t_i (t_g at i = g) and d_i (i < g)
+  auto issue = [&](int i) {
+    const char* tp = row_of<DT>(a, b, g, i) + (int64_t)lo * E::kBytes;
+    gt = geom_of<DT, AL>(tp, len);
+    load_slice<DT, R, AL>(tp, gt, st);
+    if (i < g) {
+      const char* dp = row_of<DT>(a, b, g, g + 1 + i) + (int64_t)lo * E::kBytes;
+      gd = geom_of<DT, AL>(dp, len);
+      load_slice<DT, R, AL>(dp, gd, sd);
+    }
+  };
+  auto pairs_of = [&](int i) {
+    issue(i);
+    slice_pairs<DT, R, AL>(a, L, st, gt, sd, gd, i < g ? 2 : 1, i, g + 1 + i);
+  };
+  pairs_of(0);
+  publish_rows(a, L, b, c, g > 0 ? 2 : 1, 0, g + 1);
+  for (int i = 0;; ++i) {
+    const bool bonus = i == g;
+    const int rt = i, rd = g + 1 + i;
+    gather_rows(a, L, b, bonus ? 1 : 2, rt, rd);
+    if (L.bad) {  // a slice's pairs never arrived (cannot happen in a correct launch)
+      write_sentinel(a, b);
+      row_exit(a, L, b, nrows);
+      return;
+    }
+    if (t < 64) {
+      if (c == 0 && a.pr_m && lane < (bonus ? 1 : 2)) {
+        const int r = lane == 0 ? rt : rd;
+        const int slot = probe_slot(a, g, r);
+        const float mm = L.M[r];
+        a.pr_m[(int64_t)b * (2 * a.G + 1) + slot] = mm;
+        if (a.pr_s)
+          a.pr_s[(int64_t)b * (2 * a.G + 1) + slot] =
+              mm != NEG_INF ? L.S[r] * ex2(-fmaf(mm, a.k2, -ref_of(mm, a.k2))) : L.S[r];
+      }
+      int v = 1;  // bonus: the walk ends here
+      if (!bonus) {
+        // the test at i, in lane i (which holds x_i, u_i and the logits at x_i)
+        const bool valid = (unsigned)in.x < (unsigned)a.V;
+        bool fail = true;
+        if (valid) {
+          const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.M[rt], a.k2))) / L.S[rt];
+          const float q = ex2(fmaf(in.dv, a.k2, -ref_of(L.M[rd], a.k2))) / L.S[rd];
+          if (c == 0 && lane == i && a.pr_px) {
+            a.pr_px[(int64_t)b * a.G + i] = p;
+            a.pr_qx[(int64_t)b * a.G + i] = q;
+          }
+          fail = !(in.u * q < p);
+        }
+        v = __builtin_amdgcn_readlane(fail ? (valid ? 1 : 2) : 0, i);
+      }
+      // a row the walk uses must have a finite logit (a dead p_i or q_i
+      // fails the test at i, so only the stop position can hold one)
+      if (v == 1 && (L.M[rt] == NEG_INF || (!bonus && L.M[rd] == NEG_INF))) v = 2;
+      if (t == 0) L.pick = v;
+    }
+    __syncthreads();
+    verdict = L.pick;
+    if (verdict != 0) {
+      n = i;
+      break;
+    }
+    // x_i accepted: position i + 1 (reading it any earlier, during this
+    // hand-off, measured slower: the reads of rows that stop here compete
+    // with every other row's)
+    pairs_of(i + 1);
+    publish_rows(a, L, b, c, i + 1 < g ? 2 : 1, i + 1, g + 2 + i);
+  }
+  const bool sentinel = verdict == 2;
+  if (t < 64) {
+    if (c == 0) {
+      // lane i owns output position i (gamma_max <= 63)
+      if (lane <= a.G && !(lane == n && !sentinel))
+        a.out_tok[(int64_t)b * (a.G + 1) + lane] = !sentinel && lane < n ? in.x : -1;
+      if (lane == 0) {
+        const int kv = a.kv ? a.kv[b] : 0;
+        a.out_n[b] = sentinel ? -1 : n;
+        a.out_len[b] = sentinel ? kv : kv + n;
+      }
+    }
+    if (t == 0) {
+      Decision d;
+      d.n = n, d.dead = sentinel, d.resid = n < g;
+      d.xn = 0, d.tx = 0.f;
+      d.mt = L.M[n], d.st = L.S[n];
+      d.md = n < g ? L.M[g + 1 + n] : 0.f;
+      d.sd = n < g ? L.S[g + 1 + n] : 1.f;
+      L.dec = d;
+    }
+    // u of the draw: u_{n+1} after a rejection at n, u_g for the bonus draw
+    const float ustar =
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in.u), n < g ? n + 1 : g));
+    if (t == 0) L.dec.ustar = ustar;
+  }
+  __syncthreads();
+  const Decision dc = L.dec;
+  if (dc.dead) {
+    row_exit(a, L, b, nrows);
+    return;
+  }
+  if (dc.resid && !AL && gd.head != gt.head) {
+    // the weights pair element j of both rows: d_n in t_n's register layout
+    const char* dp = row_of<DT>(a, b, g, g + 1 + n) + (int64_t)lo * E::kBytes;
+    load_slice_as<DT, R>(dp, gt, sd);
+  }
+  if (!dc.resid) sd = st;
+  __builtin_amdgcn_s_setprio(1);
+  draw_body<DT, R, false, false, AL, true>(a, L, b, c, g, lo, nrows, dc, st, sd, gt);
 }
 
 // ------------------------------------------------------------------ filtering
@@ -2392,6 +2642,16 @@ void launch_r(int R, bool prio, dim3 grid, hipStream_t s, const Args& a) {
     hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL, FILT, false>), grid, dim3(kThreads), 0, s, a);
 }
 
+template <int DT, bool AL>
+void launch_rows_r(int R, dim3 grid, hipStream_t s, const Args& a) {
+  if (R == 1)
+    hipLaunchKernelGGL((verify_rows_kernel<DT, 1, AL>), grid, dim3(kThreads), 0, s, a);
+  else if (R == 2)
+    hipLaunchKernelGGL((verify_rows_kernel<DT, 2, AL>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((verify_rows_kernel<DT, 4, AL>), grid, dim3(kThreads), 0, s, a);
+}
+
 // greedy never filters (the filters keep the largest logit)
 template <int DT, int MODE>
 void launch(int R, bool prio, bool al, bool filt, dim3 grid, hipStream_t s, const Args& a) {
@@ -2492,6 +2752,22 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
                   dtype, s);
     const int hs = hip_status(hipGetLastError());
     if (hs != SPEC_OK) return hs;
+  }
+  // unfiltered sampling reads the rows position by position, up to the
+  // walk's stop (unless the one-pass stream is asked for)
+  if (sample && !filt && !(g_tune.flags & SPEC_TUNE_ONE_PASS)) {
+    if (dtype == SPEC_DTYPE_BF16) {
+      if (al)
+        launch_rows_r<SPEC_DTYPE_BF16, true>(p.R, grid, s, a);
+      else
+        launch_rows_r<SPEC_DTYPE_BF16, false>(p.R, grid, s, a);
+    } else {
+      if (al)
+        launch_rows_r<SPEC_DTYPE_F32, true>(p.R, grid, s, a);
+      else
+        launch_rows_r<SPEC_DTYPE_F32, false>(p.R, grid, s, a);
+    }
+    return hip_status(hipGetLastError());
   }
   if (dtype == SPEC_DTYPE_BF16) {
     if (sample)
@@ -2693,13 +2969,14 @@ int spec_verify_plan(int B, int gamma_max, int V, int dtype, int mode, int64_t* 
   return SPEC_OK;
 }
 
-int spec_verify_tune(int vectors, int target_workgroups, int reserved) {
-  if (reserved != 0) return SPEC_ERR_ARG;
+int spec_verify_tune(int vectors, int target_workgroups, int flags) {
+  if ((flags & ~SPEC_TUNE_ONE_PASS) != 0) return SPEC_ERR_ARG;
   if (vectors != 0 && vectors != 1 && vectors != 2 && vectors != 4) return SPEC_ERR_ARG;
   if (target_workgroups < 0) return SPEC_ERR_ARG;
   Tuning t;
   t.vectors = vectors;
   if (target_workgroups) t.target_workgroups = target_workgroups;
+  t.flags = flags;
   g_tune = t;
   return SPEC_OK;
 }

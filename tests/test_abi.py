@@ -172,7 +172,11 @@ def test_tune_changes_plan_and_restores(lib):
         for bad in (dict(vectors=3), dict(vectors=8), dict(vectors=-1), dict(target_workgroups=-5)):
             with pytest.raises(sv.SpecVerifyError):
                 sv.tune(**bad)
-        assert lib.spec_verify_tune(0, 0, 1) == sv.ERR_ARG
+        # flags: only SPEC_TUNE_ONE_PASS is defined; it leaves the plan alone
+        for bad_flags in (2, 4, -1):
+            assert lib.spec_verify_tune(0, 0, bad_flags) == sv.ERR_ARG
+        sv.tune(one_pass=True)
+        assert sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE) == base
     finally:
         sv.tune()
     assert sv.plan(64, 4, 128256, sv.BF16, sv.SAMPLE) == base

@@ -30,9 +30,12 @@ def torch():
     return _t
 
 
-def _check(case, torch, **kw):
+def _check(case, torch, all_rows=None, **kw):
     tok, n, ln, pr = run(case, torch, **kw)
-    rep = parity.compare(case, tok, n, ln, pr)
+    # the one-pass kernels (point-mass drafts here) report every row's statistics
+    if all_rows is None:
+        all_rows = case.mode == "point"
+    rep = parity.compare(case, tok, n, ln, pr, all_rows=all_rows)
     assert rep.ok, (rep.summary(), rep.mismatched[:5], rep.prob_errors[:5])
     return rep, tok, n, ln, pr
 
@@ -92,7 +95,8 @@ def test_parity_full_size(torch, cfg, mode):
             pr = None
             if all(p[4] is not None for p in pending):
                 pr = {k: np.concatenate([p[4][k] for p in pending]) for k in pending[0][4]}
-        total.merge(parity.compare(c, tok, n, ln, pr, row_offset=total.rows))
+        total.merge(parity.compare(c, tok, n, ln, pr, row_offset=total.rows,
+                                   all_rows=mode == "point"))
         pending.clear()
 
     for k in range(calls):
@@ -274,7 +278,9 @@ def test_repeat_is_bit_identical(torch):
 
 def test_tuning_invariance(torch):
     """Greedy is bit-identical for any slice size; sampling stays within the
-    parity bar for each of them."""
+    parity bar for each of them, and for a given slice size the row-by-row
+    and the one-pass sampling kernels give the same bits (the same merged
+    statistics, tests and draws)."""
     cg = inputs.make_case(3, rnd=1, mode="greedy", B=16, V=40000)
     cs = inputs.make_case(3, rnd=1, B=16, V=40000)
     ref = run(cg, torch, probe=False)
@@ -285,9 +291,56 @@ def test_tuning_invariance(torch):
             got = run(cg, torch, probe=False)
             for x, y in zip(ref[:3], got[:3]):
                 np.testing.assert_array_equal(x, y)
-            _check(cs, torch)
+            _, *rows = _check(cs, torch)
+            sv.tune(vectors, one_pass=True)
+            print(f"tune vectors={vectors} one_pass", flush=True)
+            _, *one = _check(cs, torch, all_rows=True)
+            for x, y in zip(rows[:3], one[:3]):
+                np.testing.assert_array_equal(x, y)
     finally:
         sv.tune()
+
+
+ONE_PASS = [(1, dict(B=4, V=5003)), (2, dict(B=8, V=3001)), (3, dict(B=16, V=20011)),
+            (4, dict(B=12, V=9999)), (5, dict(B=12, V=7777))]
+
+
+@pytest.mark.parametrize("cfg,kw", ONE_PASS)
+def test_parity_one_pass_sampling(torch, cfg, kw):
+    """The one-pass sampling kernel (every row streamed, all positions decided
+    at once), with every row's statistics checked, and its outputs equal to
+    the row-by-row kernel's."""
+    try:
+        for rnd in range(2):
+            case = inputs.make_case(cfg, rnd=300 + rnd, **kw)
+            print(f"one-pass cfg={cfg} rnd={rnd} {kw}", flush=True)
+            sv.tune(one_pass=True)
+            _, *one = _check(case, torch, all_rows=True)
+            sv.tune()
+            _, *rows = _check(case, torch)
+            for x, y in zip(one[:3], rows[:3]):
+                np.testing.assert_array_equal(x, y)
+    finally:
+        sv.tune()
+
+
+def test_parity_one_pass_full_size(torch):
+    """The one-pass sampling kernel at the headline shape (B=64, gamma=4,
+    V=128256, bf16), 2,048 rows, every row's statistics checked."""
+    total = parity.Report()
+    try:
+        sv.tune(one_pass=True)
+        for k in range(32):
+            case = inputs.make_case(3, rnd=500 + k)
+            if k % 8 == 0:
+                print(f"one-pass full call={k}/32", flush=True)
+            tok, n, ln, pr = run(case, torch, probe=k % 8 == 0)
+            total.merge(parity.compare(case, tok, n, ln, pr, row_offset=total.rows,
+                                       all_rows=True))
+    finally:
+        sv.tune()
+    print("one-pass full", total.summary(), flush=True)
+    assert total.ok, (total.summary(), total.mismatched[:5], total.prob_errors[:5])
 
 
 def test_workspace_reuse_and_diagnostics(torch):
