@@ -10,7 +10,13 @@ the 256 MB Infinity Cache.
 
 Prints one JSON line.  `value` is verified rows per second; the roofline
 object gives the dominant (only) kernel's achieved HBM rate from the
-compulsory logit bytes and its event-timed average launch duration.
+compulsory logit bytes (every row of the call: (2 g_b + 1) V e per batch row
+when sampling) and its event-timed average launch duration.  Unfiltered
+sampling runs the kernel that reads the rows position by position and stops
+at the walk's first rejection, so it reads fewer bytes than that:
+`walk_bytes_per_step` counts the rows the walk uses ((t_i, d_i) for i <= n,
+t_g after g acceptances), and --one-pass times the kernel that streams every
+row instead.
 
 With --top-k / --top-p a step is the filtered verify: the threshold kernel,
 then the verify on the filtered rows (two launches); the draft tokens are
@@ -79,6 +85,9 @@ def parse():
     ap.add_argument("--with-copy", action="store_true",
                     help="also run the reference copy kernel (counter calibration)")
     ap.add_argument("--tune", default="", help="vectors[,target_workgroups]")
+    ap.add_argument("--one-pass", action="store_true",
+                    help="unfiltered sampling streams every row in one pass instead of "
+                         "reading the rows position by position")
     return ap.parse_args()
 
 
@@ -389,8 +398,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     sv.load()
-    if args.tune:
-        sv.tune(*[int(v) for v in args.tune.split(",")])
+    if args.tune or args.one_pass:
+        tv = [int(v) for v in args.tune.split(",")] if args.tune else []
+        sv.tune(*tv, one_pass=args.one_pass)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
@@ -490,7 +500,9 @@ def main():
     # is the back-to-back time per step (event pairs around single launches
     # add their own overhead and are reported separately)
     kern_s = ms_per_step * 1e-3
-    kernel_name = "verify_kernel"
+    # unfiltered sampling reads the rows position by position (its own kernel)
+    by_rows = mode == sv.SAMPLE and not filt and not args.one_pass
+    kernel_name = "verify_rows_kernel" if by_rows else "verify_kernel"
     if filter_us is not None:
         # two launches per step: the longer one is the dominant kernel
         verify_s = kern_s - filter_us * 1e-6
@@ -499,6 +511,15 @@ def main():
     achieved = step_bytes / kern_s / 1e9
     emitted = int((n_acc + 1).sum())
     tested = int(np.minimum(n_acc + 1, case.gamma).sum())
+    # the rows the walk uses: (t_i, d_i) for i <= n, t_g when every draft is
+    # accepted (sampling); t_0..t_n (greedy, point-mass drafts)
+    gb = np.clip(case.gamma.astype(np.int64), 0, G)
+    na = n_acc.astype(np.int64)
+    if mode == sv.SAMPLE:
+        walk_rows = np.where(na < 0, 0, np.where(na < gb, 2 * (na + 1), 2 * gb + 1))
+    else:
+        walk_rows = np.where(na < 0, 0, na + 1)
+    walk_bytes = int(walk_rows.sum()) * V * case.target.itemsize
 
     ceiling = read_ceiling(sv, torch, dev, stream, args.with_copy)
 
@@ -567,6 +588,8 @@ def main():
         "config": cfgd,
         "emitted_tokens_per_s": emitted * K / (total_ms * 1e-3),
         "step_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "walk_bytes_per_step": walk_bytes,
+        "walk_gbps": walk_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernel_us": kern_s * 1e6,
         "filter_kernel_us": filter_us,
