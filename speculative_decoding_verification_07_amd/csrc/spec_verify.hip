@@ -1870,94 +1870,87 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
 // The walk stops at its first rejection n and uses no row after it: only
 // (t_i, d_i) for i <= n, and t_g when every draft is accepted ("Speculative
 // decoding", mhtirogla.ai, "How it works" steps 3-4; tusharamrit, the
-// acceptance loop of the proof).  This kernel reads the rows position by
-// position: every workgroup of a row's group loads its slice of t_i and d_i,
-// publishes their (m, S), waits for the group's pairs of those two rows,
-// merges them and runs the test at i -- the same test, from the same merged
-// statistics, as the one-pass kernel -- and goes on to position i + 1 only
-// when x_i is accepted.  A rejection draws from the pair still in registers.
-// Each position costs a group hand-off; in exchange no row after the stop is
-// read at all.
+// acceptance loop of the proof).  This kernel reads the rows a few positions
+// at a time: every workgroup of a row's group loads its slices of the rows of
+// positions [i, j), publishes their (m, S), waits for the group's pairs of
+// those rows, merges them and runs the tests at i, i + 1, ... -- the same
+// tests, from the same merged statistics, as the one-pass kernel -- and reads
+// the next positions only when all of [i, j) are accepted.  A rejection draws
+// from the pair still in registers.  Each group of positions costs one
+// hand-off between the group's workgroups; no row after the stop's group of
+// positions is read.  The groups are position 0 alone (every row reads it,
+// and the first test is the one most often failed), then kChunk positions.
+constexpr int kChunk = 2;
 
-// Merges the staged pairs of k <= 2 rows (stage[j * nc + c]) into L.M / L.S
-// at rows ra (j = 0) and rb (j = 1), with the reduction of the one-pass merge
-// (so a row's merged pair is the same bits in both kernels).  Wave 0.
+// The vocabulary rows of a group of positions starting at i: t_i, d_i,
+// t_{i+1}, d_{i+1}, ... (no d_g), k of them.
+struct RowSet {
+  int i, g, k;
+  __device__ int row(int j) const { return (j & 1) ? g + 1 + i + (j >> 1) : i + (j >> 1); }
+};
+
+// Merges the staged pairs of the rows of `rs` (row j's slice c at
+// stage[j * nc + c]) into L.M / L.S, with the reduction of the one-pass merge
+// (so a row's merged pair is the same bits in both kernels).
 template <int LPR>
-__device__ void merge_two(const Args& a, Lds& L, int k, int nc, int ra, int rb) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane / LPR, c = lane % LPR;
-  const bool have = j < k && c < nc;
+__device__ void merge_set(const Args& a, Lds& L, const RowSet& rs, int nc) {
+  static_assert(LPR * 2 * kChunk <= kThreads, "the workgroup merges every row of a set at once");
+  const int j = threadIdx.x / LPR, c = threadIdx.x % LPR;
+  const bool have = j < rs.k && c < nc;
   const uint64_t st = have ? L.sm.stage[j * nc + c] : 0;
   float m = have ? lo_f(st) : NEG_INF, s = have ? hi_f(st) : 0.f;
   group_ms<LPR>(m, s, a.k2);
-  if (c == 0 && j < k) {
-    const int r = j == 0 ? ra : rb;
-    L.M[r] = m, L.S[r] = s;
-  }
+  if (c == 0 && j < rs.k) L.M[rs.row(j)] = m, L.S[rs.row(j)] = s;
 }
 
-__device__ void merge_two_wide(const Args& a, Lds& L, int k, int nc, int ra, int rb) {
+__device__ void merge_set_wide(const Args& a, Lds& L, const RowSet& rs, int nc) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (w >= k) return;
-  const uint64_t* st = &L.sm.stage[w * nc];
-  float m = NEG_INF, s = 0.f;
-  for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
-  wave_ms_dpp(m, s, a.k2);
-  if (lane == 0) {
-    const int r = w == 0 ? ra : rb;
-    L.M[r] = m, L.S[r] = s;
+  for (int j = w; j < rs.k; j += kWaves) {
+    const uint64_t* st = &L.sm.stage[j * nc];
+    float m = NEG_INF, s = 0.f;
+    for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
+    wave_ms_dpp(m, s, a.k2);
+    if (lane == 0) L.M[rs.row(j)] = m, L.S[rs.row(j)] = s;
   }
 }
 
-// This workgroup's (m, S) of its slices of rows ra (and rb when k = 2), as
-// per-wave partials in L.sm.wm / L.sm.ws.
+// This workgroup's (m, S) of its slice of row r, as per-wave partials in
+// L.sm.wm / L.sm.ws.
 template <int DT, int R, bool AL>
-__device__ void slice_pairs(const Args& a, Lds& L, const Slice<DT, R>& st, const Geom& gt,
-                            const Slice<DT, R>& sd, const Geom& gd, int k, int ra, int rb) {
+__device__ void slice_pair(const Args& a, Lds& L, const Slice<DT, R>& s, const Geom& g, int r) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float m, sm;
-  wave_slice_ms<DT, R, AL, false>(st, gt, a.k2, NEG_INF, m, sm);
-  if (lane == 0) L.sm.wm[ra][w] = m, L.sm.ws[ra][w] = sm;
-  if (k == 2) {
-    wave_slice_ms<DT, R, AL, false>(sd, gd, a.k2, NEG_INF, m, sm);
-    if (lane == 0) L.sm.wm[rb][w] = m, L.sm.ws[rb][w] = sm;
-  }
+  wave_slice_ms<DT, R, AL, false>(s, g, a.k2, NEG_INF, m, sm);
+  if (lane == 0) L.sm.wm[r][w] = m, L.sm.ws[r][w] = sm;
 }
 
-// Publishes this workgroup's pairs of rows ra (and rb): the four waves'
-// partials merged in a fixed order.
-__device__ void publish_rows(const Args& a, Lds& L, int b, int c, int k, int ra, int rb) {
-  const int t = threadIdx.x;
+// Publishes this workgroup's pairs of the rows of `rs` (the four waves'
+// partials merged in a fixed order), waits for the group's pairs of those
+// rows and merges them into L.M / L.S.
+__device__ void exchange_set(const Args& a, Lds& L, int b, int c, const RowSet& rs) {
+  const int t = threadIdx.x, nc = a.NC;
   __syncthreads();
-  if (t < k) {
-    const int r = t == 0 ? ra : rb;
+  if (t < rs.k) {
+    const int r = rs.row(t);
     float m = L.sm.wm[r][0], sm = L.sm.ws[r][0];
     for (int q = 1; q < kWaves; ++q) ms_merge(m, sm, L.sm.wm[r][q], L.sm.ws[r][q], a.k2);
-    put64(&a.part[((int64_t)b * a.NC + c) * a.NR + r], pack2(m, sm));
+    put64(&a.part[((int64_t)b * nc + c) * a.NR + r], pack2(m, sm));
   }
-}
-
-// Waits for the group's pairs of rows ra (and rb) and merges them into
-// L.M / L.S.
-__device__ void gather_rows(const Args& a, Lds& L, int b, int k, int ra, int rb) {
-  const int t = threadIdx.x, nc = a.NC;
   const uint64_t* base = a.part + (int64_t)b * nc * a.NR;
-  for (int q = t; q < k * nc; q += kThreads) {
-    const int r = q < nc ? ra : rb, cc = q < nc ? q : q - nc;
-    L.sm.stage[q] = poll64(a, &base[(int64_t)cc * a.NR + r], &L.bad);
+  for (int q = t; q < rs.k * nc; q += kThreads) {
+    const int j = q / nc, cc = q % nc;
+    L.sm.stage[q] = poll64(a, &base[(int64_t)cc * a.NR + rs.row(j)], &L.bad);
   }
   __syncthreads();
   if (nc <= 16) {
-    if (t < 64) {
-      if (nc <= 4)
-        merge_two<4>(a, L, k, nc, ra, rb);
-      else if (nc <= 8)
-        merge_two<8>(a, L, k, nc, ra, rb);
-      else
-        merge_two<16>(a, L, k, nc, ra, rb);
-    }
+    if (nc <= 4)
+      merge_set<4>(a, L, rs, nc);
+    else if (nc <= 8)
+      merge_set<8>(a, L, rs, nc);
+    else
+      merge_set<16>(a, L, rs, nc);
   } else {
-    merge_two_wide(a, L, k, nc, ra, rb);
+    merge_set_wide(a, L, rs, nc);
   }
   __syncthreads();
 }
@@ -1985,38 +1978,42 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   // x_i, u_i and the logits at x_i, all in flight while the first rows load
   Gathered in = gather_small<SPEC_MODE_SAMPLE>(a, b, g);
   gather_logits<DT, SPEC_MODE_SAMPLE, false>(a, b, g, in);
-  Slice<DT, R> st, sd;
-  Geom gt, gd;
+  // a ring of two row slices: the rows of a group of positions go through
+  // it in order (t_i, d_i, t_{i+1}, d_{i+1}, ...: t rows in sa, d rows in
+  // sb), each loaded while the one before it is reduced
+  Slice<DT, R> sa, sb;
+  Geom ga, gb;
+  auto load_row = [&](int r, Slice<DT, R>& s, Geom& gg) {
+    const char* p = row_of<DT>(a, b, g, r) + (int64_t)lo * E::kBytes;
+    gg = geom_of<DT, AL>(p, len);
+    load_slice<DT, R, AL>(p, gg, s);
+  };
   int n = 0, verdict = 0;  // verdict: 0 accepted, 1 rejected, 2 sentinel
-  // position i's rows: t_i (t_g at i = g) and d_i (i < g)
-  auto issue = [&](int i) {
-    const char* tp = row_of<DT>(a, b, g, i) + (int64_t)lo * E::kBytes;
-    gt = geom_of<DT, AL>(tp, len);
-    load_slice<DT, R, AL>(tp, gt, st);
-    if (i < g) {
-      const char* dp = row_of<DT>(a, b, g, g + 1 + i) + (int64_t)lo * E::kBytes;
-      gd = geom_of<DT, AL>(dp, len);
-      load_slice<DT, R, AL>(dp, gd, sd);
+  bool reread = false;     // the stop's rows have left the ring
+  for (int i = 0;;) {
+    const int j = min(i == 0 ? 1 : i + kChunk, g + 1);  // positions [i, j)
+    RowSet rs;
+    rs.i = i, rs.g = g;
+    rs.k = 2 * (j - i) - (j > g ? 1 : 0);  // no d_g
+    load_row(rs.row(0), sa, ga);
+    if (rs.k > 1) load_row(rs.row(1), sb, gb);
+    for (int q = 0; q < rs.k; q += 2) {
+      slice_pair<DT, R, AL>(a, L, sa, ga, rs.row(q));
+      if (q + 2 < rs.k) load_row(rs.row(q + 2), sa, ga);
+      if (q + 1 < rs.k) {
+        slice_pair<DT, R, AL>(a, L, sb, gb, rs.row(q + 1));
+        if (q + 3 < rs.k) load_row(rs.row(q + 3), sb, gb);
+      }
     }
-  };
-  auto pairs_of = [&](int i) {
-    issue(i);
-    slice_pairs<DT, R, AL>(a, L, st, gt, sd, gd, i < g ? 2 : 1, i, g + 1 + i);
-  };
-  pairs_of(0);
-  publish_rows(a, L, b, c, g > 0 ? 2 : 1, 0, g + 1);
-  for (int i = 0;; ++i) {
-    const bool bonus = i == g;
-    const int rt = i, rd = g + 1 + i;
-    gather_rows(a, L, b, bonus ? 1 : 2, rt, rd);
+    exchange_set(a, L, b, c, rs);
     if (L.bad) {  // a slice's pairs never arrived (cannot happen in a correct launch)
       write_sentinel(a, b);
       row_exit(a, L, b, nrows);
       return;
     }
     if (t < 64) {
-      if (c == 0 && a.pr_m && lane < (bonus ? 1 : 2)) {
-        const int r = lane == 0 ? rt : rd;
+      if (c == 0 && a.pr_m && lane < rs.k) {
+        const int r = rs.row(lane);
         const int slot = probe_slot(a, g, r);
         const float mm = L.M[r];
         a.pr_m[(int64_t)b * (2 * a.G + 1) + slot] = mm;
@@ -2024,38 +2021,44 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
           a.pr_s[(int64_t)b * (2 * a.G + 1) + slot] =
               mm != NEG_INF ? L.S[r] * ex2(-fmaf(mm, a.k2, -ref_of(mm, a.k2))) : L.S[r];
       }
-      int v = 1;  // bonus: the walk ends here
-      if (!bonus) {
-        // the test at i, in lane i (which holds x_i, u_i and the logits at x_i)
-        const bool valid = (unsigned)in.x < (unsigned)a.V;
-        bool fail = true;
-        if (valid) {
-          const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.M[rt], a.k2))) / L.S[rt];
-          const float q = ex2(fmaf(in.dv, a.k2, -ref_of(L.M[rd], a.k2))) / L.S[rd];
-          if (c == 0 && lane == i && a.pr_px) {
-            a.pr_px[(int64_t)b * a.G + i] = p;
-            a.pr_qx[(int64_t)b * a.G + i] = q;
-          }
-          fail = !(in.u * q < p);
+      // the tests at i .. j - 1 (lane p holds x_p, u_p and the logits at x_p);
+      // the first that fails, or the bonus position g, ends the walk
+      const bool valid = (unsigned)in.x < (unsigned)a.V;
+      const bool mine = lane >= i && lane < j && lane < g;
+      bool fail = true;
+      if (mine && valid) {
+        const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.M[lane], a.k2))) / L.S[lane];
+        const float q =
+            ex2(fmaf(in.dv, a.k2, -ref_of(L.M[g + 1 + lane], a.k2))) / L.S[g + 1 + lane];
+        if (c == 0 && a.pr_px) {
+          a.pr_px[(int64_t)b * a.G + lane] = p;
+          a.pr_qx[(int64_t)b * a.G + lane] = q;
         }
-        v = __builtin_amdgcn_readlane(fail ? (valid ? 1 : 2) : 0, i);
+        fail = !(in.u * q < p);
       }
-      // a row the walk uses must have a finite logit (a dead p_i or q_i
-      // fails the test at i, so only the stop position can hold one)
-      if (v == 1 && (L.M[rt] == NEG_INF || (!bonus && L.M[rd] == NEG_INF))) v = 2;
-      if (t == 0) L.pick = v;
+      const unsigned long long stop = __ballot((mine && fail) || lane == g);
+      const unsigned long long win = j >= 64 ? ~0ull : ((1ull << j) - 1);
+      const unsigned long long hit = stop & win & ~((1ull << i) - 1);
+      int v = 0, at = j;
+      if (hit) {
+        at = __ffsll((long long)hit) - 1;
+        const bool ok = at == g || __builtin_amdgcn_readlane(valid ? 1 : 0, at) != 0;
+        v = ok ? 1 : 2;
+        // a row the walk uses must have a finite logit (a dead p_i or q_i
+        // fails the test at i, so only the stop position can hold one)
+        if (v == 1 && (L.M[at] == NEG_INF || (at < g && L.M[g + 1 + at] == NEG_INF))) v = 2;
+      }
+      if (t == 0) L.pick = v, L.last = at;
     }
     __syncthreads();
     verdict = L.pick;
     if (verdict != 0) {
-      n = i;
+      n = L.last;
+      // the ring holds the rows of the group's last position only
+      reread = n < j - 1;
       break;
     }
-    // x_i accepted: position i + 1 (reading it any earlier, during this
-    // hand-off, measured slower: the reads of rows that stop here compete
-    // with every other row's)
-    pairs_of(i + 1);
-    publish_rows(a, L, b, c, i + 1 < g ? 2 : 1, i + 1, g + 2 + i);
+    i = j;
   }
   const bool sentinel = verdict == 2;
   if (t < 64) {
@@ -2089,14 +2092,18 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
     row_exit(a, L, b, nrows);
     return;
   }
-  if (dc.resid && !AL && gd.head != gt.head) {
+  if (reread) {  // t_n and d_n again (read a few microseconds ago: cached)
+    load_row(n, sa, ga);
+    if (n < g) load_row(g + 1 + n, sb, gb);
+  }
+  if (dc.resid && !AL && gb.head != ga.head) {
     // the weights pair element j of both rows: d_n in t_n's register layout
     const char* dp = row_of<DT>(a, b, g, g + 1 + n) + (int64_t)lo * E::kBytes;
-    load_slice_as<DT, R>(dp, gt, sd);
+    load_slice_as<DT, R>(dp, ga, sb);
   }
-  if (!dc.resid) sd = st;
+  if (!dc.resid) sb = sa;
   __builtin_amdgcn_s_setprio(1);
-  draw_body<DT, R, false, false, AL, true>(a, L, b, c, g, lo, nrows, dc, st, sd, gt);
+  draw_body<DT, R, false, false, AL, true>(a, L, b, c, g, lo, nrows, dc, sa, sb, ga);
 }
 
 // ------------------------------------------------------------------ filtering
