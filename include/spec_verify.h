@@ -156,11 +156,11 @@ int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
  *                   (GREEDY: out_m only, out_s holds the argmax as float;
  *                   GREEDY and POINT leave the draft slots untouched)
  *   In unfiltered SAMPLE calls without SPEC_TUNE_ONE_PASS the rows are read
- *   a position (0) or two (1-2, 3-4, ...) at a time up to the walk's stop n,
- *   and only what was read is reported: out_px / out_qx for the positions
- *   read (i <= n, and n + 1 when n is the first of a pair), out_m / out_s for
- *   their rows t_i and d_i (t_g when it was read); the other entries are
- *   untouched.
+ *   in groups of positions (0; 1-2; then up to four at a time) up to the
+ *   group holding the walk's stop n, and only what was read is reported:
+ *   out_px / out_qx for the positions of the groups read (which may run past
+ *   n), out_m / out_s for their rows t_i and d_i (t_g when it was read); the
+ *   other entries are untouched.
  *   out_f_lo,       fp32 [B]: the CDF bracket of the drawn token j, i.e. the
  *   out_f_hi        normalised cumulative weight of the tokens before j and
  *                   through j (u lies in [f_lo, f_hi) unless the fallback

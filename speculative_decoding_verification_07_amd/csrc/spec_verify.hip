@@ -1879,8 +1879,10 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
 // from the pair still in registers.  Each group of positions costs one
 // hand-off between the group's workgroups; no row after the stop's group of
 // positions is read.  The groups are position 0 alone (every row reads it,
-// and the first test is the one most often failed), then kChunk positions.
-constexpr int kChunk = 2;
+// and the first test is the one most often failed), then 2, then 4
+// positions (kMaxSpan): a row that keeps accepting needs fewer hand-offs,
+// one that stops early reads little past its stop.
+constexpr int kMaxSpan = 4;
 
 // The vocabulary rows of a group of positions starting at i: t_i, d_i,
 // t_{i+1}, d_{i+1}, ... (no d_g), k of them.
@@ -1894,7 +1896,7 @@ struct RowSet {
 // (so a row's merged pair is the same bits in both kernels).
 template <int LPR>
 __device__ void merge_set(const Args& a, Lds& L, const RowSet& rs, int nc) {
-  static_assert(LPR * 2 * kChunk <= kThreads, "the workgroup merges every row of a set at once");
+  static_assert(LPR * 2 * kMaxSpan <= kThreads, "the workgroup merges every row of a set at once");
   const int j = threadIdx.x / LPR, c = threadIdx.x % LPR;
   const bool have = j < rs.k && c < nc;
   const uint64_t st = have ? L.sm.stage[j * nc + c] : 0;
@@ -1990,8 +1992,11 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   };
   int n = 0, verdict = 0;  // verdict: 0 accepted, 1 rejected, 2 sentinel
   bool reread = false;     // the stop's rows have left the ring
+  // a group's staged pairs (2 rows per position, NC slices each) fit kStage
+  const int cap = min(kMaxSpan, kStage / (2 * a.NC));
+  int span = 1;
   for (int i = 0;;) {
-    const int j = min(i == 0 ? 1 : i + kChunk, g + 1);  // positions [i, j)
+    const int j = min(i + span, g + 1);  // positions [i, j)
     RowSet rs;
     rs.i = i, rs.g = g;
     rs.k = 2 * (j - i) - (j > g ? 1 : 0);  // no d_g
@@ -2059,6 +2064,7 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
       break;
     }
     i = j;
+    span = min(2 * span, cap);
   }
   const bool sentinel = verdict == 2;
   if (t < 64) {
