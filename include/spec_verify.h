@@ -42,7 +42,15 @@
  * CU count picks between launch variants that differ in speed only (wave
  * priorities when the whole grid fits on the device at once); results are
  * the same.  Calls on distinct workspaces may run concurrently; two calls
- * that share a workspace must be ordered (same stream).
+ * that share a workspace must be ordered (same stream).  A call's
+ * workgroups wait only on workgroups of their own batch row, whose ids are
+ * consecutive; one call alone always makes progress.  Concurrent calls
+ * whose grids together exceed the device's workgroup slots (four per CU)
+ * could, in principle, each hold slots that the other's unstarted row
+ * members need: every wait is bounded (about 0.2 s), and a row whose wait
+ * runs out gets the sentinel and sets diagnostic bit 0 -- never a wrong
+ * token.  Overlapping calls whose grids fit the device together cannot
+ * meet this.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -155,7 +163,7 @@ int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
  *                   largest raw logit and S = sum_j exp((l_j - max) / T)
  *                   (GREEDY: out_m only, out_s holds the argmax as float;
  *                   GREEDY and POINT leave the draft slots untouched)
- *   In unfiltered SAMPLE calls without SPEC_TUNE_ONE_PASS the rows are read
+ *   In SAMPLE calls without SPEC_TUNE_ONE_PASS the rows are read
  *   in groups of positions (0; 1-2; then up to four at a time) up to the
  *   group holding the walk's stop n, and only what was read is reported:
  *   out_px / out_qx for the positions of the groups read (which may run past
@@ -246,8 +254,8 @@ int spec_verify_plan(int B, int gamma_max, int V, int dtype, int mode, int64_t* 
 
 /* Flags of spec_verify_tune. */
 enum spec_tune_flags {
-  /* Unfiltered SAMPLE calls stream every vocabulary row of a batch row in one
-   * pass and decide all positions at once, instead of the default: reading
+  /* SAMPLE calls (filtered or not) stream every vocabulary row of a batch row
+   * in one pass and decide all positions at once, instead of the default: reading
    * the rows position by position, (t_i, d_i) for i = 0, 1, ..., and
    * stopping at the walk's first rejection (the rows after it are never
    * used), at the cost of one hand-off between a row's workgroups per

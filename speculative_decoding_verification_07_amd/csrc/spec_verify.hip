@@ -1918,24 +1918,27 @@ __device__ void merge_set_wide(const Args& a, Lds& L, const RowSet& rs, int nc) 
 
 // This workgroup's (m, S) of its slice of row r, as per-wave partials in
 // L.sm.wm / L.sm.ws.
-template <int DT, int R, bool AL>
-__device__ void slice_pair(const Args& a, Lds& L, const Slice<DT, R>& s, const Geom& g, int r) {
+template <int DT, int R, bool AL, bool FILT>
+__device__ void slice_pair(const Args& a, Lds& L, const Slice<DT, R>& s, const Geom& g, int r,
+                           float tau) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float m, sm;
-  wave_slice_ms<DT, R, AL, false>(s, g, a.k2, NEG_INF, m, sm);
+  wave_slice_ms<DT, R, AL, FILT>(s, g, a.k2, tau, m, sm);
   if (lane == 0) L.sm.wm[r][w] = m, L.sm.ws[r][w] = sm;
 }
 
 // Publishes this workgroup's pairs of the rows of `rs` (the four waves'
 // partials merged in a fixed order), waits for the group's pairs of those
-// rows and merges them into L.M / L.S.
-__device__ void exchange_set(const Args& a, Lds& L, int b, int c, const RowSet& rs) {
+// rows and merges them into L.M / L.S.  Filtered: a slice whose entries are
+// all cut publishes the identity (-inf, 0), as in the one-pass kernel.
+__device__ void exchange_set(const Args& a, Lds& L, int b, int c, const RowSet& rs, bool filt) {
   const int t = threadIdx.x, nc = a.NC;
   __syncthreads();
   if (t < rs.k) {
     const int r = rs.row(t);
     float m = L.sm.wm[r][0], sm = L.sm.ws[r][0];
     for (int q = 1; q < kWaves; ++q) ms_merge(m, sm, L.sm.wm[r][q], L.sm.ws[r][q], a.k2);
+    if (filt && sm == 0.f) m = NEG_INF;
     put64(&a.part[((int64_t)b * nc + c) * a.NR + r], pack2(m, sm));
   }
   const uint64_t* base = a.part + (int64_t)b * nc * a.NR;
@@ -1957,7 +1960,7 @@ __device__ void exchange_set(const Args& a, Lds& L, int b, int c, const RowSet& 
   __syncthreads();
 }
 
-template <int DT, int R, bool AL>
+template <int DT, int R, bool AL, bool FILT>
 __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(Args a) {
   using E = Elt<DT>;
   __shared__ Lds L;
@@ -1979,7 +1982,10 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   __builtin_amdgcn_s_setprio(3);
   // x_i, u_i and the logits at x_i, all in flight while the first rows load
   Gathered in = gather_small<SPEC_MODE_SAMPLE>(a, b, g);
-  gather_logits<DT, SPEC_MODE_SAMPLE, false>(a, b, g, in);
+  gather_logits<DT, SPEC_MODE_SAMPLE, FILT>(a, b, g, in);
+  // filtered rows: the threshold of vocabulary row r (entries below weigh 0)
+  const float* thr = FILT ? a.thr + (int64_t)b * (2 * a.G + 1) : nullptr;
+  auto tau_of = [&](int r) { return FILT ? thr[probe_slot(a, g, r)] : NEG_INF; };
   // a ring of two row slices: the rows of a group of positions go through
   // it in order (t_i, d_i, t_{i+1}, d_{i+1}, ...: t rows in sa, d rows in
   // sb), each loaded while the one before it is reduced
@@ -2003,14 +2009,14 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
     load_row(rs.row(0), sa, ga);
     if (rs.k > 1) load_row(rs.row(1), sb, gb);
     for (int q = 0; q < rs.k; q += 2) {
-      slice_pair<DT, R, AL>(a, L, sa, ga, rs.row(q));
+      slice_pair<DT, R, AL, FILT>(a, L, sa, ga, rs.row(q), tau_of(rs.row(q)));
       if (q + 2 < rs.k) load_row(rs.row(q + 2), sa, ga);
       if (q + 1 < rs.k) {
-        slice_pair<DT, R, AL>(a, L, sb, gb, rs.row(q + 1));
+        slice_pair<DT, R, AL, FILT>(a, L, sb, gb, rs.row(q + 1), tau_of(rs.row(q + 1)));
         if (q + 3 < rs.k) load_row(rs.row(q + 3), sb, gb);
       }
     }
-    exchange_set(a, L, b, c, rs);
+    exchange_set(a, L, b, c, rs, FILT);
     if (L.bad) {  // a slice's pairs never arrived (cannot happen in a correct launch)
       write_sentinel(a, b);
       row_exit(a, L, b, nrows);
@@ -2109,7 +2115,7 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   }
   if (!dc.resid) sb = sa;
   __builtin_amdgcn_s_setprio(1);
-  draw_body<DT, R, false, false, AL, true>(a, L, b, c, g, lo, nrows, dc, sa, sb, ga);
+  draw_body<DT, R, false, FILT, AL, true>(a, L, b, c, g, lo, nrows, dc, sa, sb, ga);
 }
 
 // ------------------------------------------------------------------ filtering
@@ -2655,14 +2661,29 @@ void launch_r(int R, bool prio, dim3 grid, hipStream_t s, const Args& a) {
     hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL, FILT, false>), grid, dim3(kThreads), 0, s, a);
 }
 
-template <int DT, bool AL>
+template <int DT, bool AL, bool FILT>
 void launch_rows_r(int R, dim3 grid, hipStream_t s, const Args& a) {
   if (R == 1)
-    hipLaunchKernelGGL((verify_rows_kernel<DT, 1, AL>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_rows_kernel<DT, 1, AL, FILT>), grid, dim3(kThreads), 0, s, a);
   else if (R == 2)
-    hipLaunchKernelGGL((verify_rows_kernel<DT, 2, AL>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_rows_kernel<DT, 2, AL, FILT>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((verify_rows_kernel<DT, 4, AL>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_rows_kernel<DT, 4, AL, FILT>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <int DT>
+void launch_rows(int R, bool al, bool filt, dim3 grid, hipStream_t s, const Args& a) {
+  if (filt) {
+    if (al)
+      launch_rows_r<DT, true, true>(R, grid, s, a);
+    else
+      launch_rows_r<DT, false, true>(R, grid, s, a);
+  } else {
+    if (al)
+      launch_rows_r<DT, true, false>(R, grid, s, a);
+    else
+      launch_rows_r<DT, false, false>(R, grid, s, a);
+  }
 }
 
 // greedy never filters (the filters keep the largest logit)
@@ -2766,20 +2787,13 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
     const int hs = hip_status(hipGetLastError());
     if (hs != SPEC_OK) return hs;
   }
-  // unfiltered sampling reads the rows position by position, up to the
-  // walk's stop (unless the one-pass stream is asked for)
-  if (sample && !filt && !(g_tune.flags & SPEC_TUNE_ONE_PASS)) {
-    if (dtype == SPEC_DTYPE_BF16) {
-      if (al)
-        launch_rows_r<SPEC_DTYPE_BF16, true>(p.R, grid, s, a);
-      else
-        launch_rows_r<SPEC_DTYPE_BF16, false>(p.R, grid, s, a);
-    } else {
-      if (al)
-        launch_rows_r<SPEC_DTYPE_F32, true>(p.R, grid, s, a);
-      else
-        launch_rows_r<SPEC_DTYPE_F32, false>(p.R, grid, s, a);
-    }
+  // sampling reads the rows position by position, up to the walk's stop
+  // (unless the one-pass stream is asked for)
+  if (sample && !(g_tune.flags & SPEC_TUNE_ONE_PASS)) {
+    if (dtype == SPEC_DTYPE_BF16)
+      launch_rows<SPEC_DTYPE_BF16>(p.R, al, filt, grid, s, a);
+    else
+      launch_rows<SPEC_DTYPE_F32>(p.R, al, filt, grid, s, a);
     return hip_status(hipGetLastError());
   }
   if (dtype == SPEC_DTYPE_BF16) {

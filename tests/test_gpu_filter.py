@@ -33,9 +33,9 @@ def torch():
 
 def _streams_all(case):
     """Whether the call runs the one-pass kernel, which reports every row's
-    statistics: a filter that cuts something, or point-mass drafts."""
-    k, p = case.extra.get("top_k", 0), case.extra.get("top_p", 1.0)
-    return case.mode == "point" or (0 < k < case.V) or p < 1.0
+    statistics: point-mass drafts (sampling reads the rows position by
+    position, filtered or not, and reports the rows it read)."""
+    return case.mode == "point"
 
 
 def _check(case, torch, **kw):
