@@ -11,12 +11,12 @@ the 256 MB Infinity Cache.
 Prints one JSON line.  `value` is verified rows per second; the roofline
 object gives the dominant (only) kernel's achieved HBM rate from the
 compulsory logit bytes (every row of the call: (2 g_b + 1) V e per batch row
-when sampling) and its event-timed average launch duration.  Sampling runs
-the kernel that reads the rows position by position and stops
-at the walk's first rejection, so it reads fewer bytes than that:
-`walk_bytes_per_step` counts the rows the walk uses ((t_i, d_i) for i <= n,
-t_g after g acceptances), and --one-pass times the kernel that streams every
-row instead.
+when sampling) and its event-timed average launch duration.  Every mode runs
+the kernel that reads the rows position by position and stops at the walk's
+first rejection, so it reads fewer bytes than that: `walk_bytes_per_step`
+counts the rows the walk uses (t_i, and d_i when sampling, for i <= n; t_g
+after g acceptances), and --one-pass times the kernel that streams every row
+instead.
 
 With --top-k / --top-p a step is the filtered verify: the threshold kernel,
 then the verify on the filtered rows (two launches); the draft tokens are
@@ -86,8 +86,8 @@ def parse():
                     help="also run the reference copy kernel (counter calibration)")
     ap.add_argument("--tune", default="", help="vectors[,target_workgroups]")
     ap.add_argument("--one-pass", action="store_true",
-                    help="sampling streams every row in one pass instead of reading the "
-                         "rows position by position")
+                    help="stream every row in one pass instead of reading the rows "
+                         "position by position")
     return ap.parse_args()
 
 
@@ -500,9 +500,8 @@ def main():
     # is the back-to-back time per step (event pairs around single launches
     # add their own overhead and are reported separately)
     kern_s = ms_per_step * 1e-3
-    # sampling reads the rows position by position (its own kernel)
-    by_rows = mode == sv.SAMPLE and not args.one_pass
-    kernel_name = "verify_rows_kernel" if by_rows else "verify_kernel"
+    # every mode reads the rows position by position unless --one-pass
+    kernel_name = "verify_kernel" if args.one_pass else "verify_rows_kernel"
     if filter_us is not None:
         # two launches per step: the longer one is the dominant kernel
         verify_s = kern_s - filter_us * 1e-6

@@ -163,12 +163,12 @@ int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
  *                   largest raw logit and S = sum_j exp((l_j - max) / T)
  *                   (GREEDY: out_m only, out_s holds the argmax as float;
  *                   GREEDY and POINT leave the draft slots untouched)
- *   In SAMPLE calls without SPEC_TUNE_ONE_PASS the rows are read
- *   in groups of positions (0; 1-2; then up to four at a time) up to the
- *   group holding the walk's stop n, and only what was read is reported:
- *   out_px / out_qx for the positions of the groups read (which may run past
- *   n), out_m / out_s for their rows t_i and d_i (t_g when it was read); the
- *   other entries are untouched.
+ *   Without SPEC_TUNE_ONE_PASS the rows are read in groups of positions
+ *   (0; 1-2; then up to four at a time) up to the group holding the walk's
+ *   stop n, and only what was read is reported: out_px / out_qx for the
+ *   positions of the groups read (which may run past n), out_m / out_s for
+ *   their rows t_i (and d_i in SAMPLE; t_g when it was read); the other
+ *   entries are untouched.
  *   out_f_lo,       fp32 [B]: the CDF bracket of the drawn token j, i.e. the
  *   out_f_hi        normalised cumulative weight of the tokens before j and
  *                   through j (u lies in [f_lo, f_hi) unless the fallback
@@ -254,12 +254,12 @@ int spec_verify_plan(int B, int gamma_max, int V, int dtype, int mode, int64_t* 
 
 /* Flags of spec_verify_tune. */
 enum spec_tune_flags {
-  /* SAMPLE calls (filtered or not) stream every vocabulary row of a batch row
-   * in one pass and decide all positions at once, instead of the default: reading
-   * the rows position by position, (t_i, d_i) for i = 0, 1, ..., and
-   * stopping at the walk's first rejection (the rows after it are never
-   * used), at the cost of one hand-off between a row's workgroups per
-   * position.  Results are the same either way. */
+  /* Calls of every mode (filtered or not) stream every vocabulary row of a
+   * batch row in one pass and decide all positions at once, instead of the
+   * default: reading the rows position by position (t_i, and d_i in SAMPLE,
+   * for i = 0, 1, ...) and stopping at the walk's first rejection (the rows
+   * after it are never used), at the cost of one hand-off between a row's
+   * workgroups per group of positions.  Results are the same either way. */
   SPEC_TUNE_ONE_PASS = 1
 };
 

@@ -127,8 +127,8 @@ TUNE_ONE_PASS = 1  # SPEC_TUNE_ONE_PASS
 
 def tune(vectors: int = 0, target_workgroups: int = 0, one_pass: bool = False):
     """Process-wide launch tuning (see spec_verify_tune); no arguments
-    restores the defaults.  one_pass: sampling streams every row in one pass
-    instead of reading the rows position by position."""
+    restores the defaults.  one_pass: stream every row in one pass instead
+    of reading the rows position by position (every mode)."""
     _check(load().spec_verify_tune(vectors, target_workgroups, TUNE_ONE_PASS if one_pass else 0),
            "spec_verify_tune")
 

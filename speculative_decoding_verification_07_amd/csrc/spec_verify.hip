@@ -1544,7 +1544,7 @@ __device__ Pick slice_search(const DrawParams& d, const Slice<DT, R>& st, const 
 // holds tau = u * Z writes the token.  KNOCK (point-mass drafts): after a
 // rejection the residual max(0, p_n - q_n) with q_n the indicator of x_n is
 // p_n without x_n, drawn as the plain weights of row n with x_n set to -inf.
-__device__ void row_exit(const Args& a, Lds& L, int b, int nrows);
+__device__ void row_exit(const Args& a, Lds& L, int b, int nrows, bool draws = true);
 
 // Slot `k` of the ring, selected at run time (register by register, so that
 // the ring stays in registers).
@@ -1762,12 +1762,13 @@ __device__ void clear_pairs(const Args& a, int b, int nrows) {
     put64(&base[(int64_t)(k / nrows) * a.NR + k % nrows], 0);
 }
 
-// Every workgroup of a sampled row takes the row's exit ticket after its last
-// read of the row's entries (those loads have returned: their values were
-// used); the last one clears the entries and the counter.  Every entry was
+// Every workgroup of a row takes the row's exit ticket after its last read
+// of the row's entries (those loads have returned: their values were used);
+// the last one clears the entries and the counter, and the draw's slice sums
+// when the call draws a token (greedy workspaces hold none).  Every entry was
 // seen by every workgroup before any of them got here, so no store of the
 // call can land after the clearing.
-__device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
+__device__ void row_exit(const Args& a, Lds& L, int b, int nrows, bool draws) {
   unsigned* rc = a.ctr + (int64_t)b * kRowWords;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1778,8 +1779,10 @@ __device__ void row_exit(const Args& a, Lds& L, int b, int nrows) {
   __syncthreads();
   if (!L.last) return;
   clear_pairs(a, b, nrows);
-  uint64_t* ws = a.wsum + (int64_t)b * kWs * a.NC;
-  for (int k = threadIdx.x; k < kWs * a.NC; k += kThreads) put64(&ws[k], 0);
+  if (draws) {
+    uint64_t* ws = a.wsum + (int64_t)b * kWs * a.NC;
+    for (int k = threadIdx.x; k < kWs * a.NC; k += kThreads) put64(&ws[k], 0);
+  }
   if (threadIdx.x == 0) put_u(rc + kExit, 0u);
 }
 
@@ -1884,61 +1887,100 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
 // one that stops early reads little past its stop.
 constexpr int kMaxSpan = 4;
 
-// The vocabulary rows of a group of positions starting at i: t_i, d_i,
-// t_{i+1}, d_{i+1}, ... (no d_g), k of them.
+// The vocabulary rows of a group of positions starting at i, k of them:
+// sampling t_i, d_i, t_{i+1}, d_{i+1}, ... (no d_g); otherwise t_i, t_{i+1}, ...
+// PER: vocabulary rows per position (2 sampling, 1 otherwise), a template
+// argument so that row() folds to one of its forms.
+template <int PER>
 struct RowSet {
   int i, g, k;
-  __device__ int row(int j) const { return (j & 1) ? g + 1 + i + (j >> 1) : i + (j >> 1); }
+  __device__ int row(int j) const {
+    return PER == 2 ? ((j & 1) ? g + 1 + i + (j >> 1) : i + (j >> 1)) : i + j;
+  }
 };
 
 // Merges the staged pairs of the rows of `rs` (row j's slice c at
 // stage[j * nc + c]) into L.M / L.S, with the reduction of the one-pass merge
-// (so a row's merged pair is the same bits in both kernels).
-template <int LPR>
-__device__ void merge_set(const Args& a, Lds& L, const RowSet& rs, int nc) {
+// (so a row's merged pair is the same bits in both kernels).  Sampling and
+// point mode: (max, exp-sum) pairs; greedy: (max, argmax + 1).
+template <bool kSample, int LPR, class RS>
+__device__ void merge_set(const Args& a, Lds& L, const RS& rs, int nc) {
   static_assert(LPR * 2 * kMaxSpan <= kThreads, "the workgroup merges every row of a set at once");
   const int j = threadIdx.x / LPR, c = threadIdx.x % LPR;
   const bool have = j < rs.k && c < nc;
   const uint64_t st = have ? L.sm.stage[j * nc + c] : 0;
-  float m = have ? lo_f(st) : NEG_INF, s = have ? hi_f(st) : 0.f;
-  group_ms<LPR>(m, s, a.k2);
-  if (c == 0 && j < rs.k) L.M[rs.row(j)] = m, L.S[rs.row(j)] = s;
-}
-
-__device__ void merge_set_wide(const Args& a, Lds& L, const RowSet& rs, int nc) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int j = w; j < rs.k; j += kWaves) {
-    const uint64_t* st = &L.sm.stage[j * nc];
-    float m = NEG_INF, s = 0.f;
-    for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
-    wave_ms_dpp(m, s, a.k2);
-    if (lane == 0) L.M[rs.row(j)] = m, L.S[rs.row(j)] = s;
+  if (kSample) {
+    float m = have ? lo_f(st) : NEG_INF, s = have ? hi_f(st) : 0.f;
+    group_ms<LPR>(m, s, a.k2);
+    if (c == 0 && j < rs.k) L.M[rs.row(j)] = m, L.S[rs.row(j)] = s;
+  } else {
+    float v = have ? lo_f(st) : NEG_INF;
+    int i = have ? (int)__float_as_uint(hi_f(st)) - 1 : 0x7fffffff;
+    group_am<LPR>(v, i);
+    if (c == 0 && j < rs.k) L.M[rs.row(j)] = v, L.S[rs.row(j)] = __int_as_float(i);
   }
 }
 
-// This workgroup's (m, S) of its slice of row r, as per-wave partials in
-// L.sm.wm / L.sm.ws.
-template <int DT, int R, bool AL, bool FILT>
-__device__ void slice_pair(const Args& a, Lds& L, const Slice<DT, R>& s, const Geom& g, int r,
-                           float tau) {
+template <bool kSample, class RS>
+__device__ void merge_set_wide(const Args& a, Lds& L, const RS& rs, int nc) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float m, sm;
-  wave_slice_ms<DT, R, AL, FILT>(s, g, a.k2, tau, m, sm);
-  if (lane == 0) L.sm.wm[r][w] = m, L.sm.ws[r][w] = sm;
+  for (int j = w; j < rs.k; j += kWaves) {
+    const uint64_t* st = &L.sm.stage[j * nc];
+    if (kSample) {
+      float m = NEG_INF, s = 0.f;
+      for (int c = lane; c < nc; c += 64) ms_merge(m, s, lo_f(st[c]), hi_f(st[c]), a.k2);
+      wave_ms_dpp(m, s, a.k2);
+      if (lane == 0) L.M[rs.row(j)] = m, L.S[rs.row(j)] = s;
+    } else {
+      float v = NEG_INF;
+      int i = 0x7fffffff;
+      for (int c = lane; c < nc; c += 64)
+        am_merge(v, i, lo_f(st[c]), (int)__float_as_uint(hi_f(st[c])) - 1);
+      wave_am_dpp(v, i);
+      if (lane == 0) L.M[rs.row(j)] = v, L.S[rs.row(j)] = __int_as_float(i);
+    }
+  }
+}
+
+// This workgroup's statistics of its slice of row r, as per-wave partials in
+// L.sm.wm / L.sm.ws: (m, S) (sampling, point mode), (max, argmax) (greedy).
+template <int DT, int R, bool AL, bool FILT, bool kSample>
+__device__ void slice_pair(const Args& a, Lds& L, const Slice<DT, R>& s, const Geom& g, int r,
+                           float tau, int lo) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (kSample) {
+    float m, sm;
+    wave_slice_ms<DT, R, AL, FILT>(s, g, a.k2, tau, m, sm);
+    if (lane == 0) L.sm.wm[r][w] = m, L.sm.ws[r][w] = sm;
+  } else {
+    float v;
+    int ix;
+    slice_am<DT, R>(s, g, lo, v, ix);
+    wave_am_dpp(v, ix);
+    if (lane == 0) L.sm.wm[r][w] = v, L.sm.ws[r][w] = __int_as_float(ix);
+  }
 }
 
 // Publishes this workgroup's pairs of the rows of `rs` (the four waves'
 // partials merged in a fixed order), waits for the group's pairs of those
 // rows and merges them into L.M / L.S.  Filtered: a slice whose entries are
 // all cut publishes the identity (-inf, 0), as in the one-pass kernel.
-__device__ void exchange_set(const Args& a, Lds& L, int b, int c, const RowSet& rs, bool filt) {
+// Greedy words carry the argmax plus one, so that none is zero.
+template <bool kSample, class RS>
+__device__ void exchange_set(const Args& a, Lds& L, int b, int c, const RS& rs, bool filt) {
   const int t = threadIdx.x, nc = a.NC;
   __syncthreads();
   if (t < rs.k) {
     const int r = rs.row(t);
     float m = L.sm.wm[r][0], sm = L.sm.ws[r][0];
-    for (int q = 1; q < kWaves; ++q) ms_merge(m, sm, L.sm.wm[r][q], L.sm.ws[r][q], a.k2);
-    if (filt && sm == 0.f) m = NEG_INF;
+    if (kSample) {
+      for (int q = 1; q < kWaves; ++q) ms_merge(m, sm, L.sm.wm[r][q], L.sm.ws[r][q], a.k2);
+      if (filt && sm == 0.f) m = NEG_INF;
+    } else {
+      int i = __float_as_int(sm);
+      for (int q = 1; q < kWaves; ++q) am_merge(m, i, L.sm.wm[r][q], __float_as_int(L.sm.ws[r][q]));
+      sm = __int_as_float(i + 1);
+    }
     put64(&a.part[((int64_t)b * nc + c) * a.NR + r], pack2(m, sm));
   }
   const uint64_t* base = a.part + (int64_t)b * nc * a.NR;
@@ -1949,19 +1991,23 @@ __device__ void exchange_set(const Args& a, Lds& L, int b, int c, const RowSet& 
   __syncthreads();
   if (nc <= 16) {
     if (nc <= 4)
-      merge_set<4>(a, L, rs, nc);
+      merge_set<kSample, 4>(a, L, rs, nc);
     else if (nc <= 8)
-      merge_set<8>(a, L, rs, nc);
+      merge_set<kSample, 8>(a, L, rs, nc);
     else
-      merge_set<16>(a, L, rs, nc);
+      merge_set<kSample, 16>(a, L, rs, nc);
   } else {
-    merge_set_wide(a, L, rs, nc);
+    merge_set_wide<kSample>(a, L, rs, nc);
   }
   __syncthreads();
 }
 
-template <int DT, int R, bool AL, bool FILT>
+template <int DT, int MODE, int R, bool AL, bool FILT>
 __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(Args a) {
+  constexpr bool kSample = MODE != SPEC_MODE_GREEDY;  // softmax statistics, a drawn token
+  constexpr bool kPoint = MODE == SPEC_MODE_POINT;
+  constexpr bool kDraft = MODE == SPEC_MODE_SAMPLE;   // draft rows are read
+  constexpr int kPer = kDraft ? 2 : 1;                // vocabulary rows per position
   using E = Elt<DT>;
   __shared__ Lds L;
   const int t = threadIdx.x, lane = t & 63;
@@ -1972,7 +2018,7 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
     if (c == 0) write_sentinel(a, b);
     return;
   }
-  const int nrows = 2 * g + 1;
+  const int nrows = kDraft ? 2 * g + 1 : g + 1;
   const int lo = c * a.CL;
   const int len = min(a.V - lo, a.CL);
   // The walk (reads, hand-offs, tests) runs at wave priority 3, the draw's
@@ -1981,14 +2027,15 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   // draws of rows already stopped take the slots the walk leaves.
   __builtin_amdgcn_s_setprio(3);
   // x_i, u_i and the logits at x_i, all in flight while the first rows load
-  Gathered in = gather_small<SPEC_MODE_SAMPLE>(a, b, g);
-  gather_logits<DT, SPEC_MODE_SAMPLE, FILT>(a, b, g, in);
+  Gathered in = gather_small<MODE>(a, b, g);
+  if (kSample) gather_logits<DT, MODE, FILT>(a, b, g, in);
   // filtered rows: the threshold of vocabulary row r (entries below weigh 0)
   const float* thr = FILT ? a.thr + (int64_t)b * (2 * a.G + 1) : nullptr;
   auto tau_of = [&](int r) { return FILT ? thr[probe_slot(a, g, r)] : NEG_INF; };
   // a ring of two row slices: the rows of a group of positions go through
-  // it in order (t_i, d_i, t_{i+1}, d_{i+1}, ...: t rows in sa, d rows in
-  // sb), each loaded while the one before it is reduced
+  // it in order (t_i, d_i, t_{i+1}, d_{i+1}, ... when sampling, t_i,
+  // t_{i+1}, ... otherwise; even rows in sa, odd in sb), each loaded while
+  // the one before it is reduced
   Slice<DT, R> sa, sb;
   Geom ga, gb;
   auto load_row = [&](int r, Slice<DT, R>& s, Geom& gg) {
@@ -1996,30 +2043,31 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
     gg = geom_of<DT, AL>(p, len);
     load_slice<DT, R, AL>(p, gg, s);
   };
-  int n = 0, verdict = 0;  // verdict: 0 accepted, 1 rejected, 2 sentinel
+  int n = 0, verdict = 0;  // verdict: 0 accepted, 1 stop, 2 sentinel
   bool reread = false;     // the stop's rows have left the ring
-  // a group's staged pairs (2 rows per position, NC slices each) fit kStage
-  const int cap = min(kMaxSpan, kStage / (2 * a.NC));
+  // a group's staged pairs (kPer rows per position, NC slices each) fit kStage
+  const int cap = min(kMaxSpan, kStage / (kPer * a.NC));
   int span = 1;
   for (int i = 0;;) {
     const int j = min(i + span, g + 1);  // positions [i, j)
-    RowSet rs;
+    RowSet<kPer> rs;
     rs.i = i, rs.g = g;
-    rs.k = 2 * (j - i) - (j > g ? 1 : 0);  // no d_g
+    rs.k = kDraft ? 2 * (j - i) - (j > g ? 1 : 0) : j - i;  // no d_g
     load_row(rs.row(0), sa, ga);
     if (rs.k > 1) load_row(rs.row(1), sb, gb);
     for (int q = 0; q < rs.k; q += 2) {
-      slice_pair<DT, R, AL, FILT>(a, L, sa, ga, rs.row(q), tau_of(rs.row(q)));
+      slice_pair<DT, R, AL, FILT, kSample>(a, L, sa, ga, rs.row(q), tau_of(rs.row(q)), lo);
       if (q + 2 < rs.k) load_row(rs.row(q + 2), sa, ga);
       if (q + 1 < rs.k) {
-        slice_pair<DT, R, AL, FILT>(a, L, sb, gb, rs.row(q + 1), tau_of(rs.row(q + 1)));
+        slice_pair<DT, R, AL, FILT, kSample>(a, L, sb, gb, rs.row(q + 1), tau_of(rs.row(q + 1)),
+                                             lo);
         if (q + 3 < rs.k) load_row(rs.row(q + 3), sb, gb);
       }
     }
-    exchange_set(a, L, b, c, rs, FILT);
+    exchange_set<kSample>(a, L, b, c, rs, FILT);
     if (L.bad) {  // a slice's pairs never arrived (cannot happen in a correct launch)
       write_sentinel(a, b);
-      row_exit(a, L, b, nrows);
+      row_exit(a, L, b, nrows, kSample);
       return;
     }
     if (t < 64) {
@@ -2028,24 +2076,34 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
         const int slot = probe_slot(a, g, r);
         const float mm = L.M[r];
         a.pr_m[(int64_t)b * (2 * a.G + 1) + slot] = mm;
+        // sampling: S relative to the raw max (the rounding of R(m) undone);
+        // greedy: the argmax, as a float
         if (a.pr_s)
           a.pr_s[(int64_t)b * (2 * a.G + 1) + slot] =
-              mm != NEG_INF ? L.S[r] * ex2(-fmaf(mm, a.k2, -ref_of(mm, a.k2))) : L.S[r];
+              !kSample ? (float)__float_as_int(L.S[r])
+                       : (mm != NEG_INF ? L.S[r] * ex2(-fmaf(mm, a.k2, -ref_of(mm, a.k2)))
+                                        : L.S[r]);
       }
       // the tests at i .. j - 1 (lane p holds x_p, u_p and the logits at x_p);
-      // the first that fails, or the bonus position g, ends the walk
+      // the first that fails, or position g, ends the walk
       const bool valid = (unsigned)in.x < (unsigned)a.V;
       const bool mine = lane >= i && lane < j && lane < g;
       bool fail = true;
       if (mine && valid) {
-        const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.M[lane], a.k2))) / L.S[lane];
-        const float q =
-            ex2(fmaf(in.dv, a.k2, -ref_of(L.M[g + 1 + lane], a.k2))) / L.S[g + 1 + lane];
-        if (c == 0 && a.pr_px) {
-          a.pr_px[(int64_t)b * a.G + lane] = p;
-          a.pr_qx[(int64_t)b * a.G + lane] = q;
+        if (kSample) {
+          const float p = ex2(fmaf(in.tv, a.k2, -ref_of(L.M[lane], a.k2))) / L.S[lane];
+          // point-mass drafts: q_i is the indicator of x_i, so q_i(x_i) = 1
+          const float q = kPoint ? 1.f
+                                 : ex2(fmaf(in.dv, a.k2, -ref_of(L.M[g + 1 + lane], a.k2))) /
+                                       L.S[g + 1 + lane];
+          if (c == 0 && a.pr_px) {
+            a.pr_px[(int64_t)b * a.G + lane] = p;
+            a.pr_qx[(int64_t)b * a.G + lane] = q;
+          }
+          fail = !(in.u * q < p);
+        } else {
+          fail = in.x != __float_as_int(L.S[lane]);
         }
-        fail = !(in.u * q < p);
       }
       const unsigned long long stop = __ballot((mine && fail) || lane == g);
       const unsigned long long win = j >= 64 ? ~0ull : ((1ull << j) - 1);
@@ -2055,9 +2113,11 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
         at = __ffsll((long long)hit) - 1;
         const bool ok = at == g || __builtin_amdgcn_readlane(valid ? 1 : 0, at) != 0;
         v = ok ? 1 : 2;
-        // a row the walk uses must have a finite logit (a dead p_i or q_i
-        // fails the test at i, so only the stop position can hold one)
-        if (v == 1 && (L.M[at] == NEG_INF || (at < g && L.M[g + 1 + at] == NEG_INF))) v = 2;
+        // sampling: a row the walk uses must have a finite logit (a dead p_i
+        // or q_i fails the test at i, so only the stop position can hold one)
+        if (kSample && v == 1 &&
+            (L.M[at] == NEG_INF || (kDraft && at < g && L.M[g + 1 + at] == NEG_INF)))
+          v = 2;
       }
       if (t == 0) L.pick = v, L.last = at;
     }
@@ -2065,8 +2125,15 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
     verdict = L.pick;
     if (verdict != 0) {
       n = L.last;
-      // the ring holds the rows of the group's last position only
-      reread = n < j - 1;
+      // the ring holds the group's last two rows: the last position when
+      // sampling, the last two otherwise
+      if constexpr (kDraft) {
+        reread = n < j - 1;
+      } else {
+        const int q = n - i;  // t_n's row in the group
+        reread = q < rs.k - 2;
+        if (!reread && (q & 1)) sa = sb, ga = gb;  // t_n was in sb
+      }
       break;
     }
     i = j;
@@ -2075,28 +2142,50 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   const bool sentinel = verdict == 2;
   if (t < 64) {
     if (c == 0) {
-      // lane i owns output position i (gamma_max <= 63)
-      if (lane <= a.G && !(lane == n && !sentinel))
-        a.out_tok[(int64_t)b * (a.G + 1) + lane] = !sentinel && lane < n ? in.x : -1;
+      // lane i owns output position i (gamma_max <= 63); greedy writes the
+      // target's argmax at n, the other modes leave it to the draw
+      if constexpr (kSample) {
+        if (lane <= a.G && !(lane == n && !sentinel))
+          a.out_tok[(int64_t)b * (a.G + 1) + lane] = !sentinel && lane < n ? in.x : -1;
+      } else {
+        if (lane <= a.G) {
+          int v = -1;
+          if (!sentinel && lane < n)
+            v = in.x;
+          else if (!sentinel && lane == n)
+            v = __float_as_int(L.S[n]);
+          a.out_tok[(int64_t)b * (a.G + 1) + lane] = v;
+        }
+      }
       if (lane == 0) {
         const int kv = a.kv ? a.kv[b] : 0;
         a.out_n[b] = sentinel ? -1 : n;
         a.out_len[b] = sentinel ? kv : kv + n;
       }
     }
-    if (t == 0) {
-      Decision d;
-      d.n = n, d.dead = sentinel, d.resid = n < g;
-      d.xn = 0, d.tx = 0.f;
-      d.mt = L.M[n], d.st = L.S[n];
-      d.md = n < g ? L.M[g + 1 + n] : 0.f;
-      d.sd = n < g ? L.S[g + 1 + n] : 1.f;
-      L.dec = d;
+    if (kSample) {
+      // point mode knocks x_n out of the residual (sampling never reads these)
+      const int xn = kPoint ? __builtin_amdgcn_readlane(in.x, n < g ? n : 0) : 0;
+      const float tx =
+          kPoint ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in.tv), n < g ? n : 0))
+                 : 0.f;
+      // u of the draw: u_{n+1} after a rejection at n, u_g for the bonus draw
+      const float ustar =
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in.u), n < g ? n + 1 : g));
+      if (t == 0) {
+        Decision d;
+        d.n = n, d.dead = sentinel, d.resid = n < g;
+        d.xn = xn, d.tx = tx, d.ustar = ustar;
+        d.mt = L.M[n], d.st = L.S[n];
+        d.md = kDraft && n < g ? L.M[g + 1 + n] : 0.f;
+        d.sd = kDraft && n < g ? L.S[g + 1 + n] : 1.f;
+        L.dec = d;
+      }
     }
-    // u of the draw: u_{n+1} after a rejection at n, u_g for the bonus draw
-    const float ustar =
-        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in.u), n < g ? n + 1 : g));
-    if (t == 0) L.dec.ustar = ustar;
+  }
+  if (!kSample) {  // greedy draws nothing
+    row_exit(a, L, b, nrows, false);
+    return;
   }
   __syncthreads();
   const Decision dc = L.dec;
@@ -2104,18 +2193,18 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
     row_exit(a, L, b, nrows);
     return;
   }
-  if (reread) {  // t_n and d_n again (read a few microseconds ago: cached)
+  if (reread) {  // the stop's rows again (read a few microseconds ago: cached)
     load_row(n, sa, ga);
-    if (n < g) load_row(g + 1 + n, sb, gb);
+    if (kDraft && n < g) load_row(g + 1 + n, sb, gb);
   }
-  if (dc.resid && !AL && gb.head != ga.head) {
+  if (kDraft && dc.resid && !AL && gb.head != ga.head) {
     // the weights pair element j of both rows: d_n in t_n's register layout
     const char* dp = row_of<DT>(a, b, g, g + 1 + n) + (int64_t)lo * E::kBytes;
     load_slice_as<DT, R>(dp, ga, sb);
   }
-  if (!dc.resid) sb = sa;
+  if (!(kDraft && dc.resid)) sb = sa;
   __builtin_amdgcn_s_setprio(1);
-  draw_body<DT, R, false, FILT, AL, true>(a, L, b, c, g, lo, nrows, dc, sa, sb, ga);
+  draw_body<DT, R, kPoint, FILT, AL, true>(a, L, b, c, g, lo, nrows, dc, sa, sb, ga);
 }
 
 // ------------------------------------------------------------------ filtering
@@ -2661,28 +2750,30 @@ void launch_r(int R, bool prio, dim3 grid, hipStream_t s, const Args& a) {
     hipLaunchKernelGGL((verify_kernel<DT, MODE, 4, AL, FILT, false>), grid, dim3(kThreads), 0, s, a);
 }
 
-template <int DT, bool AL, bool FILT>
+template <int DT, int MODE, bool AL, bool FILT>
 void launch_rows_r(int R, dim3 grid, hipStream_t s, const Args& a) {
   if (R == 1)
-    hipLaunchKernelGGL((verify_rows_kernel<DT, 1, AL, FILT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_rows_kernel<DT, MODE, 1, AL, FILT>), grid, dim3(kThreads), 0, s, a);
   else if (R == 2)
-    hipLaunchKernelGGL((verify_rows_kernel<DT, 2, AL, FILT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_rows_kernel<DT, MODE, 2, AL, FILT>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((verify_rows_kernel<DT, 4, AL, FILT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_rows_kernel<DT, MODE, 4, AL, FILT>), grid, dim3(kThreads), 0, s, a);
 }
 
-template <int DT>
+// greedy never filters (the filters keep the largest logit)
+template <int DT, int MODE>
 void launch_rows(int R, bool al, bool filt, dim3 grid, hipStream_t s, const Args& a) {
-  if (filt) {
+  constexpr bool kCanFilter = MODE != SPEC_MODE_GREEDY;
+  if (kCanFilter && filt) {
     if (al)
-      launch_rows_r<DT, true, true>(R, grid, s, a);
+      launch_rows_r<DT, MODE, true, kCanFilter>(R, grid, s, a);
     else
-      launch_rows_r<DT, false, true>(R, grid, s, a);
+      launch_rows_r<DT, MODE, false, kCanFilter>(R, grid, s, a);
   } else {
     if (al)
-      launch_rows_r<DT, true, false>(R, grid, s, a);
+      launch_rows_r<DT, MODE, true, false>(R, grid, s, a);
     else
-      launch_rows_r<DT, false, false>(R, grid, s, a);
+      launch_rows_r<DT, MODE, false, false>(R, grid, s, a);
   }
 }
 
@@ -2787,13 +2878,24 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
     const int hs = hip_status(hipGetLastError());
     if (hs != SPEC_OK) return hs;
   }
-  // sampling reads the rows position by position, up to the walk's stop
-  // (unless the one-pass stream is asked for)
-  if (sample && !(g_tune.flags & SPEC_TUNE_ONE_PASS)) {
-    if (dtype == SPEC_DTYPE_BF16)
-      launch_rows<SPEC_DTYPE_BF16>(p.R, al, filt, grid, s, a);
-    else
-      launch_rows<SPEC_DTYPE_F32>(p.R, al, filt, grid, s, a);
+  // the rows are read position by position, up to the walk's stop (unless
+  // the one-pass stream is asked for)
+  if (!(g_tune.flags & SPEC_TUNE_ONE_PASS)) {
+    if (dtype == SPEC_DTYPE_BF16) {
+      if (sample)
+        launch_rows<SPEC_DTYPE_BF16, SPEC_MODE_SAMPLE>(p.R, al, filt, grid, s, a);
+      else if (draws)
+        launch_rows<SPEC_DTYPE_BF16, SPEC_MODE_POINT>(p.R, al, filt, grid, s, a);
+      else
+        launch_rows<SPEC_DTYPE_BF16, SPEC_MODE_GREEDY>(p.R, al, false, grid, s, a);
+    } else {
+      if (sample)
+        launch_rows<SPEC_DTYPE_F32, SPEC_MODE_SAMPLE>(p.R, al, filt, grid, s, a);
+      else if (draws)
+        launch_rows<SPEC_DTYPE_F32, SPEC_MODE_POINT>(p.R, al, filt, grid, s, a);
+      else
+        launch_rows<SPEC_DTYPE_F32, SPEC_MODE_GREEDY>(p.R, al, false, grid, s, a);
+    }
     return hip_status(hipGetLastError());
   }
   if (dtype == SPEC_DTYPE_BF16) {

@@ -32,10 +32,10 @@ def torch():
 
 
 def _streams_all(case):
-    """Whether the call runs the one-pass kernel, which reports every row's
-    statistics: point-mass drafts (sampling reads the rows position by
-    position, filtered or not, and reports the rows it read)."""
-    return case.mode == "point"
+    """Whether the call reports every row's statistics: never by default
+    (every mode reads the rows position by position, filtered or not, and
+    reports only the rows it read)."""
+    return False
 
 
 def _check(case, torch, **kw):

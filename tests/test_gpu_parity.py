@@ -30,11 +30,10 @@ def torch():
     return _t
 
 
-def _check(case, torch, all_rows=None, **kw):
+def _check(case, torch, all_rows=False, **kw):
     tok, n, ln, pr = run(case, torch, **kw)
-    # the one-pass kernels (point-mass drafts here) report every row's statistics
-    if all_rows is None:
-        all_rows = case.mode == "point"
+    # all_rows: the one-pass kernel reports every row's statistics, the
+    # row-by-row kernel only those of the rows it read
     rep = parity.compare(case, tok, n, ln, pr, all_rows=all_rows)
     assert rep.ok, (rep.summary(), rep.mismatched[:5], rep.prob_errors[:5])
     return rep, tok, n, ln, pr
@@ -95,8 +94,7 @@ def test_parity_full_size(torch, cfg, mode):
             pr = None
             if all(p[4] is not None for p in pending):
                 pr = {k: np.concatenate([p[4][k] for p in pending]) for k in pending[0][4]}
-        total.merge(parity.compare(c, tok, n, ln, pr, row_offset=total.rows,
-                                   all_rows=mode == "point"))
+        total.merge(parity.compare(c, tok, n, ln, pr, row_offset=total.rows))
         pending.clear()
 
     for k in range(calls):
@@ -291,6 +289,11 @@ def test_tuning_invariance(torch):
             got = run(cg, torch, probe=False)
             for x, y in zip(ref[:3], got[:3]):
                 np.testing.assert_array_equal(x, y)
+            sv.tune(vectors, one_pass=True)
+            got = run(cg, torch, probe=False)
+            for x, y in zip(ref[:3], got[:3]):
+                np.testing.assert_array_equal(x, y)
+            sv.tune(vectors)
             _, *rows = _check(cs, torch)
             sv.tune(vectors, one_pass=True)
             print(f"tune vectors={vectors} one_pass", flush=True)
@@ -305,15 +308,16 @@ ONE_PASS = [(1, dict(B=4, V=5003)), (2, dict(B=8, V=3001)), (3, dict(B=16, V=200
             (4, dict(B=12, V=9999)), (5, dict(B=12, V=7777))]
 
 
+@pytest.mark.parametrize("mode", ["sample", "point", "greedy"])
 @pytest.mark.parametrize("cfg,kw", ONE_PASS)
-def test_parity_one_pass_sampling(torch, cfg, kw):
-    """The one-pass sampling kernel (every row streamed, all positions decided
-    at once), with every row's statistics checked, and its outputs equal to
-    the row-by-row kernel's."""
+def test_parity_one_pass(torch, cfg, kw, mode):
+    """The one-pass kernel (every row streamed, all positions decided at
+    once), with every row's statistics checked, and its outputs equal to the
+    row-by-row kernel's."""
     try:
         for rnd in range(2):
-            case = inputs.make_case(cfg, rnd=300 + rnd, **kw)
-            print(f"one-pass cfg={cfg} rnd={rnd} {kw}", flush=True)
+            case = inputs.make_case(cfg, rnd=300 + rnd, mode=mode, **kw)
+            print(f"one-pass cfg={cfg} mode={mode} rnd={rnd} {kw}", flush=True)
             sv.tune(one_pass=True)
             _, *one = _check(case, torch, all_rows=True)
             sv.tune()
@@ -359,6 +363,39 @@ def test_workspace_reuse_and_diagnostics(torch):
         body[4:8] = 0
         assert not body.any(), f"cfg {cfg}: workspace not cleared"
     assert ws.diagnostics() == 0
+
+
+def test_workspace_bounds(torch):
+    """No call writes past the workspace size the library asks for: a guard
+    region after it keeps its pattern through calls of every mode, row by
+    row and in one pass, filtered and not (a greedy workspace is the
+    smallest: it holds no draw sums and no thresholds)."""
+    guard = 1 << 20
+    calls = [(3, dict(B=16, V=20011), m, f) for m in ("sample", "greedy", "point")
+             for f in ((0, 1.0), (20, 0.9))] + [(4, dict(B=12, V=9999), "greedy", (0, 1.0))]
+    try:
+        for one_pass in (False, True):
+            sv.tune(one_pass=one_pass)
+            for cfg, kw, mode, (k, p) in calls:
+                if mode == "greedy" and k:
+                    continue  # filters keep the argmax: greedy takes none
+                case = inputs.make_case(cfg, rnd=31, mode=mode, **kw)
+                if k:
+                    case.extra = dict(case.extra, top_k=k, top_p=float(np.float32(p)))
+                need = sv.workspace_bytes(case.B, case.G, case.V,
+                                          1 if case.target.dtype == np.uint16 else 0,
+                                          MODES[mode])
+                ws = sv.Workspace(need + guard)
+                g = ws.tensor[ws.offset + need: ws.offset + need + guard]
+                g.fill_(0xA5)
+                print(f"bounds one_pass={one_pass} cfg={cfg} mode={mode} k={k} p={p}", flush=True)
+                for _ in range(2):
+                    run(case, torch, workspace=ws, probe=False)
+                left = g.cpu().numpy()
+                bad = np.flatnonzero(left != 0xA5)
+                assert bad.size == 0, f"{bad.size} guard bytes written, first at +{bad[0]}"
+    finally:
+        sv.tune()
 
 
 @pytest.mark.parametrize("mode", ["sample", "greedy", "point"])
