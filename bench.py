@@ -160,6 +160,8 @@ def bench_drafting(args):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lib = sv.load()
+    if args.one_pass:
+        sv.tune(one_pass=True)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     hs = ctypes.c_void_p(stream.cuda_stream)
@@ -289,9 +291,10 @@ def bench_drafting(args):
         verify_us = verify_ms / K * 1e3
         n_acc = vout[1].cpu().numpy()
         emitted = int((n_acc + 1).sum())
-        kern_name, kern_us = (("verify_kernel", verify_us) if verify_us >= draft_us
+        vname = "verify_kernel" if args.one_pass else "verify_rows_kernel"
+        kern_name, kern_us = ((vname, verify_us) if verify_us >= draft_us
                               else ("ngram_kernel", draft_us))
-        kern_bytes = int((g_v + 1).sum()) * V * e if kern_name == "verify_kernel" else draft_bytes
+        kern_bytes = int((g_v + 1).sum()) * V * e if kern_name == vname else draft_bytes
         line_extra.update({"verify_kernel_us": verify_us, "emitted_tokens_per_s":
                            emitted * K / (total_ms * 1e-3), "mean_emitted_per_row": emitted / B,
                            "diagnostics": vws.diagnostics()})
