@@ -304,6 +304,29 @@ def test_tuning_invariance(torch):
         sv.tune()
 
 
+@pytest.mark.parametrize("vectors", [1, 2, 4])
+def test_slice_sizes_aligned_rows(torch, vectors):
+    """Aligned rows (V a whole number of vectors, the kernels' straight-line
+    loads): every mode, filtered and not, at each slice size, against the
+    oracle and bit-identical to the one-pass kernel.  gamma = 8, so that
+    the row-by-row kernel's groups reach four positions (eight rows)."""
+    from gpu_util import filtered_case
+    cases = [inputs.make_case(2, rnd=40 + vectors, mode=m, B=12, V=24000)
+             for m in ("sample", "greedy", "point")]
+    cases += [filtered_case(2, 50 + vectors, m, 20, 0.9, B=12, V=24000) for m in ("sample", "point")]
+    try:
+        for case in cases:
+            print(f"aligned vectors={vectors} mode={case.mode} extra={case.extra}", flush=True)
+            sv.tune(vectors)
+            _, *rows = _check(case, torch)
+            sv.tune(vectors, one_pass=True)
+            _, *one = _check(case, torch, all_rows=True)
+            for x, y in zip(rows[:3], one[:3]):
+                np.testing.assert_array_equal(x, y)
+    finally:
+        sv.tune()
+
+
 ONE_PASS = [(1, dict(B=4, V=5003)), (2, dict(B=8, V=3001)), (3, dict(B=16, V=20011)),
             (4, dict(B=12, V=9999)), (5, dict(B=12, V=7777))]
 
