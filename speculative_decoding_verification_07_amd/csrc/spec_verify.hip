@@ -2228,7 +2228,6 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
 constexpr int kFThreads = 256;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kFBins = 256;
-constexpr double kMassUnit = 4398046511104.0;  // 2^42
 
 struct FArgs {
   const void* tgt;
@@ -2411,9 +2410,17 @@ __device__ __forceinline__ int pmass_bin(float e) {
   return kFBins - 1 - (int)d;
 }
 
-// The weight 2^e in fixed point: trunc(ex2(e) * 2^42).
+// The weight 2^e in fixed point: trunc(ex2(e) * 2^42), formed in fp32 as its
+// two 32-bit halves: hi = trunc(f * 2^10), lo = trunc((f * 2^10 - hi) * 2^32).
+// Every step is exact for 0 <= f < 2^22 (the scalings are powers of two, the
+// difference is the fraction bits of f * 2^10), which covers every weight
+// here (e <= about 0); checked against the double conversion for every
+// float below 2.
 __device__ __forceinline__ unsigned long long fixed_mass_e(float e) {
-  return (unsigned long long)((double)ex2(e) * kMassUnit);
+  const float fs = ex2(e) * 1024.f;
+  const unsigned hi = (unsigned)fs;
+  const unsigned lo = (unsigned)((fs - (float)hi) * 4294967296.f);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ unsigned long long fixed_mass(float l, float k2, float R) {
@@ -2541,20 +2548,19 @@ __device__ __forceinline__ void filter_row(const FArgs& a, int b, int slot, FLds
     const float Rp = ref_of(mx, a.k2);
     for (int i = t; i < kFBins; i += kFThreads) L.h[i] = 0;
     __syncthreads();
-    unsigned long long ws = 0;
     // every entry is added (a zero mass adds nothing): no branch per entry
     auto hist = [&](float l) {
       const float e = fmaf(l, a.k2, -Rp);
-      const unsigned long long w = fixed_mass_e(e);
-      ws += w;
-      atomicAdd(&L.h[pmass_bin(e)], w);
+      atomicAdd(&L.h[pmass_bin(e)], fixed_mass_e(e));
     };
     row_for_each_v<DT>(row, a.V, 1, hist, [&](const float* fe) {
 #pragma unroll
       for (int e = 0; e < E::kVec; ++e) hist(fe[e]);
     });
     __syncthreads();
-    uint64_t incl, excl, W;
+    // the row's total mass: the sum of the bins (exact integers)
+    uint64_t ws = 0, incl, excl, W;
+    for (int i = t; i < kFBins; i += kFThreads) ws += L.h[i];
     fblock_scan(ws, L, incl, excl, W);
     uint64_t need = (uint64_t)ceil((double)a.top_p * (double)W), above, total;
     if (need < 1) need = 1;
