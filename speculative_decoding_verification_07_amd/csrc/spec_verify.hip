@@ -1886,6 +1886,9 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
 // positions (kMaxSpan): a row that keeps accepting needs fewer hand-offs,
 // one that stops early reads little past its stop.
 constexpr int kMaxSpan = 4;
+// the group cap min(kMaxSpan, kStage / (rows per position * NC)) is at least
+// one position at every slice count allowed, so every group advances
+static_assert(kStage / (2 * kMaxSlices) >= 1, "a position's pairs must fit the stage");
 
 // The vocabulary rows of a group of positions starting at i, k of them:
 // sampling t_i, d_i, t_{i+1}, d_{i+1}, ... (no d_g); otherwise t_i, t_{i+1}, ...
