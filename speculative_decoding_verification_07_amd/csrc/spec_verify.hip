@@ -5,23 +5,24 @@
 // [c*CL, (c+1)*CL) of every vocabulary row of b: target rows 0..g and, when
 // sampling, draft rows 0..g-1 (g = gamma_per_row[b]).
 //
-//   1. Each workgroup streams its slice of every row from HBM with 16-byte
-//      loads (the next row's loads in flight while the current row is
-//      reduced) and reduces each to the softmax pair (m, S) = (largest logit,
-//      sum 2^((l - m) log2e / T)); greedy: (largest logit, lowest index).
-//   2. It publishes its pairs to the workspace.
-//      Greedy: slice 0 waits for the group's pairs, merges them, compares
-//      the draft tokens with the target's argmaxes and writes the row.
-//      Sampling: every workgroup waits for its whole group, merges the pairs
-//      in the same fixed order (so all of them hold bit-identical statistics),
-//      runs every acceptance test u_i q_i(x_i) < p_i(x_i) at once and finds
-//      the first rejection n with a wave ballot.
-//   3. Sampling: every workgroup re-reads its slice of the row(s) the token is
-//      drawn from -- the residual max(0, p_n - q_n) after a rejection at n,
-//      p_g for the bonus -- sums the weights in fp64, publishes the sum and
-//      waits for the group's sums.  The workgroup whose slice holds
-//      tau = u * Z finds the token with block prefix scans over the slice it
-//      still holds in registers.
+//   1. Each workgroup reads its slice of a row with 16-byte loads and reduces
+//      it to the softmax pair (m, S) = (largest logit, sum 2^((l - m)
+//      log2e / T)); greedy: (largest logit, lowest index).  It publishes its
+//      pairs to the workspace, waits for its group's pairs of the same rows
+//      and merges them in a fixed order, so that every workgroup of the group
+//      holds bit-identical statistics.
+//   2. The acceptance tests (u_i q_i(x_i) < p_i(x_i); greedy: x_i equal to
+//      the argmax) run in a wave, and a ballot finds the first rejection n.
+//      By default (verify_rows_kernel) the rows are read a group of positions
+//      at a time and the walk reads on only after an acceptance, so no row
+//      after the stop's group is read; verify_kernel streams every row in one
+//      pass and runs all tests at once (SPEC_TUNE_ONE_PASS).
+//   3. Sampling and point mode: every workgroup sums its slice of the
+//      distribution the token is drawn from -- the residual max(0, p_n - q_n)
+//      after a rejection at n, p_g for the bonus -- in fp64 from the slices
+//      it holds in registers, publishes the sums and waits for the group's.
+//      The workgroup whose slice holds tau = u * Z finds the token with block
+//      prefix scans over its slice.  Greedy writes the argmax at n.
 //   4. The last workgroup of a row to leave clears the row's workspace
 //      entries, so a completed call leaves the workspace all zero.
 //
@@ -1869,17 +1870,19 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
   }
 }
 
-// ------------------------------------------------------------------ sampling, row by row
+// ------------------------------------------------------------------ verify, row by row
 // The walk stops at its first rejection n and uses no row after it: only
-// (t_i, d_i) for i <= n, and t_g when every draft is accepted ("Speculative
-// decoding", mhtirogla.ai, "How it works" steps 3-4; tusharamrit, the
-// acceptance loop of the proof).  This kernel reads the rows a few positions
-// at a time: every workgroup of a row's group loads its slices of the rows of
-// positions [i, j), publishes their (m, S), waits for the group's pairs of
-// those rows, merges them and runs the tests at i, i + 1, ... -- the same
-// tests, from the same merged statistics, as the one-pass kernel -- and reads
-// the next positions only when all of [i, j) are accepted.  A rejection draws
-// from the pair still in registers.  Each group of positions costs one
+// position i's rows for i <= n (t_i and d_i when sampling, t_i alone when
+// greedy or with point-mass drafts), and t_g when every draft is accepted
+// ("Speculative decoding", mhtirogla.ai, "How it works" steps 3-4;
+// tusharamrit, the acceptance loop of the proof).  This kernel reads the rows
+// a few positions at a time: every workgroup of a row's group loads its
+// slices of the rows of positions [i, j), publishes their statistics ((m, S);
+// greedy: the max and its index), waits for the group's words of those rows,
+// merges them and runs the tests at i, i + 1, ... -- the same tests, from the
+// same merged statistics, as the one-pass kernel -- and reads the next
+// positions only when all of [i, j) are accepted.  A rejection draws from the
+// slices still in registers where it can.  Each group of positions costs one
 // hand-off between the group's workgroups; no row after the stop's group of
 // positions is read.  The groups are position 0 alone (every row reads it,
 // and the first test is the one most often failed), then 2, then 4
