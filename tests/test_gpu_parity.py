@@ -327,6 +327,27 @@ def test_slice_sizes_aligned_rows(torch, vectors):
         sv.tune()
 
 
+@pytest.mark.parametrize("mode", ["sample", "greedy", "point"])
+def test_many_slices_per_row(torch, mode):
+    """A large vocabulary in a small batch: B = 2, V = 500,000 fp32 (one
+    element past a whole number of vectors) gives about 245 slices per row,
+    past the 16 that the narrow merges take and near the 256 allowed, with
+    groups of positions capped by the stage.  Against the oracle with both
+    kernels, outputs bit-identical."""
+    case = inputs.make_case(1, rnd=61, mode=mode, B=2, V=500_001)
+    plan = sv.plan(case.B, case.G, case.V, sv.F32, MODES[mode])
+    assert plan["slices"] > 128, plan
+    print(f"many slices mode={mode} plan={plan}", flush=True)
+    try:
+        _, *rows = _check(case, torch)
+        sv.tune(one_pass=True)
+        _, *one = _check(case, torch, all_rows=True)
+        for x, y in zip(rows[:3], one[:3]):
+            np.testing.assert_array_equal(x, y)
+    finally:
+        sv.tune()
+
+
 ONE_PASS = [(1, dict(B=4, V=5003)), (2, dict(B=8, V=3001)), (3, dict(B=16, V=20011)),
             (4, dict(B=12, V=9999)), (5, dict(B=12, V=7777))]
 
