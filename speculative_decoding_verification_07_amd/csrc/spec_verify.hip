@@ -2032,9 +2032,10 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   // the path to the call's end, and issue goes first to its waves; the
   // draws of rows already stopped take the slots the walk leaves.
   __builtin_amdgcn_s_setprio(3);
-  // x_i, u_i and the logits at x_i, all in flight while the first rows load
+  // x_i and u_i first; the logits at x_i (which wait for x_i) once the
+  // first group's rows are requested, so that wave 0's row loads do not
+  // wait for x_i
   Gathered in = gather_small<MODE>(a, b, g);
-  if (kSample) gather_logits<DT, MODE, FILT>(a, b, g, in);
   // filtered rows: the threshold of vocabulary row r (entries below weigh 0)
   const float* thr = FILT ? a.thr + (int64_t)b * (2 * a.G + 1) : nullptr;
   auto tau_of = [&](int r) { return FILT ? thr[probe_slot(a, g, r)] : NEG_INF; };
@@ -2061,6 +2062,7 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
     rs.k = kDraft ? 2 * (j - i) - (j > g ? 1 : 0) : j - i;  // no d_g
     load_row(rs.row(0), sa, ga);
     if (rs.k > 1) load_row(rs.row(1), sb, gb);
+    if (kSample && i == 0) gather_logits<DT, MODE, FILT>(a, b, g, in);
     for (int q = 0; q < rs.k; q += 2) {
       slice_pair<DT, R, AL, FILT, kSample>(a, L, sa, ga, rs.row(q), tau_of(rs.row(q)), lo);
       if (q + 2 < rs.k) load_row(rs.row(q + 2), sa, ga);
