@@ -29,10 +29,11 @@ def _prepared(case, dev, stream):
     return call, ws, out
 
 
+@pytest.mark.parametrize("modes", [("sample", "point"), ("greedy", "sample")])
 @pytest.mark.parametrize("sizes", ["small", "full"])
-def test_verify_on_two_streams(sizes):
+def test_verify_on_two_streams(sizes, modes):
     kw = dict(B=16, V=20000) if sizes == "small" else {}
-    cases = [inputs.make_case(3, rnd=41, **kw), inputs.make_case(3, rnd=42, mode="point", **kw)]
+    cases = [inputs.make_case(3, rnd=41 + k, mode=m, **kw) for k, m in enumerate(modes)]
     devs = [case_to_dev(c, torch) for c in cases]
     torch.cuda.synchronize()
     # one after the other on the default stream
@@ -47,7 +48,7 @@ def test_verify_on_two_streams(sizes):
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     preps = [_prepared(c, d, s) for c, d, s in zip(cases, devs, streams)]
     torch.cuda.synchronize()
-    print(f"two streams, {sizes} sizes", flush=True)
+    print(f"two streams, {sizes} sizes, modes {modes}", flush=True)
     for it in range(20):
         for call, _, _ in preps:
             call()
