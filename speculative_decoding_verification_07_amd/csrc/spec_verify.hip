@@ -1889,6 +1889,8 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_kernel(Args a
 // positions (kMaxSpan): a row that keeps accepting needs fewer hand-offs,
 // one that stops early reads little past its stop.
 constexpr int kMaxSpan = 4;
+// a launch of at most this many workgroups leaves CUs idle (256 CUs)
+constexpr int kSmallGrid = 256;
 // the group cap min(kMaxSpan, kStage / (rows per position * NC)) is at least
 // one position at every slice count allowed, so every group advances
 static_assert(kStage / (2 * kMaxSlices) >= 1, "a position's pairs must fit the stage");
@@ -2054,7 +2056,12 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   bool reread = false;     // the stop's rows have left the ring
   // a group's staged pairs (kPer rows per position, NC slices each) fit kStage
   const int cap = min(kMaxSpan, kStage / (kPer * a.NC));
-  int span = 1;
+  // With one row per position (greedy, point-mass drafts) and fewer
+  // workgroups than CUs, the first group takes positions 0 and 1: their two
+  // rows fill the ring at once (no second read latency in series), the
+  // memory system has bandwidth to spare at that size, and a row that
+  // accepts x_0 saves a hand-off.
+  int span = kPer == 1 && (int)gridDim.x <= kSmallGrid ? min(2, cap) : 1;
   for (int i = 0;;) {
     const int j = min(i + span, g + 1);  // positions [i, j)
     RowSet<kPer> rs;
