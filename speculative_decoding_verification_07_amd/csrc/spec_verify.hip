@@ -1573,6 +1573,32 @@ __device__ __forceinline__ void ring_pick(const Ring<DT, R>& ring, int k, Slice<
   }
 }
 
+// Slot `k` of an array of row slices, selected at run time (register by
+// register, so that the array stays in registers).
+template <int N, int DT, int R>
+__device__ __forceinline__ void pick_slot(const Slice<DT, R> (&buf)[N], const Geom (&geo)[N],
+                                          int k, Slice<DT, R>& s, Geom& g) {
+  s = buf[0];
+  g = geo[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) {
+    const bool take = k == j;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      s.v[q].x = take ? buf[j].v[q].x : s.v[q].x;
+      s.v[q].y = take ? buf[j].v[q].y : s.v[q].y;
+      s.v[q].z = take ? buf[j].v[q].z : s.v[q].z;
+      s.v[q].w = take ? buf[j].v[q].w : s.v[q].w;
+    }
+    s.hd = take ? buf[j].hd : s.hd;
+    s.tl = take ? buf[j].tl : s.tl;
+    g.head = take ? geo[j].head : g.head;
+    g.nv = take ? geo[j].nv : g.nv;
+    g.jb = take ? geo[j].jb : g.jb;
+    g.len = take ? geo[j].len : g.len;
+  }
+}
+
 // The softmax sum of a merged pair relative to the raw maximum m, i.e. with
 // the rounding of its reference R(m) undone: sum_j 2^((l_j - m) k2).
 __device__ __forceinline__ float s_rel(float m, float s, float k2) {
@@ -2041,12 +2067,21 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   // filtered rows: the threshold of vocabulary row r (entries below weigh 0)
   const float* thr = FILT ? a.thr + (int64_t)b * (2 * a.G + 1) : nullptr;
   auto tau_of = [&](int r) { return FILT ? thr[probe_slot(a, g, r)] : NEG_INF; };
-  // a ring of two row slices: the rows of a group of positions go through
-  // it in order (t_i, d_i, t_{i+1}, d_{i+1}, ... when sampling, t_i,
-  // t_{i+1}, ... otherwise; even rows in sa, odd in sb), each loaded while
-  // the one before it is reduced
+  // A ring of NS row slices, eight vectors per thread in all: the rows of a
+  // group of positions go through it in order (t_i, d_i, t_{i+1}, d_{i+1},
+  // ... when sampling, t_i, t_{i+1}, ... otherwise), row q in slot q mod NS,
+  // each loaded once the row before it in its slot is reduced.  NS = 2 (four
+  // vectors per thread and row): even rows in sa, odd in sb.  Smaller slices
+  // keep more rows in flight (a group of up to eight rows at once with one
+  // vector per thread), and sa / sb then receive the stop's rows for the
+  // draw.  Rows that are not 16-byte aligned keep two slots (their head and
+  // tail elements and geometry per slot would not fit the registers), and
+  // so do filtered rows of two vectors per thread (which would spill).
+  constexpr int NS = AL && !(FILT && R == 2) ? 8 / R : 2;
   Slice<DT, R> sa, sb;
   Geom ga, gb;
+  Slice<DT, R> ring[NS > 2 ? NS : 1];
+  Geom gring[NS > 2 ? NS : 1];
   auto load_row = [&](int r, Slice<DT, R>& s, Geom& gg) {
     const char* p = row_of<DT>(a, b, g, r) + (int64_t)lo * E::kBytes;
     gg = geom_of<DT, AL>(p, len);
@@ -2056,27 +2091,44 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
   bool reread = false;     // the stop's rows have left the ring
   // a group's staged pairs (kPer rows per position, NC slices each) fit kStage
   const int cap = min(kMaxSpan, kStage / (kPer * a.NC));
-  // With one row per position (greedy, point-mass drafts) and fewer
-  // workgroups than CUs, the first group takes positions 0 and 1: their two
-  // rows fill the ring at once (no second read latency in series), the
-  // memory system has bandwidth to spare at that size, and a row that
-  // accepts x_0 saves a hand-off.
-  int span = kPer == 1 && (int)gridDim.x <= kSmallGrid ? min(2, cap) : 1;
+  // With fewer workgroups than CUs, the first group takes positions 0 and 1
+  // when their rows fill the ring at once (one row per position -- greedy,
+  // point-mass drafts -- or a ring of four slots or more): the wider group
+  // then costs no read latency in series, the memory system has bandwidth
+  // to spare at that size, and a row that accepts x_0 saves a hand-off.
+  int span = (kPer == 1 || NS >= 4) && (int)gridDim.x <= kSmallGrid ? min(2, cap) : 1;
   for (int i = 0;;) {
     const int j = min(i + span, g + 1);  // positions [i, j)
     RowSet<kPer> rs;
     rs.i = i, rs.g = g;
     rs.k = kDraft ? 2 * (j - i) - (j > g ? 1 : 0) : j - i;  // no d_g
-    load_row(rs.row(0), sa, ga);
-    if (rs.k > 1) load_row(rs.row(1), sb, gb);
-    if (kSample && i == 0) gather_logits<DT, MODE, FILT>(a, b, g, in);
-    for (int q = 0; q < rs.k; q += 2) {
-      slice_pair<DT, R, AL, FILT, kSample>(a, L, sa, ga, rs.row(q), tau_of(rs.row(q)), lo);
-      if (q + 2 < rs.k) load_row(rs.row(q + 2), sa, ga);
-      if (q + 1 < rs.k) {
-        slice_pair<DT, R, AL, FILT, kSample>(a, L, sb, gb, rs.row(q + 1), tau_of(rs.row(q + 1)),
-                                             lo);
-        if (q + 3 < rs.k) load_row(rs.row(q + 3), sb, gb);
+    if constexpr (NS == 2) {
+      load_row(rs.row(0), sa, ga);
+      if (rs.k > 1) load_row(rs.row(1), sb, gb);
+      if (kSample && i == 0) gather_logits<DT, MODE, FILT>(a, b, g, in);
+      for (int q = 0; q < rs.k; q += 2) {
+        slice_pair<DT, R, AL, FILT, kSample>(a, L, sa, ga, rs.row(q), tau_of(rs.row(q)), lo);
+        if (q + 2 < rs.k) load_row(rs.row(q + 2), sa, ga);
+        if (q + 1 < rs.k) {
+          slice_pair<DT, R, AL, FILT, kSample>(a, L, sb, gb, rs.row(q + 1),
+                                               tau_of(rs.row(q + 1)), lo);
+          if (q + 3 < rs.k) load_row(rs.row(q + 3), sb, gb);
+        }
+      }
+    } else {
+      // every slot is loaded unconditionally (a slot past the group's last
+      // row re-reads that row), so that the compiler counts the loads in
+      // flight statically instead of draining them before each load
+#pragma unroll
+      for (int q = 0; q < NS; ++q) load_row(rs.row(min(q, rs.k - 1)), ring[q], gring[q]);
+      if (kSample && i == 0) gather_logits<DT, MODE, FILT>(a, b, g, in);
+#pragma unroll
+      for (int q = 0; q < 2 * kMaxSpan; ++q) {
+        if (q < rs.k)
+          slice_pair<DT, R, AL, FILT, kSample>(a, L, ring[q % NS], gring[q % NS], rs.row(q),
+                                               tau_of(rs.row(q)), lo);
+        if (q + NS < 2 * kMaxSpan)
+          load_row(rs.row(min(q + NS, rs.k - 1)), ring[q % NS], gring[q % NS]);
       }
     }
     exchange_set<kSample>(a, L, b, c, rs, FILT);
@@ -2142,12 +2194,28 @@ __global__ __launch_bounds__(kThreads, SPEC_MIN_WAVES) void verify_rows_kernel(A
       n = L.last;
       // the ring holds the group's last two rows: the last position when
       // sampling, the last two otherwise
-      if constexpr (kDraft) {
-        reread = n < j - 1;
+      const int q = kPer * (n - i);  // t_n's row in the group (d_n follows it)
+      if constexpr (NS == 2) {
+        if constexpr (kDraft) {
+          reread = n < j - 1;
+        } else {
+          reread = q < rs.k - 2;
+          if (!reread && (q & 1)) sa = sb, ga = gb;  // t_n was in sb
+        }
       } else {
-        const int q = n - i;  // t_n's row in the group
-        reread = q < rs.k - 2;
-        if (!reread && (q & 1)) sa = sb, ga = gb;  // t_n was in sb
+        // slot s ends holding the group's row min(the last row index equal
+        // to s mod NS below 2 kMaxSpan, k - 1) (the loads are unconditional);
+        // the stop's rows are used from the ring when that is what their
+        // slots hold
+        auto resident = [&](int r) {
+          const int sl = r % NS;
+          return min(sl + NS * ((2 * kMaxSpan - 1 - sl) / NS), rs.k - 1) == r;
+        };
+        reread = !resident(q) || (kDraft && n < g && !resident(q + 1));
+        if (!reread) {
+          pick_slot(ring, gring, q % NS, sa, ga);
+          if (kDraft) pick_slot(ring, gring, (q + 1) % NS, sb, gb);
+        }
       }
       break;
     }
