@@ -164,9 +164,9 @@ int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
  *                   (GREEDY: out_m only, out_s holds the argmax as float;
  *                   GREEDY and POINT leave the draft slots untouched)
  *   Without SPEC_TUNE_ONE_PASS the rows are read in groups of positions
- *   (0; 1-2; then up to four at a time -- GREEDY and POINT on launches of at
- *   most 256 workgroups: 0-1 first) up to the group holding the walk's stop
- *   n, and only what was read is reported: out_px / out_qx for the
+ *   (0; 1-2; then up to four at a time -- on launches of at most 256
+ *   workgroups the first group may hold 0-1) up to the group holding the
+ *   walk's stop n, and only what was read is reported: out_px / out_qx for the
  *   positions of the groups read (which may run past n), out_m / out_s for
  *   their rows t_i (and d_i in SAMPLE; t_g when it was read); the other
  *   entries are untouched.
